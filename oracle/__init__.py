@@ -1,0 +1,16 @@
+"""CPU oracle of the N-vium decode step (float64 NumPy).
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg import it; the HIP path never does.
+
+Parity status per function (pins are in tests/test_oracle_*.py):
+  rmsnorm, silu, softmax, causal_attention   pinned: torch.nn.functional routines
+  rope                                       pinned: complex-rotation form + relative-position invariance
+  layer_rows, prefill, decode_step (exit 4)  pinned: independent torch LLaMA forward (strict generalisation)
+  gate, exit_probs                           pinned: closed forms (sum to 1, stated exit masses)
+  walk_gates, inverse_cdf, mixture           pinned: brute force + chi-square against pi_mix
+  generate_deferred                          pinned: bit-identity with sequential decoding,
+                                             brute force over forced exit patterns
+  head_logits (exits 1-3)                    pinned only through the same routines as exit 4
+"""
+from . import model, deferred  # noqa: F401
