@@ -1,0 +1,145 @@
+/*
+ * nvium.h -- C ABI of the N-vium mixture-of-exits decode library (HIP, gfx950).
+ *
+ * The method (arXiv 2605.13190, "N-vium: Mixture-of-Exits Transformer for
+ * Accelerated Exact Generation"): a LLaMA-2-style decoder is cut into four depth
+ * segments; after each segment an exit holds a router w_k (here the linear gate
+ * sigmoid(g_k . h + b_k), the last one fixed to 1) and its own RMSNorm + LM head.
+ * The next-token distribution is the mixture pi_mix = sum_k p_k pi_k with the
+ * stick-breaking weights p_k = w_k prod_{j<k}(1 - w_j) (gist.science technical
+ * summary, section 2 "Methodik", part "Architektur", equations for p_k and
+ * pi_mix).  A token is drawn exactly from pi_mix by walking the gates with
+ * caller-supplied uniforms and sampling only the head where the walk stops
+ * (same summary, section 3, "exact sampling"; abstract).  The layers above that
+ * exit are deferred and run later, as a causal chunk concatenated with the
+ * following tokens that reach those depths, so that every layer's KV cache is
+ * complete (section 2, part "Inferenz: Piggybacking"; abstract).
+ *
+ * Conventions for every call:
+ *   - Host pointers belong to the caller and are read or written only during
+ *     the call.  Device memory belongs to the model (inside the caller's arena
+ *     when one is given) and is released by nv_free.
+ *   - Every call is synchronous with respect to the host: results are in host
+ *     memory when it returns.  Work is issued on the stream given to nv_load.
+ *   - One model handle must not be used from two threads at once.
+ *   - Errors return a negative nv_status; nv_last_error gives the text.  After
+ *     NV_EDEVICE (any HIP runtime error) the handle can only be freed.
+ */
+#ifndef NVIUM_H
+#define NVIUM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct nv_model nv_model;
+
+typedef enum nv_status {
+    NV_OK = 0,
+    NV_EINVAL = -1,     /* bad argument: NULL pointer, uniform outside [0,1) or NaN,
+                           token id >= vocab, sequence index out of range */
+    NV_ESTATE = -2,     /* call not valid in the current state (e.g. step before prefill,
+                           prefilled sequences not numbered 0..n-1) */
+    NV_ECAPACITY = -3,  /* a sequence would exceed max_ctx positions, or an arena too small */
+    NV_EIO = -4,        /* weights file missing, truncated or inconsistent */
+    NV_EDEVICE = -5     /* HIP runtime error; the handle is no longer usable */
+} nv_status;
+
+/* Model shape, as read from the weights file. */
+typedef struct nv_config {
+    int32_t n_layers, d_model, n_heads, head_dim, ffn, vocab, n_exits;
+    int32_t wdtype;                 /* 0: fp32 matrices and KV; 1: bf16 matrices and KV */
+    float norm_eps, rope_base;
+    int32_t exit_layer[4];          /* 1-based layer after which exit k sits */
+    float gate_bias[4];             /* b_k; the last is +inf (w = 1) */
+} nv_config;
+
+/* Device bytes nv_load needs for this weights file at this capacity
+ * (weights + KV caches + hidden states + workspaces), or 0 if the file
+ * cannot be read.  Lets a caller allocate the arena (e.g. a torch tensor). */
+size_t nv_mem_required(const char *weights_path, int32_t max_batch, int32_t max_ctx);
+
+/* Load a weights file (layout in synth/weights.py of this repository) and
+ * allocate state for up to max_batch sequences of up to max_ctx positions each.
+ *   device_arena: device memory of at least nv_mem_required() bytes owned by
+ *                 the caller and kept alive until nv_free, or NULL to let the
+ *                 library allocate (hipMalloc).
+ *   hip_stream:   a hipStream_t to issue all work on, or NULL for the null stream.
+ * Errors: NV_EINVAL (NULL path/out, sizes < 1), NV_EIO (file), NV_ECAPACITY
+ * (arena too small), NV_EDEVICE. */
+nv_status nv_load(const char *weights_path, int32_t max_batch, int32_t max_ctx,
+                  void *device_arena, size_t arena_bytes, void *hip_stream,
+                  nv_model **out);
+
+void nv_free(nv_model *m);
+
+/* Text of the last error on this handle ("" if none).  Valid until the next call. */
+const char *nv_last_error(const nv_model *m);
+
+nv_status nv_get_config(const nv_model *m, nv_config *out);
+
+/* Start (or restart) sequence `seq` with prompt tokens[0..n-1], n >= 1.
+ * Positions 0..n-2 run through every layer (building their KV); tokens[n-1]
+ * becomes the pending input that the next nv_step consumes at position n-1.
+ * Restarting drops the sequence's KV, deferred states and frontiers.
+ * Errors: NV_EINVAL (seq out of range, NULL tokens, n < 1, token >= vocab),
+ * NV_ECAPACITY (n > max_ctx), NV_EDEVICE. */
+nv_status nv_prefill(nv_model *m, int32_t seq, const int32_t *tokens, int32_t n);
+
+/* One decode step for every prefilled sequence 0..n_seq-1 in lock-step.
+ *   uniforms   [n_seq][4] float32 in [0,1): u[0..2] walk gates 1..3 (stop at gate
+ *              k iff u[k-1] < w_k), u[3] draws the token by inverse CDF of the
+ *              stopping exit's softmax in token-id order (smallest id i with
+ *              u[3] < F(i)).
+ *   tokens_out [n_seq] sampled next token; it becomes the pending input.
+ *   exits_out  [n_seq] exit the token came from, 1..4.
+ * Layers above the exit are deferred; they run when a later token of the same
+ * sequence reaches them, or at nv_flush.
+ * Errors: NV_EINVAL (NULL pointers, bad uniforms), NV_ESTATE (no prefilled
+ * sequence, or prefilled indices not contiguous from 0), NV_ECAPACITY (a
+ * sequence has no free position), NV_EDEVICE. */
+nv_status nv_step(nv_model *m, const float *uniforms, int32_t *tokens_out, int32_t *exits_out);
+
+/* nv_step with the next inputs given by the caller (teacher forcing): sampling
+ * and deferral happen exactly as in nv_step and tokens_out/exits_out report the
+ * draw, but next_inputs[i] (< vocab) becomes sequence i's pending input instead
+ * of the sampled token.  Used to score a given continuation. */
+nv_status nv_step_forced(nv_model *m, const float *uniforms, const int32_t *next_inputs,
+                         int32_t *tokens_out, int32_t *exits_out);
+
+/* Run every deferred segment of sequence `seq` (-1: all prefilled sequences)
+ * over all consumed positions, with no gates and no heads.  Afterwards every
+ * layer's KV is complete for every consumed position.  A second flush is a
+ * no-op.  Errors: NV_EINVAL (seq out of range), NV_EDEVICE. */
+nv_status nv_flush(nv_model *m, int32_t seq);
+
+/* ---- inspection (not on the timed path) ------------------------------------ */
+
+/* Positions consumed so far (prompt prefix + decode steps) and the four
+ * frontiers: every position < frontier[s] has completed segment s+1. */
+nv_status nv_debug_frontiers(nv_model *m, int32_t seq, int32_t *n_consumed, int32_t frontier[4]);
+
+/* Logits (float32, [vocab]) of the exit that produced the last step's token. */
+nv_status nv_debug_logits(nv_model *m, int32_t seq, float *out);
+
+/* Router outputs w_1..w_4 of the last step (float64; NaN for gates not reached,
+ * w_4 = 1 when exit 4 was reached). */
+nv_status nv_debug_gates(nv_model *m, int32_t seq, double *out);
+
+/* K and V of layer `layer` (0-based) for positions pos0..pos0+n-1, as float32
+ * [n][n_heads][head_dim] each (K after RoPE). */
+nv_status nv_debug_kv(nv_model *m, int32_t seq, int32_t layer, int32_t pos0, int32_t n,
+                      float *k_out, float *v_out);
+
+/* Hidden states (float32 [n][d_model]) of positions pos0..pos0+n-1: the output
+ * of the last segment each position completed. */
+nv_status nv_debug_hidden(nv_model *m, int32_t seq, int32_t pos0, int32_t n, float *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVIUM_H */

@@ -1,0 +1,943 @@
+// Host runtime of libnvium: the C ABI declared in include/nvium.h.
+//
+// Scheduling follows section 2, part "Inferenz: Piggybacking" of the gist.science
+// technical summary of N-vium: a token that exits at node k leaves its layers above
+// that exit pending; when a later token of the same sequence reaches those depths the
+// pending hidden states are concatenated with the current one and run as one causal
+// chunk.  Per sequence the runtime keeps one frontier per segment (every position below
+// frontier[s] has completed segment s) and one hidden-state row per position (the output
+// of the last segment that position completed), so the chunk of segment s at position p
+// is the contiguous range [frontier[s], p] and runs in place.
+#include "nv_internal.h"
+#include "nvium.h"
+
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace nv;
+
+namespace {
+
+constexpr int kMaxExits = 4;
+constexpr int kAttnRowsPerItem = 32;
+constexpr size_t kAlign = 256;
+
+struct LayerPtrs {
+    float* attn_norm;
+    void* wqkv;   // [3d][d]: rows of W_q, then W_k, then W_v
+    void* wo;     // [d][d]
+    float* mlp_norm;
+    void* wgu;    // [2F][d]: row 2j = W_gate row j, row 2j+1 = W_up row j
+    void* wd;     // [d][F]
+};
+
+struct ExitPtrs {
+    float* gate_w;
+    float* norm;
+    void* head;   // [V][d]
+    float bias;
+};
+
+struct SeqHost {
+    bool live = false;
+    int n = 0;                 // positions consumed
+    int f[kMaxExits] = {0, 0, 0, 0};
+    int pending = 0;
+    int last_exit = 0;
+};
+
+struct Chunk {
+    int seq, pos0, nrows;
+};
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sizes of everything the model keeps in device memory.
+struct Plan {
+    size_t es = 0, kes = 0;
+    size_t embed = 0, layer_w = 0, exit_w = 0;
+    size_t hidden = 0, kv = 0, rope = 0;
+    int R_max = 0, part_cap = 0, items_cap = 0;
+    size_t qkv = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0;
+    size_t tables = 0, small = 0, logits = 0;
+    size_t total = 0;
+};
+
+struct FileHeader {
+    nv_config c;
+};
+
+bool read_header(const char* path, nv_config* c, std::string* err) {
+    int fd = ::open(path, O_RDONLY);
+    if (fd < 0) {
+        *err = std::string("cannot open weights file: ") + path;
+        return false;
+    }
+    unsigned char h[256];
+    ssize_t got = ::pread(fd, h, sizeof(h), 0);
+    ::close(fd);
+    if (got != (ssize_t)sizeof(h) || std::memcmp(h, "NVIUMW01", 8) != 0) {
+        *err = "weights file header missing or wrong magic";
+        return false;
+    }
+    int32_t iv[9];
+    std::memcpy(iv, h + 8, sizeof(iv));
+    if (iv[0] != 256) {
+        *err = "unsupported weights header size";
+        return false;
+    }
+    c->n_layers = iv[1];
+    c->d_model = iv[2];
+    c->n_heads = iv[3];
+    c->head_dim = iv[4];
+    c->ffn = iv[5];
+    c->vocab = iv[6];
+    c->n_exits = iv[7];
+    c->wdtype = iv[8];
+    std::memcpy(&c->norm_eps, h + 44, 4);
+    std::memcpy(&c->rope_base, h + 48, 4);
+    std::memcpy(c->exit_layer, h + 52, 16);
+    std::memcpy(c->gate_bias, h + 68, 16);
+    const int L = c->n_layers, d = c->d_model;
+    bool ok = L > 0 && d > 0 && c->n_heads > 0 && c->head_dim > 0 && c->n_heads * c->head_dim == d &&
+              c->ffn > 0 && c->vocab > 0 && c->n_exits == kMaxExits && (c->wdtype == 0 || c->wdtype == 1) &&
+              L % kMaxExits == 0 && (c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128) &&
+              d % 8 == 0 && c->ffn % 8 == 0 && c->vocab % 8 == 0;
+    for (int k = 0; ok && k < kMaxExits; ++k) ok = c->exit_layer[k] == (k + 1) * (L / kMaxExits);
+    if (!ok) {
+        *err = "weights header describes an unsupported shape";
+        return false;
+    }
+    return true;
+}
+
+Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
+    Plan p;
+    const size_t L = c.n_layers, d = c.d_model, F = c.ffn, V = c.vocab, H = c.n_heads, hd = c.head_dim;
+    p.es = c.wdtype == 1 ? 2 : 4;
+    p.kes = p.es;
+    p.embed = align_up(V * d * p.es);
+    p.layer_w = align_up(d * 4) * 2 + align_up(3 * d * d * p.es) + align_up(d * d * p.es) +
+                align_up(2 * F * d * p.es) + align_up(d * F * p.es);
+    p.exit_w = align_up(d * 4) * 2 + align_up(V * d * p.es);
+    p.hidden = align_up((size_t)max_batch * max_ctx * d * 4);
+    p.kv = align_up((size_t)max_batch * L * 2 * H * max_ctx * hd * p.kes);
+    p.rope = align_up((size_t)max_ctx * hd * 4);
+    size_t rmax = std::max<size_t>(64, std::min<size_t>((size_t)max_batch * max_ctx, 4096));
+    p.R_max = (int)rmax;
+    p.part_cap = (int)(rmax * H * 4);
+    p.items_cap = p.part_cap;
+    p.qkv = align_up(rmax * 3 * d * 4);
+    p.attn_o = align_up(rmax * d * 4);
+    p.mlp = align_up(rmax * F * 4);
+    p.part_ml = align_up((size_t)p.part_cap * 2 * 4);
+    p.part_o = align_up((size_t)p.part_cap * hd * 4);
+    p.tables = align_up(rmax * sizeof(RowInfo) * 2 + rmax * sizeof(CombineInfo) +
+                        (size_t)p.items_cap * sizeof(AttnItem) + rmax * 4);
+    // uniforms, router outputs, stop flags, tokens in/out, head lists
+    p.small = align_up((size_t)max_batch * (16 + 4 + sizeof(RowInfo))) +
+              2 * align_up((size_t)max_batch * (4 + 2 * sizeof(RowInfo))) + align_up((size_t)max_batch * 32) +
+              2 * align_up((size_t)max_batch * 4);
+    p.logits = align_up((size_t)max_batch * V * 4);
+    p.total = p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.hidden + p.kv + p.rope + p.qkv + p.attn_o +
+              p.mlp + p.part_ml + p.part_o + p.tables + p.small + p.logits + kAlign;
+    return p;
+}
+
+}  // namespace
+
+struct nv_model {
+    nv_config cfg{};
+    int L = 0, d = 0, H = 0, hd = 0, F = 0, V = 0, seg = 0;
+    bool bf16 = false;
+    int max_batch = 0, max_ctx = 0;
+    Plan plan;
+    hipStream_t st = nullptr;
+    char* arena = nullptr;
+    size_t arena_off = 0;
+    bool own_arena = false;
+    bool dead = false;
+
+    void* embed = nullptr;
+    std::vector<LayerPtrs> layers;
+    ExitPtrs exits[kMaxExits]{};
+    float* Hs = nullptr;
+    void* kv = nullptr;
+    float* rope = nullptr;
+    float* qkv = nullptr;
+    float* attn_o = nullptr;
+    float* mlp = nullptr;
+    float* part_ml = nullptr;
+    float* part_o = nullptr;
+    char* d_tables = nullptr;
+    // Small per-step blocks; each has a pinned host mirror of the same layout so that it
+    // goes up in one copy.  step: [uniforms MB*4 f32][pending tokens MB i32][current rows MB]
+    // list (gate, head): [sequence ids MB i32][current rows MB][output rows MB]
+    char* d_stepblk = nullptr;
+    char* d_gatelist = nullptr;
+    char* d_headlist = nullptr;
+    double* d_w = nullptr;
+    int* d_stop = nullptr;
+    int* d_tok_out = nullptr;
+    float* logits = nullptr;
+
+    char* h_stage = nullptr;   // pinned; mirrors the device table region
+    size_t h_stage_bytes = 0;
+    bool stage_busy = false;   // an async copy from h_stage may still be pending
+    char* h_stepblk = nullptr;
+    char* h_gatelist = nullptr;
+    char* h_headlist = nullptr;
+    char* h_out = nullptr;     // pinned: stop flags, tokens, router outputs coming back
+
+    size_t stepblk_bytes() const { return (size_t)max_batch * (16 + 4 + sizeof(RowInfo)); }
+    size_t list_bytes() const { return (size_t)max_batch * (4 + 2 * sizeof(RowInfo)); }
+    static float* unif(char* b) { return (float*)b; }
+    int* tok_in(char* b) const { return (int*)(b + (size_t)max_batch * 16); }
+    RowInfo* cur_rows(char* b) const { return (RowInfo*)(b + (size_t)max_batch * 20); }
+    static int* lseqs(char* b) { return (int*)b; }
+    RowInfo* lrows(char* b) const { return (RowInfo*)(b + (size_t)max_batch * 4); }
+    RowInfo* lorows(char* b) const { return (RowInfo*)(b + (size_t)max_batch * (4 + sizeof(RowInfo))); }
+
+    std::vector<SeqHost> seqs;
+    std::vector<double> last_w;   // [max_batch][4]
+    std::string err;
+
+    LayerDims dims() const {
+        LayerDims D;
+        D.L = L;
+        D.d = d;
+        D.H = H;
+        D.hd = hd;
+        D.F = F;
+        D.V = V;
+        D.max_ctx = max_ctx;
+        D.kv_bf16 = bf16 ? 1 : 0;
+        return D;
+    }
+
+    char* take(size_t n) {
+        char* p = arena + arena_off;
+        arena_off += align_up(n);
+        return p;
+    }
+};
+
+namespace {
+
+nv_status fail(nv_model* m, nv_status s, const std::string& msg) {
+    if (m) m->err = msg;
+    return s;
+}
+
+#define NV_HIP(m, expr)                                                                           \
+    do {                                                                                          \
+        hipError_t e_ = (expr);                                                                   \
+        if (e_ != hipSuccess) {                                                                   \
+            (m)->dead = true;                                                                     \
+            return fail((m), NV_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_));      \
+        }                                                                                         \
+    } while (0)
+
+// Read `n` bytes at `off` of the weights file into host memory.
+bool pread_all(int fd, void* dst, size_t n, size_t off) {
+    char* p = (char*)dst;
+    while (n > 0) {
+        ssize_t r = ::pread(fd, p, n, (off_t)off);
+        if (r <= 0) return false;
+        p += r;
+        n -= (size_t)r;
+        off += (size_t)r;
+    }
+    return true;
+}
+
+nv_status stage_sync(nv_model* m) {
+    if (m->stage_busy) {
+        NV_HIP(m, hipStreamSynchronize(m->st));
+        m->stage_busy = false;
+    }
+    return NV_OK;
+}
+
+// Build and upload the tables for one launch group of causal chunks at one segment:
+// compact rows, attention items and combine info.  Layout in the device table region:
+// [rows R][headless: reserved R][comb R][items n_items].
+struct Tables {
+    RowInfo* rows;
+    CombineInfo* comb;
+    AttnItem* items;
+    int R, n_items;
+};
+
+nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t) {
+    nv_status s = stage_sync(m);
+    if (s != NV_OK) return s;
+    const Plan& P = m->plan;
+    int R = 0;
+    for (const Chunk& c : chunks) R += c.nrows;
+    if (R > P.R_max) return fail(m, NV_ECAPACITY, "internal: launch group exceeds workspace rows");
+    RowInfo* hrows = (RowInfo*)m->h_stage;
+    CombineInfo* hcomb = (CombineInfo*)(m->h_stage + sizeof(RowInfo) * P.R_max);
+    AttnItem* hitems = (AttnItem*)(m->h_stage + (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max);
+    // rows
+    int r = 0;
+    for (const Chunk& c : chunks)
+        for (int i = 0; i < c.nrows; ++i, ++r) {
+            hrows[r].seq = c.seq;
+            hrows[r].pos = c.pos0 + i;
+            hrows[r].hrow = c.seq * m->max_ctx + c.pos0 + i;
+            hrows[r].pad = 0;
+        }
+    // attention items: the key range of each block of <= 32 rows is split into pieces of
+    // split_len keys; the split length doubles until the partial slots fit.
+    int split_len = R <= 64 ? 64 : 512;
+    for (;;) {
+        long slots = 0, items = 0;
+        for (const Chunk& c : chunks)
+            for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
+                int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
+                int ctx = c.pos0 + rb + nr;
+                int ns = (ctx + split_len - 1) / split_len;
+                slots += (long)m->H * ns * nr;
+                items += (long)m->H * ns;
+            }
+        if (slots <= P.part_cap && items <= P.items_cap) break;
+        split_len *= 2;
+    }
+    int n_items = 0, slot = 0, row0 = 0;
+    for (const Chunk& c : chunks) {
+        for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
+            int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
+            int ctx = c.pos0 + rb + nr;
+            int ns = (ctx + split_len - 1) / split_len;
+            for (int h = 0; h < m->H; ++h)
+                for (int s2 = 0; s2 < ns; ++s2) {
+                    AttnItem& it = hitems[n_items++];
+                    it.row0 = row0 + rb;
+                    it.nrows = nr;
+                    it.head = h;
+                    it.lo = s2 * split_len;
+                    it.hi = std::min(ctx, (s2 + 1) * split_len);
+                    it.part = slot + (h * ns + s2) * nr;
+                    it.pad0 = it.pad1 = 0;
+                }
+            for (int i = 0; i < nr; ++i) {
+                CombineInfo& ci = hcomb[row0 + rb + i];
+                ci.base = slot;
+                ci.off = i;
+                ci.nsplit = ns;
+                ci.nrows = nr;
+            }
+            slot += m->H * ns * nr;
+        }
+        row0 += c.nrows;
+    }
+    size_t bytes = (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max + sizeof(AttnItem) * (size_t)n_items;
+    NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, bytes, hipMemcpyHostToDevice, m->st));
+    m->stage_busy = true;
+    t->rows = (RowInfo*)m->d_tables;
+    t->comb = (CombineInfo*)(m->d_tables + sizeof(RowInfo) * P.R_max);
+    t->items = (AttnItem*)(m->d_tables + (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max);
+    t->R = R;
+    t->n_items = n_items;
+    return NV_OK;
+}
+
+// Run the layers of segment s (0-based) over the rows of the uploaded tables.
+nv_status run_segment(nv_model* m, int s, const Tables& t) {
+    const LayerDims D = m->dims();
+    const int d = m->d;
+    for (int l = s * m->seg; l < (s + 1) * m->seg; ++l) {
+        const LayerPtrs& W = m->layers[l];
+        GemmArgs g{};
+        g.eps = m->cfg.norm_eps;
+        g.wbf16 = m->bf16 ? 1 : 0;
+        g.R = t.R;
+        // q, k, v = RMSNorm(x) W_qkv^T
+        g.A = m->Hs;
+        g.lda = d;
+        g.a_rows = t.rows;
+        g.norm_w = W.attn_norm;
+        g.W = W.wqkv;
+        g.N = 3 * d;
+        g.K = d;
+        g.epi = EPI_STORE;
+        g.out = m->qkv;
+        g.ldo = 3 * d;
+        g.o_rows = nullptr;
+        NV_HIP(m, launch_gemm(g, m->st));
+        NV_HIP(m, launch_rope_kv(m->qkv, t.rows, t.R, m->kv, l, D, m->rope, m->st));
+        NV_HIP(m, launch_attn(t.items, t.n_items, t.rows, m->qkv, m->kv, l, D, m->part_ml, m->part_o, m->st));
+        NV_HIP(m, launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st));
+        // x += o W_o^T
+        g.A = m->attn_o;
+        g.lda = d;
+        g.a_rows = nullptr;
+        g.norm_w = nullptr;
+        g.W = W.wo;
+        g.N = d;
+        g.K = d;
+        g.epi = EPI_RESID;
+        g.out = m->Hs;
+        g.ldo = d;
+        g.o_rows = t.rows;
+        NV_HIP(m, launch_gemm(g, m->st));
+        // u = silu(RMSNorm(x) W_g^T) * (RMSNorm(x) W_u^T)
+        g.A = m->Hs;
+        g.lda = d;
+        g.a_rows = t.rows;
+        g.norm_w = W.mlp_norm;
+        g.W = W.wgu;
+        g.N = 2 * m->F;
+        g.K = d;
+        g.epi = EPI_SWIGLU;
+        g.out = m->mlp;
+        g.ldo = m->F;
+        g.o_rows = nullptr;
+        NV_HIP(m, launch_gemm(g, m->st));
+        // x += u W_d^T
+        g.A = m->mlp;
+        g.lda = m->F;
+        g.a_rows = nullptr;
+        g.norm_w = nullptr;
+        g.W = W.wd;
+        g.N = d;
+        g.K = m->F;
+        g.epi = EPI_RESID;
+        g.out = m->Hs;
+        g.ldo = d;
+        g.o_rows = t.rows;
+        NV_HIP(m, launch_gemm(g, m->st));
+    }
+    return NV_OK;
+}
+
+// Run segment s over a list of chunks, splitting into launch groups that fit the
+// workspace.  Pieces of one sequence go in ascending position order and in separate
+// groups, so each piece sees the KV of the pieces before it.
+nv_status run_chunks(nv_model* m, int s, const std::vector<Chunk>& chunks) {
+    const int cap = m->plan.R_max;
+    std::vector<Chunk> pieces;
+    for (const Chunk& c : chunks)
+        for (int o = 0; o < c.nrows; o += cap) pieces.push_back({c.seq, c.pos0 + o, std::min(cap, c.nrows - o)});
+    std::vector<bool> done(pieces.size(), false);
+    size_t left = pieces.size();
+    while (left > 0) {
+        std::vector<Chunk> group;
+        std::vector<int> seqs_in;
+        int rows = 0;
+        for (size_t i = 0; i < pieces.size(); ++i) {
+            if (done[i]) continue;
+            const Chunk& p = pieces[i];
+            bool seq_taken = std::find(seqs_in.begin(), seqs_in.end(), p.seq) != seqs_in.end();
+            if (seq_taken) continue;
+            seqs_in.push_back(p.seq);   // later pieces of this sequence wait for the next group
+            if (rows + p.nrows > cap) continue;
+            group.push_back(p);
+            rows += p.nrows;
+            done[i] = true;
+            --left;
+        }
+        Tables t;
+        nv_status st = upload_tables(m, group, &t);
+        if (st != NV_OK) return st;
+        st = run_segment(m, s, t);
+        if (st != NV_OK) return st;
+    }
+    return NV_OK;
+}
+
+nv_status check_seq(nv_model* m, int seq) {
+    if (!m) return NV_EINVAL;
+    if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
+    if (seq < 0 || seq >= m->max_batch) return fail(m, NV_EINVAL, "sequence index out of range");
+    return NV_OK;
+}
+
+}  // namespace
+
+// ==========================================================================================
+// C ABI
+// ==========================================================================================
+
+extern "C" {
+
+size_t nv_mem_required(const char* weights_path, int32_t max_batch, int32_t max_ctx) {
+    if (!weights_path || max_batch < 1 || max_ctx < 1) return 0;
+    nv_config c;
+    std::string err;
+    if (!read_header(weights_path, &c, &err)) return 0;
+    return make_plan(c, max_batch, max_ctx).total;
+}
+
+const char* nv_last_error(const nv_model* m) { return m ? m->err.c_str() : "null model handle"; }
+
+nv_status nv_get_config(const nv_model* m, nv_config* out) {
+    if (!m || !out) return NV_EINVAL;
+    *out = m->cfg;
+    return NV_OK;
+}
+
+void nv_free(nv_model* m) {
+    if (!m) return;
+    if (m->st) (void)hipStreamSynchronize(m->st);
+    if (m->own_arena && m->arena) (void)hipFree(m->arena);
+    if (m->h_stage) (void)hipHostFree(m->h_stage);
+    if (m->h_stepblk) (void)hipHostFree(m->h_stepblk);
+    if (m->h_gatelist) (void)hipHostFree(m->h_gatelist);
+    if (m->h_headlist) (void)hipHostFree(m->h_headlist);
+    if (m->h_out) (void)hipHostFree(m->h_out);
+    delete m;
+}
+
+nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* device_arena, size_t arena_bytes,
+                  void* hip_stream, nv_model** out) {
+    if (!path || !out || max_batch < 1 || max_ctx < 1) return NV_EINVAL;
+    *out = nullptr;
+    nv_model* m = new nv_model();
+    std::string err;
+    if (!read_header(path, &m->cfg, &err)) {
+        m->err = err;
+        *out = m;
+        return NV_EIO;
+    }
+    *out = m;
+    const nv_config& c = m->cfg;
+    m->L = c.n_layers;
+    m->d = c.d_model;
+    m->H = c.n_heads;
+    m->hd = c.head_dim;
+    m->F = c.ffn;
+    m->V = c.vocab;
+    m->seg = c.n_layers / kMaxExits;
+    m->bf16 = c.wdtype == 1;
+    m->max_batch = max_batch;
+    m->max_ctx = max_ctx;
+    m->plan = make_plan(c, max_batch, max_ctx);
+    const Plan& P = m->plan;
+    m->st = (hipStream_t)hip_stream;
+
+    // check the file length before touching the device
+    struct stat sb;
+    size_t need = 256;
+    {
+        const size_t d = m->d, F = m->F, V = m->V, es = P.es;
+        size_t off = 256;
+        auto adv = [&](size_t n) { off = align_up(off) + n; };
+        adv(V * d * es);
+        for (int l = 0; l < m->L; ++l) {
+            adv(d * 4);
+            adv(d * d * es);
+            adv(d * d * es);
+            adv(d * d * es);
+            adv(d * d * es);
+            adv(d * 4);
+            adv(F * d * es);
+            adv(F * d * es);
+            adv(d * F * es);
+        }
+        for (int k = 0; k < kMaxExits; ++k) {
+            adv(d * 4);
+            adv(d * 4);
+            adv(V * d * es);
+        }
+        need = off;
+    }
+    if (::stat(path, &sb) != 0 || (size_t)sb.st_size < need) return fail(m, NV_EIO, "weights file truncated");
+
+    if (device_arena) {
+        if (arena_bytes < P.total) return fail(m, NV_ECAPACITY, "device arena smaller than nv_mem_required()");
+        m->arena = (char*)device_arena;
+    } else {
+        NV_HIP(m, hipMalloc((void**)&m->arena, P.total));
+        m->own_arena = true;
+    }
+    m->arena = (char*)align_up((size_t)m->arena);
+    NV_HIP(m, init_kernel_attributes());
+
+    // carve the arena
+    m->embed = m->take(P.embed);
+    m->layers.resize(m->L);
+    for (int l = 0; l < m->L; ++l) {
+        LayerPtrs& W = m->layers[l];
+        W.attn_norm = (float*)m->take((size_t)m->d * 4);
+        W.mlp_norm = (float*)m->take((size_t)m->d * 4);
+        W.wqkv = m->take(3 * (size_t)m->d * m->d * P.es);
+        W.wo = m->take((size_t)m->d * m->d * P.es);
+        W.wgu = m->take(2 * (size_t)m->F * m->d * P.es);
+        W.wd = m->take((size_t)m->d * m->F * P.es);
+    }
+    for (int k = 0; k < kMaxExits; ++k) {
+        m->exits[k].gate_w = (float*)m->take((size_t)m->d * 4);
+        m->exits[k].norm = (float*)m->take((size_t)m->d * 4);
+        m->exits[k].head = m->take((size_t)m->V * m->d * P.es);
+        m->exits[k].bias = c.gate_bias[k];
+    }
+    m->Hs = (float*)m->take(P.hidden);
+    m->kv = m->take(P.kv);
+    m->rope = (float*)m->take(P.rope);
+    m->qkv = (float*)m->take(P.qkv);
+    m->attn_o = (float*)m->take(P.attn_o);
+    m->mlp = (float*)m->take(P.mlp);
+    m->part_ml = (float*)m->take(P.part_ml);
+    m->part_o = (float*)m->take(P.part_o);
+    m->d_tables = m->take(P.tables);
+    m->d_stepblk = m->take(m->stepblk_bytes());
+    m->d_gatelist = m->take(m->list_bytes());
+    m->d_headlist = m->take(m->list_bytes());
+    m->d_w = (double*)m->take((size_t)max_batch * 32);
+    m->d_stop = (int*)m->take((size_t)max_batch * 4);
+    m->d_tok_out = (int*)m->take((size_t)max_batch * 4);
+    m->logits = (float*)m->take(P.logits);
+    if (m->arena_off > P.total) return fail(m, NV_ECAPACITY, "internal: arena plan too small");
+
+    m->h_stage_bytes = P.tables;
+    NV_HIP(m, hipHostMalloc((void**)&m->h_stage, m->h_stage_bytes, hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_stepblk, m->stepblk_bytes(), hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_gatelist, m->list_bytes(), hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_headlist, m->list_bytes(), hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_out, (size_t)max_batch * 48, hipHostMallocDefault));
+
+    // weights: file tensors -> pinned bounce buffer -> device (repacking W_gate/W_up rows)
+    int fd = ::open(path, O_RDONLY);
+    if (fd < 0) return fail(m, NV_EIO, "cannot open weights file");
+    const size_t d = m->d, F = m->F, V = m->V, es = P.es;
+    const size_t bounce_bytes = 64ull << 20;
+    char* bounce = nullptr;
+    if (hipHostMalloc((void**)&bounce, bounce_bytes, hipHostMallocDefault) != hipSuccess) {
+        ::close(fd);
+        m->dead = true;
+        return fail(m, NV_EDEVICE, "hipHostMalloc failed for the load buffer");
+    }
+    size_t off = 256;
+    bool io_ok = true;
+    hipError_t herr = hipSuccess;
+    auto copy_tensor = [&](void* dst, size_t nbytes) {
+        off = align_up(off);
+        size_t done = 0;
+        while (io_ok && herr == hipSuccess && done < nbytes) {
+            size_t n = std::min(bounce_bytes, nbytes - done);
+            if (!pread_all(fd, bounce, n, off + done)) {
+                io_ok = false;
+                break;
+            }
+            herr = hipMemcpy((char*)dst + done, bounce, n, hipMemcpyHostToDevice);
+            done += n;
+        }
+        off += nbytes;
+    };
+    // W_gate rows go to even rows of wgu, W_up rows to odd rows.
+    auto copy_interleaved = [&](void* dst, size_t rows, size_t row_bytes, int parity) {
+        off = align_up(off);
+        const size_t rows_per = bounce_bytes / row_bytes;
+        size_t done = 0;
+        while (io_ok && herr == hipSuccess && done < rows) {
+            size_t n = std::min(rows_per, rows - done);
+            if (!pread_all(fd, bounce, n * row_bytes, off + done * row_bytes)) {
+                io_ok = false;
+                break;
+            }
+            herr = hipMemcpy2D((char*)dst + (2 * done + parity) * row_bytes, 2 * row_bytes, bounce, row_bytes,
+                               row_bytes, n, hipMemcpyHostToDevice);
+            done += n;
+        }
+        off += rows * row_bytes;
+    };
+    copy_tensor(m->embed, V * d * es);
+    for (int l = 0; l < m->L && io_ok && herr == hipSuccess; ++l) {
+        LayerPtrs& W = m->layers[l];
+        copy_tensor(W.attn_norm, d * 4);
+        copy_tensor(W.wqkv, d * d * es);
+        copy_tensor((char*)W.wqkv + d * d * es, d * d * es);
+        copy_tensor((char*)W.wqkv + 2 * d * d * es, d * d * es);
+        copy_tensor(W.wo, d * d * es);
+        copy_tensor(W.mlp_norm, d * 4);
+        copy_interleaved(W.wgu, F, d * es, 0);
+        copy_interleaved(W.wgu, F, d * es, 1);
+        copy_tensor(W.wd, d * F * es);
+    }
+    for (int k = 0; k < kMaxExits && io_ok && herr == hipSuccess; ++k) {
+        copy_tensor(m->exits[k].gate_w, d * 4);
+        copy_tensor(m->exits[k].norm, d * 4);
+        copy_tensor(m->exits[k].head, V * d * es);
+    }
+    ::close(fd);
+    (void)hipHostFree(bounce);
+    if (!io_ok) return fail(m, NV_EIO, "weights file read failed");
+    NV_HIP(m, herr);
+    NV_HIP(m, launch_rope_table(m->rope, max_ctx, m->hd, c.rope_base, m->st));
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    m->seqs.assign(max_batch, SeqHost());
+    m->last_w.assign((size_t)max_batch * 4, NAN);
+    return NV_OK;
+}
+
+nv_status nv_prefill(nv_model* m, int32_t seq, const int32_t* tokens, int32_t n) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!tokens || n < 1) return fail(m, NV_EINVAL, "prefill needs at least one token");
+    if (n > m->max_ctx) return fail(m, NV_ECAPACITY, "prompt longer than max_ctx");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->V) return fail(m, NV_EINVAL, "token id out of range");
+    SeqHost& S = m->seqs[seq];
+    S = SeqHost();
+    S.live = true;
+    S.pending = tokens[n - 1];
+    const int np = n - 1;
+    // embed positions 0..np-1 in pieces
+    const int cap = m->plan.R_max;
+    for (int o = 0; o < np; o += cap) {
+        const int k = std::min(cap, np - o);
+        if ((s = stage_sync(m)) != NV_OK) return s;
+        RowInfo* hr = (RowInfo*)m->h_stage;
+        int* ht = (int*)(m->h_stage + sizeof(RowInfo) * k);
+        for (int i = 0; i < k; ++i) {
+            hr[i] = RowInfo{seq * m->max_ctx + o + i, seq, o + i, 0};
+            ht[i] = tokens[o + i];
+        }
+        NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, (sizeof(RowInfo) + 4) * k, hipMemcpyHostToDevice, m->st));
+        m->stage_busy = true;
+        NV_HIP(m, launch_embed((const int*)(m->d_tables + sizeof(RowInfo) * k), (const RowInfo*)m->d_tables, k,
+                               m->embed, m->bf16, m->Hs, m->d, m->st));
+    }
+    if (np > 0) {
+        std::vector<Chunk> ch{{seq, 0, np}};
+        for (int sg = 0; sg < kMaxExits; ++sg)
+            if ((s = run_chunks(m, sg, ch)) != NV_OK) return s;
+    }
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    m->stage_busy = false;
+    S.n = np;
+    for (int k = 0; k < kMaxExits; ++k) S.f[k] = np;
+    for (int k = 0; k < 4; ++k) m->last_w[(size_t)seq * 4 + k] = NAN;
+    return NV_OK;
+}
+
+static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, int32_t* tok_out, int32_t* exit_out) {
+    if (!m) return NV_EINVAL;
+    if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
+    if (!u || !tok_out || !exit_out) return fail(m, NV_EINVAL, "null pointer");
+    int n = 0;
+    while (n < m->max_batch && m->seqs[n].live) ++n;
+    if (n == 0) return fail(m, NV_ESTATE, "no prefilled sequence");
+    for (int i = n; i < m->max_batch; ++i)
+        if (m->seqs[i].live) return fail(m, NV_ESTATE, "prefilled sequences are not numbered 0..n-1");
+    for (int i = 0; i < n * 4; ++i)
+        if (!(u[i] >= 0.0f && u[i] < 1.0f)) return fail(m, NV_EINVAL, "uniform outside [0,1) or NaN");
+    if (forced)
+        for (int i = 0; i < n; ++i)
+            if (forced[i] < 0 || forced[i] >= m->V) return fail(m, NV_EINVAL, "forced token out of range");
+    for (int i = 0; i < n; ++i)
+        if (m->seqs[i].n + 1 > m->max_ctx) return fail(m, NV_ECAPACITY, "sequence reached max_ctx");
+
+    nv_status s = stage_sync(m);
+    if (s != NV_OK) return s;
+    // uniforms, pending tokens and current-position rows in one upload
+    char* hb = m->h_stepblk;
+    std::memcpy(nv_model::unif(hb), u, (size_t)n * 16);
+    for (int i = 0; i < n; ++i) {
+        m->tok_in(hb)[i] = m->seqs[i].pending;
+        m->cur_rows(hb)[i] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
+    }
+    NV_HIP(m, hipMemcpyAsync(m->d_stepblk, hb, m->stepblk_bytes(), hipMemcpyHostToDevice, m->st));
+    const float* d_unif = nv_model::unif(m->d_stepblk);
+    NV_HIP(m, launch_embed(m->tok_in(m->d_stepblk), m->cur_rows(m->d_stepblk), n, m->embed, m->bf16, m->Hs, m->d,
+                           m->st));
+
+    std::vector<int> active(n), exit_of(n, kMaxExits);
+    for (int i = 0; i < n; ++i) active[i] = i;
+    for (int i = 0; i < n * 4; ++i) m->last_w[i] = NAN;
+    int* hstop = (int*)m->h_out;
+    int* htok_out = (int*)(m->h_out + (size_t)m->max_batch * 4);
+    double* hw = (double*)(m->h_out + (size_t)m->max_batch * 8);
+    for (int sg = 0; sg < kMaxExits && !active.empty(); ++sg) {
+        std::vector<Chunk> ch;
+        for (int i : active) {
+            const SeqHost& S = m->seqs[i];
+            ch.push_back({i, S.f[sg], S.n - S.f[sg] + 1});
+        }
+        if ((s = run_chunks(m, sg, ch)) != NV_OK) return s;
+        std::vector<int> stopping;
+        if (sg < kMaxExits - 1) {
+            // router gate on the current rows of the active sequences; the walk's decision
+            // comes back to the host, which launches the next segment or the head
+            char* gl = m->h_gatelist;
+            const int na = (int)active.size();
+            for (int j = 0; j < na; ++j) {
+                const int i = active[j];
+                nv_model::lseqs(gl)[j] = i;
+                m->lrows(gl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
+            }
+            NV_HIP(m, hipMemcpyAsync(m->d_gatelist, gl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
+            NV_HIP(m, launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs,
+                                  m->d, m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop,
+                                  m->st));
+            NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
+            NV_HIP(m, hipStreamSynchronize(m->st));
+            m->stage_busy = false;
+            std::vector<int> rest;
+            for (int i : active) (hstop[i] ? stopping : rest).push_back(i);
+            active.swap(rest);
+        } else {
+            stopping = active;
+            active.clear();
+        }
+        if (!stopping.empty()) {
+            // exit RMSNorm + the exit's own LM head for the stopping sequences, logits into
+            // row `seq` of the logits buffer, then the inverse-CDF draw
+            char* hl = m->h_headlist;
+            const int ns = (int)stopping.size();
+            for (int j = 0; j < ns; ++j) {
+                const int i = stopping[j];
+                exit_of[i] = sg + 1;
+                nv_model::lseqs(hl)[j] = i;
+                m->lrows(hl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
+                m->lorows(hl)[j] = RowInfo{i, i, 0, 0};
+            }
+            NV_HIP(m, hipMemcpyAsync(m->d_headlist, hl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
+            GemmArgs g{};
+            g.A = m->Hs;
+            g.lda = m->d;
+            g.a_rows = m->lrows(m->d_headlist);
+            g.norm_w = m->exits[sg].norm;
+            g.eps = m->cfg.norm_eps;
+            g.W = m->exits[sg].head;
+            g.N = m->V;
+            g.K = m->d;
+            g.R = ns;
+            g.wbf16 = m->bf16 ? 1 : 0;
+            g.epi = EPI_STORE;
+            g.out = m->logits;
+            g.ldo = m->V;
+            g.o_rows = m->lorows(m->d_headlist);
+            NV_HIP(m, launch_gemm(g, m->st));
+            NV_HIP(m, launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif,
+                                    m->d_tok_out, m->st));
+        }
+    }
+    NV_HIP(m, hipMemcpyAsync(htok_out, m->d_tok_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
+    NV_HIP(m, hipMemcpyAsync(hw, m->d_w, (size_t)n * 32, hipMemcpyDeviceToHost, m->st));
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    m->stage_busy = false;
+    for (int i = 0; i < n; ++i) {
+        SeqHost& S = m->seqs[i];
+        const int e = exit_of[i];
+        for (int k = 0; k < e && k < kMaxExits - 1; ++k) m->last_w[(size_t)i * 4 + k] = hw[i * 4 + k];
+        if (e == kMaxExits) m->last_w[(size_t)i * 4 + 3] = 1.0;
+        for (int k = 0; k < e; ++k) S.f[k] = S.n + 1;
+        S.n += 1;
+        S.last_exit = e;
+        tok_out[i] = htok_out[i];
+        exit_out[i] = e;
+        S.pending = forced ? forced[i] : htok_out[i];
+    }
+    return NV_OK;
+}
+
+nv_status nv_step(nv_model* m, const float* uniforms, int32_t* tokens_out, int32_t* exits_out) {
+    return step_impl(m, uniforms, nullptr, tokens_out, exits_out);
+}
+
+nv_status nv_step_forced(nv_model* m, const float* uniforms, const int32_t* next_inputs, int32_t* tokens_out,
+                         int32_t* exits_out) {
+    if (!next_inputs) return m ? fail(m, NV_EINVAL, "null next_inputs") : NV_EINVAL;
+    return step_impl(m, uniforms, next_inputs, tokens_out, exits_out);
+}
+
+nv_status nv_flush(nv_model* m, int32_t seq) {
+    if (!m) return NV_EINVAL;
+    if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
+    if (seq < -1 || seq >= m->max_batch) return fail(m, NV_EINVAL, "sequence index out of range");
+    std::vector<int> targets;
+    for (int i = 0; i < m->max_batch; ++i)
+        if (m->seqs[i].live && (seq == -1 || seq == i)) targets.push_back(i);
+    nv_status s;
+    for (int sg = 1; sg < kMaxExits; ++sg) {
+        std::vector<Chunk> ch;
+        for (int i : targets) {
+            const SeqHost& S = m->seqs[i];
+            if (S.n > S.f[sg]) ch.push_back({i, S.f[sg], S.n - S.f[sg]});
+        }
+        if (!ch.empty() && (s = run_chunks(m, sg, ch)) != NV_OK) return s;
+        for (int i : targets) m->seqs[i].f[sg] = m->seqs[i].n;
+    }
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    m->stage_busy = false;
+    return NV_OK;
+}
+
+nv_status nv_debug_frontiers(nv_model* m, int32_t seq, int32_t* n_consumed, int32_t frontier[4]) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!n_consumed || !frontier) return fail(m, NV_EINVAL, "null pointer");
+    *n_consumed = m->seqs[seq].n;
+    for (int k = 0; k < kMaxExits; ++k) frontier[k] = m->seqs[seq].f[k];
+    return NV_OK;
+}
+
+nv_status nv_debug_logits(nv_model* m, int32_t seq, float* out) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!out) return fail(m, NV_EINVAL, "null pointer");
+    NV_HIP(m, hipMemcpy(out, m->logits + (size_t)seq * m->V, (size_t)m->V * 4, hipMemcpyDeviceToHost));
+    return NV_OK;
+}
+
+nv_status nv_debug_gates(nv_model* m, int32_t seq, double* out) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!out) return fail(m, NV_EINVAL, "null pointer");
+    for (int k = 0; k < 4; ++k) out[k] = m->last_w[(size_t)seq * 4 + k];
+    return NV_OK;
+}
+
+nv_status nv_debug_kv(nv_model* m, int32_t seq, int32_t layer, int32_t pos0, int32_t n, float* k_out,
+                      float* v_out) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!k_out || !v_out || layer < 0 || layer >= m->L || pos0 < 0 || n < 0 || pos0 + n > m->max_ctx)
+        return fail(m, NV_EINVAL, "bad kv range");
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    const size_t kes = m->plan.kes;
+    std::vector<char> buf((size_t)n * m->hd * kes);
+    for (int which = 0; which < 2; ++which)
+        for (int h = 0; h < m->H; ++h) {
+            const size_t base = ((((size_t)seq * m->L + layer) * 2 + which) * m->H + h) * (size_t)m->max_ctx * m->hd;
+            NV_HIP(m, hipMemcpy(buf.data(), (char*)m->kv + (base + (size_t)pos0 * m->hd) * kes, buf.size(),
+                                hipMemcpyDeviceToHost));
+            float* dst = which ? v_out : k_out;
+            for (int p = 0; p < n; ++p)
+                for (int e = 0; e < m->hd; ++e) {
+                    float v;
+                    const size_t i = (size_t)p * m->hd + e;
+                    if (kes == 2) {
+                        uint32_t b = ((uint32_t)((uint16_t*)buf.data())[i]) << 16;
+                        std::memcpy(&v, &b, 4);
+                    } else {
+                        v = ((float*)buf.data())[i];
+                    }
+                    dst[((size_t)p * m->H + h) * m->hd + e] = v;
+                }
+        }
+    return NV_OK;
+}
+
+nv_status nv_debug_hidden(nv_model* m, int32_t seq, int32_t pos0, int32_t n, float* out) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!out || pos0 < 0 || n < 0 || pos0 + n > m->max_ctx) return fail(m, NV_EINVAL, "bad hidden range");
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    NV_HIP(m, hipMemcpy(out, m->Hs + ((size_t)seq * m->max_ctx + pos0) * m->d, (size_t)n * m->d * 4,
+                        hipMemcpyDeviceToHost));
+    return NV_OK;
+}
+
+}  // extern "C"
