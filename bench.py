@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Decode throughput of the N-vium mixture-of-exits step on one MI355X.
+
+Workload (default "A"): the 1.5B N-vium (48 layers, d 1536, 12 x 128 heads, SwiGLU
+4096, vocab 32000, bf16 weights and KV), batch 1, a 512-token uniform-random
+prompt, then `--steps` decode steps (512 = the full workload) with seeded uniforms;
+random-init weights (seed 0), exit mass ~[.4,.25,.2,.15].  A step is one nv_step:
+embed, every reached segment with its deferred chunk, the gates walked, one exit
+head and the draw.  Inputs are resident in device memory before timing starts.
+
+Printed: one JSON line.  `value` = generated tokens/s over the timed steps.
+Beside it: the same kernels with every intermediate gate closed (all tokens exit at
+4, standard decode), per-kernel-class device time from HIP events in a second,
+identical pass (roofline of the block GEMM against 8 TB/s), and the CPU oracle
+timed on a bounded sample of the same decode.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def run_decode(lib, h, prompt, U, steps, warmup):
+    """Warm up, restart the sequence, then time `steps` decode steps."""
+    import torch
+    lib.nv_prefill(h, 0, prompt)
+    for t in range(warmup):
+        lib.nv_step(h, U[t:t + 1])
+    lib.nv_prefill(h, 0, prompt)
+    exits = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(steps):
+        _, ex = lib.nv_step(h, U[t:t + 1])
+        exits.append(int(ex[0]))
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, exits
+
+
+def timing_pass(lib, h, prompt, U, steps):
+    lib.nv_prefill(h, 0, prompt)
+    lib.nv_timing_enable(h, True)
+    for t in range(steps):
+        lib.nv_step(h, U[t:t + 1])
+    res = lib.nv_timing_read(h)
+    lib.nv_timing_enable(h, False)
+    return res
+
+
+def cpu_baseline(wl, path, prompt, U, budget_s):
+    """The oracle (float64 NumPy) on the host: decode steps after an untimed prefill."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import model as om
+    M = om.OracleModel(path)
+    st = om.new_state(M, len(prompt) + len(U))
+    om.prefill(M, st, prompt[:-1])
+    y = int(prompt[-1])
+    n = 0
+    t0 = time.perf_counter()
+    while n < len(U):
+        o = om.decode_step(M, st, y, U[n], all_heads=False)
+        y = o.token
+        n += 1
+        if time.perf_counter() - t0 > budget_s and n >= 2:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} decode steps of workload {wl.name} (positions {len(prompt) - 1}.."
+                      f"{len(prompt) - 2 + n}) after an untimed {len(prompt) - 1}-token prefill, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="A")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the exit-4-forced run")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path "
+              f"is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from dataclasses import replace
+
+    from mixture_exits_transformer_amd import lib
+    from synth import cached_weights, prompts, uniforms, workload
+    from synth.configs import BIAS_ALL_LAST
+
+    torch.cuda.set_device(0)
+    wl = workload(args.workload)
+    assert wl.batch == 1, "bench.py times the batch-1 workloads"
+    steps, warmup = args.steps, args.warmup
+    prompt = prompts(wl)[0]
+    U = uniforms(wl, steps=max(steps, warmup))[:, 0, :]
+    max_ctx = len(prompt) + max(steps, warmup)
+
+    path = cached_weights(wl.model)
+    h = lib.nv_load(path, 1, max_ctx)
+    dt, exits = run_decode(lib, h, prompt, U, steps, warmup)
+    tim = timing_pass(lib, h, prompt, U, steps)
+    lib.nv_free(h)
+    tok_s = steps / dt
+
+    base = None
+    if not args.no_baseline:
+        m4 = replace(wl.model, gate_bias=BIAS_ALL_LAST)
+        h4 = lib.nv_load(cached_weights(m4), 1, max_ctx)
+        dt4, ex4 = run_decode(lib, h4, prompt, U, steps, warmup)
+        lib.nv_free(h4)
+        assert set(ex4) == {4}
+        base = steps / dt4
+
+    ms, by, nl = tim["block_gemm"]
+    achieved = by / (ms * 1e-3) / 1e9
+    hist = np.bincount(np.asarray(exits), minlength=5)[1:]
+    out = {
+        "metric": "generated tokens/s, 1.5B bs=1, vs exit-4-forced decode; achieved HBM GB/s",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(dt / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.model.wdtype,
+        "data": "synthetic: uniform-random token ids, seeded uniforms, random-init N(0,0.02) weights",
+        "config": {"workload": f"{wl.name}: {wl.note}", "batch": wl.batch, "prompt": len(prompt),
+                   "decode_steps": steps},
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_valu (transformer-block skinny GEMMs)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
+                     "bytes_per_launch": round(by / max(nl, 1))},
+        "kernel_classes_ms_per_step": {k: round(v[0] / steps, 4) for k, v in tim.items()},
+        "exit4_forced_tokens_per_s": round(base, 2) if base else None,
+        "speedup_vs_exit4": round(tok_s / base - 1.0, 4) if base else None,
+        "exit_histogram": [int(x) for x in hist],
+        "mean_segments_per_token": round(float(np.mean(exits)), 4),
+        "pages_reference": "57.9% wall-clock speedup at 1.5B on unspecified hardware (context only)",
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, path, prompt, U[:steps], args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

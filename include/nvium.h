@@ -138,6 +138,25 @@ nv_status nv_debug_kv(nv_model *m, int32_t seq, int32_t layer, int32_t pos0, int
  * of the last segment each position completed. */
 nv_status nv_debug_hidden(nv_model *m, int32_t seq, int32_t pos0, int32_t n, float *out);
 
+/* ---- kernel timing (measurement; adds events between launches) ------------------ */
+
+/* Kernel classes timed by nv_timing_*: */
+#define NV_TIME_BLOCK_GEMM 0   /* the transformer-block skinny GEMMs (QKV, O, gate/up, down) */
+#define NV_TIME_ATTENTION 1    /* RoPE + KV append, chunked attention, split combine */
+#define NV_TIME_EXIT_HEAD 2    /* exit RMSNorm + LM-head GEMV */
+#define NV_TIME_OTHER 3        /* embedding gather, router gates, sampling */
+#define NV_TIME_CLASSES 4
+
+/* on != 0: from now on bracket every kernel launch with HIP events on the model's
+ * stream and accumulate per-class device time, launch counts and algorithmic bytes
+ * (bytes each launch must move at minimum: weights read once, activations in/out,
+ * keys/values read); on == 0: stop.  Either way the counters restart at zero. */
+nv_status nv_timing_enable(nv_model *m, int32_t on);
+
+/* Totals since nv_timing_enable: ms[k] device milliseconds, bytes[k] algorithmic
+ * bytes and launches[k] launches of class k, for k < NV_TIME_CLASSES. */
+nv_status nv_timing_read(nv_model *m, double *ms, double *bytes, int64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif

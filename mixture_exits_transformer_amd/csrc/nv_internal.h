@@ -7,7 +7,11 @@ namespace nv {
 
 struct RowInfo;
 
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+
+struct LayerDims {
+    int L, d, H, hd, F, V, max_ctx, kv_bf16;
+};
 
 // out[i][n] (+)= sum_k A'[i][k] * W[n][k], where A' is row i of A, RMSNormed when
 // norm_w is set.  Rows of A and of out are addressed through optional index lists
@@ -23,9 +27,21 @@ struct GemmArgs {
     int wbf16;
     int epi;              // EPI_STORE: out = acc; EPI_RESID: out += acc;
                           // EPI_SWIGLU: columns (2j, 2j+1) = (gate_j, up_j), out[j] = silu(g) * u
+                          // EPI_QKV: columns (2p, 2p+1) are rotation partners (see below):
+                          //   q -> RoPE -> q_out[row]; k -> RoPE -> KV cache; v -> KV cache
     float* out;
     int64_t ldo;
     const struct RowInfo* o_rows;  // row i of out is out + o_rows[i].hrow * ldo (identity if null)
+    int head;             // 1: an exit head (separate kernel symbol, so profiles tell them apart)
+    float* rms_ws;        // [R] scratch for per-row inverse RMS (matrix-core path with norm_w)
+    int mfma_min_rows;    // use the matrix-core path when R >= this (0: never)
+    // EPI_QKV only.  Weight row 2p + i (i = 0, 1) of the fused QKV matrix is original
+    // row part*d + h*hd + j + i*hd/2, where p = part*(d/2) + h*(hd/2) + j, part 0/1/2 = q/k/v.
+    float* q_out;         // [R][d]
+    void* kv;
+    const float* rope;    // [max_ctx][hd/2] (cos, sin)
+    int layer;
+    LayerDims D;
 };
 
 // One row of a chunk: position `pos` of sequence `seq`; hrow = seq * max_ctx + pos
@@ -38,7 +54,9 @@ struct RowInfo {
 // positions of one sequence) against keys/values at positions [lo, hi) of head `head`.
 // Partial results go to slots part + r (r < nrows).
 struct AttnItem {
-    int row0, nrows, head, lo, hi, part, pad0, pad1;
+    int row0, nrows, head, lo, hi, part;
+    int split, nsplit;    // split index and count over the key range of (row block, head)
+    int pad[4];
 };
 
 // Where the split partials of compact row i live: slot(h, s) =
@@ -47,20 +65,22 @@ struct CombineInfo {
     int base, off, nsplit, nrows;
 };
 
-struct LayerDims {
-    int L, d, H, hd, F, V, max_ctx, kv_bf16;
-};
-
 // Launch wrappers (nv_kernels.hip).
 hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStream_t st);
 hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const void* E, int wbf16,
                         float* Hs, int d, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-hipError_t launch_rope_kv(float* qkv, const RowInfo* rows, int R, void* kv, int layer,
-                          const LayerDims& D, const float* cs, hipStream_t st);
-hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* qkv,
+// Decode-sized row blocks (<= ATTN_DEC_ROWS rows): each item is one split of one
+// (row block, head); split partials are merged by launch_attn_combine.
+constexpr int ATTN_DEC_ROWS = 8;
+constexpr int ATTN_DEC_ITERS = 4;
+constexpr int ATTN_COMB_MAX = 4096;      // (head, split) pairs per row the combine pass holds   // key groups per wave: a split covers <= 16 * (512 / head_dim) keys
+hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
+                           const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
+                           float* out, hipStream_t st);
+hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
                        const void* kv, int layer, const LayerDims& D, float* part_ml,
-                       float* part_o, hipStream_t st);
+                       float* part_o, float* out, hipStream_t st);
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
                                const float* part_ml, const float* part_o, float* out,
                                hipStream_t st);

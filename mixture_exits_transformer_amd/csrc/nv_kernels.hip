@@ -36,6 +36,23 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Cross-lane adds with DPP (no LDS traffic).  quad_perm [1,0,3,2] and [2,3,0,1] pair lanes
+// within a quad; row_half_mirror / row_mirror pair lane i with 7-i / 15-i of its 8 / 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of G lanes (G = 4, 8 or 16); every lane of a group gets the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    if constexpr (G >= 8) v += dpp_f<0x141>(v);
+    if constexpr (G >= 16) v += dpp_f<0x140>(v);
+    return v;
+}
+
 __device__ __forceinline__ float kv_load(const void* kv, int bf16, int64_t i) {
     if (bf16) return __uint_as_float(((uint32_t)((const uint16_t*)kv)[i]) << 16);
     return ((const float*)kv)[i];
@@ -97,8 +114,239 @@ hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const voi
     return hipGetLastError();
 }
 
+
 // ------------------------------------------------------------------------------------------
-// Skinny GEMM on the vector ALUs.  Each block owns GV_COLS consecutive output columns,
+// Epilogue for a pair of adjacent output columns (n, n+1), n even, of row `row`.
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, float v0, float v1) {
+    if (a.epi == EPI_SWIGLU) {
+        const int orow = a.o_rows ? a.o_rows[row].hrow : row;
+        a.out[(int64_t)orow * a.ldo + (n >> 1)] = v0 / (1.0f + expf(-v0)) * v1;
+        return;
+    }
+    if (a.epi == EPI_QKV) {
+        // columns n, n+1 hold rotation partners j and j + hd/2 of one head of q, k or v
+        const RowInfo ri = a.a_rows[row];
+        const LayerDims& D = a.D;
+        const int half = D.hd >> 1;
+        const int p = n >> 1;
+        const int part = p / (D.d >> 1);
+        const int pp = p - part * (D.d >> 1);
+        const int h = pp / half, j = pp - h * half;
+        if (part == 2) {
+            const int64_t b = kv_base(D, ri.seq, a.layer, 1, h) + (int64_t)ri.pos * D.hd;
+            kv_store(a.kv, D.kv_bf16, b + j, v0);
+            kv_store(a.kv, D.kv_bf16, b + j + half, v1);
+            return;
+        }
+        const float c = a.rope[((int64_t)ri.pos * half + j) * 2];
+        const float s = a.rope[((int64_t)ri.pos * half + j) * 2 + 1];
+        const float r0 = v0 * c - v1 * s, r1 = v1 * c + v0 * s;
+        if (part == 0) {
+            float* q = a.q_out + (int64_t)row * D.d + h * D.hd;
+            q[j] = r0;
+            q[j + half] = r1;
+        } else {
+            const int64_t b = kv_base(D, ri.seq, a.layer, 0, h) + (int64_t)ri.pos * D.hd;
+            kv_store(a.kv, D.kv_bf16, b + j, r0);
+            kv_store(a.kv, D.kv_bf16, b + j + half, r1);
+        }
+        return;
+    }
+    const int orow = a.o_rows ? a.o_rows[row].hrow : row;
+    float* o = a.out + (int64_t)orow * a.ldo + n;
+    if (a.epi == EPI_STORE) {
+        o[0] = v0;
+        o[1] = v1;
+    } else {
+        o[0] += v0;
+        o[1] += v1;
+    }
+}
+
+
+// What the epilogue of one (row, column pair) needs from memory, fetched early so the
+// epilogue itself issues no dependent loads.
+struct EpiCtx {
+    int orow;      // output row (hidden-state row for EPI_RESID)
+    int seq, pos;  // EPI_QKV: sequence and position of the row
+    float c, s;    // EPI_QKV: RoPE cos / sin for this pair
+};
+
+__device__ __forceinline__ EpiCtx epi_prepare(const GemmArgs& a, int row, int n) {
+    EpiCtx e{};
+    if (a.epi == EPI_QKV) {
+        const RowInfo ri = a.a_rows[row];
+        e.seq = ri.seq;
+        e.pos = ri.pos;
+        const int half = a.D.hd >> 1;
+        const int p = n >> 1;
+        const int pp = p % (a.D.d >> 1);
+        const int j = pp % half;
+        e.c = a.rope[((int64_t)ri.pos * half + j) * 2];
+        e.s = a.rope[((int64_t)ri.pos * half + j) * 2 + 1];
+    } else {
+        e.orow = a.o_rows ? a.o_rows[row].hrow : row;
+    }
+    return e;
+}
+
+__device__ __forceinline__ void epi_apply(const GemmArgs& a, const EpiCtx& e, int row, int n, float v0, float v1) {
+    if (a.epi == EPI_SWIGLU) {
+        a.out[(int64_t)e.orow * a.ldo + (n >> 1)] = v0 / (1.0f + expf(-v0)) * v1;
+    } else if (a.epi == EPI_QKV) {
+        const LayerDims& D = a.D;
+        const int half = D.hd >> 1;
+        const int p = n >> 1;
+        const int part = p / (D.d >> 1);
+        const int pp = p - part * (D.d >> 1);
+        const int h = pp / half, j = pp - h * half;
+        if (part == 2) {
+            const int64_t b = kv_base(D, e.seq, a.layer, 1, h) + (int64_t)e.pos * D.hd;
+            kv_store(a.kv, D.kv_bf16, b + j, v0);
+            kv_store(a.kv, D.kv_bf16, b + j + half, v1);
+            return;
+        }
+        const float r0 = v0 * e.c - v1 * e.s, r1 = v1 * e.c + v0 * e.s;
+        if (part == 0) {
+            float* q = a.q_out + (int64_t)row * D.d + h * D.hd;
+            q[j] = r0;
+            q[j + half] = r1;
+        } else {
+            const int64_t b = kv_base(D, e.seq, a.layer, 0, h) + (int64_t)e.pos * D.hd;
+            kv_store(a.kv, D.kv_bf16, b + j, r0);
+            kv_store(a.kv, D.kv_bf16, b + j + half, r1);
+        }
+    } else {
+        float* o = a.out + (int64_t)e.orow * a.ldo + n;
+        if (a.epi == EPI_STORE) {
+            o[0] = v0;
+            o[1] = v1;
+        } else {
+            o[0] += v0;
+            o[1] += v1;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMV-shaped products (R <= GV_RMAX rows) on the vector ALUs.  Each wave owns CPW adjacent
+// output columns; lanes span K in 16-byte chunks (chunk c of a row is read by lane c % 64,
+// so one instruction reads 1 KB of a weight row, fully coalesced).  All of a wave's
+// weight loads are issued before the activation rows are staged (RMSNormed, fp32) into
+// LDS, so the weight stream is in flight while the prologue runs.  Each (row, column) dot
+// product ends with a wavefront reduction.
+// ------------------------------------------------------------------------------------------
+
+constexpr int GV_RMAX = 8;
+
+template <bool WBF, int CPW, int CH, int HEAD>
+__global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
+    extern __shared__ float sm[];
+    constexpr int EPC = WBF ? 8 : 4;
+    constexpr int ESZ = WBF ? 2 : 4;
+    const int K = a.K, R = a.R;
+    const int nch = K / EPC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = (blockIdx.x * 4 + wave) * CPW;
+    float* As = sm;
+    float* inv = sm + R * K;
+
+    uint4 w[CPW][CH];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const uint4* wp = (const uint4*)((const char*)a.W + (size_t)(n0 + c) * K * ESZ);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int ch = lane + 64 * j;
+            w[c][j] = ch < nch ? wp[ch] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    for (int r = wave; r < R; r += 4) {
+        const int ar = a.a_rows ? a.a_rows[r].hrow : r;
+        const float* src = a.A + (int64_t)ar * a.lda;
+        float ss = 0.f;
+        if (a.norm_w) {
+            for (int k = lane; k < K; k += 64) ss += src[k] * src[k];
+            ss = wave_sum(ss);
+        }
+        if (lane == 0) inv[r] = a.norm_w ? 1.0f / sqrtf(ss / (float)K + a.eps) : 1.0f;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x * 4; idx < R * K; idx += blockDim.x * 4) {
+        const int r = idx / K, k = idx - r * K;      // K % 4 == 0: a float4 stays in one row
+        const int ar = a.a_rows ? a.a_rows[r].hrow : r;
+        float4 v = *(const float4*)(a.A + (int64_t)ar * a.lda + k);
+        const float iv = inv[r];
+        v.x *= iv; v.y *= iv; v.z *= iv; v.w *= iv;
+        if (a.norm_w) {
+            const float4 g = *(const float4*)(a.norm_w + k);
+            v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+        }
+        *(float4*)(As + idx) = v;
+    }
+    __syncthreads();
+
+    float acc[CPW][GV_RMAX];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int r = 0; r < GV_RMAX; ++r) acc[c][r] = 0.f;
+
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int ch = lane + 64 * j;
+        if (ch < nch) {
+            float wf[CPW][EPC];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const uint32_t u[4] = {w[c][j].x, w[c][j].y, w[c][j].z, w[c][j].w};
+                if constexpr (WBF) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        wf[c][2 * e] = bf_lo(u[e]);
+                        wf[c][2 * e + 1] = bf_hi(u[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) wf[c][e] = __uint_as_float(u[e]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < GV_RMAX; ++r) {
+                if (r < R) {
+                    float av[EPC];
+                    const float4* ap = (const float4*)(As + r * K + ch * EPC);
+#pragma unroll
+                    for (int e = 0; e < EPC / 4; ++e) {
+                        const float4 t = ap[e];
+                        av[4 * e] = t.x; av[4 * e + 1] = t.y; av[4 * e + 2] = t.z; av[4 * e + 3] = t.w;
+                    }
+#pragma unroll
+                    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) acc[c][r] = fmaf(wf[c][e], av[e], acc[c][r]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < GV_RMAX; ++r) {
+        if (r < R) {
+            float v[CPW];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) v[c] = wave_sum(acc[c][r]);
+            if (lane == 0) {
+#pragma unroll
+                for (int c = 0; c < CPW; c += 2) epi_pair(a, r, n0 + c, v[c], v[c + 1]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Row-tiled GEMM on the vector ALUs (fp32 weights or no matrix-core shape), any R.  Each block owns GV_COLS consecutive output columns,
 // two per wave (so a SwiGLU gate/up pair stays in one wave).  Lanes span K with 16-byte
 // weight loads (a wave reads 1 KB of a weight row per instruction, fully coalesced), the
 // activation tile (RMSNormed, fp32) sits in LDS, and each (row, column) dot product is
@@ -113,7 +361,7 @@ __host__ __device__ inline int gv_row_tile(int K) {
     return rt < 1 ? 1 : (rt > GV_RT_MAX ? GV_RT_MAX : rt);
 }
 
-template <bool WBF>
+template <bool WBF, int HEAD>
 __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
     extern __shared__ float sm[];
     const int K = a.K;
@@ -190,73 +438,540 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
             if (r < nr) {
                 const float g = wave_sum(acc0[r]);
                 const float u = wave_sum(acc1[r]);
-                if (lane == 0) {
-                    const int orow = a.o_rows ? a.o_rows[rt0 + r].hrow : rt0 + r;
-                    float* o = a.out + (int64_t)orow * a.ldo;
-                    if (a.epi == EPI_STORE) {
-                        o[n0] = g;
-                        o[n0 + 1] = u;
-                    } else if (a.epi == EPI_RESID) {
-                        o[n0] += g;
-                        o[n0 + 1] += u;
-                    } else {
-                        o[n0 >> 1] = g / (1.0f + expf(-g)) * u;
-                    }
-                }
+                if (lane == 0) epi_pair(a, rt0 + r, n0, g, u);
             }
         }
         __syncthreads();
     }
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    if (a.R <= 0) return hipSuccess;
-    const int rt = gv_row_tile(a.K);
-    const size_t shm = ((size_t)rt * a.K + GV_RT_MAX) * sizeof(float);
-    dim3 grid(a.N / GV_COLS);
-    if (a.wbf16)
-        hipLaunchKernelGGL(k_gemm_valu<true>, grid, dim3(256), shm, st, a);
-    else
-        hipLaunchKernelGGL(k_gemm_valu<false>, grid, dim3(256), shm, st, a);
-    return hipGetLastError();
+
+// ------------------------------------------------------------------------------------------
+// Skinny / tall GEMM on the matrix cores (bf16 weights, rows >= a threshold).
+// Block = 4 waves, tile 64 rows x BN columns, K in stages of 64 staged through LDS
+// (double-buffered).  Activations are RMSNormed (inverse RMS precomputed per row),
+// rounded to bf16 and held in LDS; wave w owns rows 16w..16w+15 of the tile and all
+// BN/16 column tiles, accumulating with v_mfma_f32_16x16x32_bf16:
+//   A operand: lane l holds A[l%16][8*(l/16) .. +8]; B operand: lane l holds
+//   W[n = l%16][8*(l/16) .. +8]; result: lane l holds D[4*(l/16) + i][l%16].
+// BN = 16 spreads decode-sized chunks over many blocks; BN = 64 reuses each weight
+// tile across 64 rows per block for long prompts.
+// ------------------------------------------------------------------------------------------
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int MF_BM = 64, MF_BK = 64, MF_LDK = MF_BK + 8;
+
+__global__ __launch_bounds__(256) void k_row_rms(const float* A, int64_t lda, const RowInfo* rows, int R, int K,
+                                                 float eps, float* inv) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= R) return;
+    const float* src = A + (int64_t)(rows ? rows[r].hrow : r) * lda;
+    float ss = 0.f;
+    for (int k = lane; k < K; k += 64) ss += src[k] * src[k];
+    ss = wave_sum(ss);
+    if (lane == 0) inv[r] = 1.0f / sqrtf(ss / (float)K + eps);
 }
 
-// ------------------------------------------------------------------------------------------
-// RoPE on q (in place) and k; k, v appended to the KV cache at the rows' positions.
-// qkv row i = [q (d) | k (d) | v (d)], head h occupying [h*hd, (h+1)*hd) of each.
-// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
 
-__global__ void k_rope_kv(float* qkv, const RowInfo* rows, int R, void* kv, int layer, LayerDims D,
-                          const float* cs) {
-    const int i = blockIdx.x;
-    if (i >= R) return;
-    const RowInfo ri = rows[i];
-    float* q = qkv + (int64_t)i * 3 * D.d;
-    const float* k = q + D.d;
-    const float* v = k + D.d;
-    const int half = D.hd / 2;
-    const float* c = cs + (int64_t)ri.pos * half * 2;
-    for (int idx = threadIdx.x; idx < D.H * half; idx += blockDim.x) {
-        const int h = idx / half, j = idx - h * half;
-        const float co = c[2 * j], si = c[2 * j + 1];
-        const int e0 = h * D.hd + j, e1 = e0 + half;
-        const float qa = q[e0], qb = q[e1];
-        q[e0] = qa * co - qb * si;
-        q[e1] = qb * co + qa * si;
-        const float ka = k[e0], kb = k[e1];
-        const int64_t kb0 = kv_base(D, ri.seq, layer, 0, h) + (int64_t)ri.pos * D.hd;
-        const int64_t vb0 = kv_base(D, ri.seq, layer, 1, h) + (int64_t)ri.pos * D.hd;
-        kv_store(kv, D.kv_bf16, kb0 + j, ka * co - kb * si);
-        kv_store(kv, D.kv_bf16, kb0 + j + half, kb * co + ka * si);
-        kv_store(kv, D.kv_bf16, vb0 + j, v[e0]);
-        kv_store(kv, D.kv_bf16, vb0 + j + half, v[e1]);
+template <int BN, int HEAD>
+__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
+    constexpr int NT = BN / 16;
+    __shared__ __align__(16) uint16_t As[2][MF_BM * MF_LDK];
+    __shared__ __align__(16) uint16_t Ws[2][BN * MF_LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * MF_BM;
+    const int K = a.K;
+    // global -> LDS assignment: thread handles 16 consecutive k of one row
+    const int lr = tid >> 2, lk = (tid & 3) * 16;
+    const int grow = m0 + lr;
+    const bool a_ok = grow < a.R;
+    const float* Arow = a.A + (int64_t)(a_ok ? (a.a_rows ? a.a_rows[grow].hrow : grow) : 0) * a.lda;
+    const float rs = (a_ok && a.norm_w) ? a.rms_ws[grow] : 1.0f;
+    const bool w_on = lr < BN;
+    const uint16_t* Wrow = (const uint16_t*)a.W + (int64_t)(n0 + (w_on ? lr : 0)) * K;
+
+    float4 ar[4];
+    uint4 wr[2];
+    auto gload = [&](int k0) {
+        if (a_ok) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ar[j] = *(const float4*)(Arow + k0 + lk + 4 * j);
+        }
+        if (w_on) {
+            wr[0] = *(const uint4*)(Wrow + k0 + lk);
+            wr[1] = *(const uint4*)(Wrow + k0 + lk + 8);
+        }
+    };
+    auto lstore = [&](int buf, int k0) {
+        uint32_t p[8];
+        if (a_ok) {
+            const float* v = (const float*)ar;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float x0 = v[2 * j] * rs, x1 = v[2 * j + 1] * rs;
+                if (a.norm_w) {
+                    x0 *= a.norm_w[k0 + lk + 2 * j];
+                    x1 *= a.norm_w[k0 + lk + 2 * j + 1];
+                }
+                p[j] = pack_bf2(x0, x1);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = 0u;
+        }
+        uint4* dst = (uint4*)&As[buf][lr * MF_LDK + lk];
+        dst[0] = make_uint4(p[0], p[1], p[2], p[3]);
+        dst[1] = make_uint4(p[4], p[5], p[6], p[7]);
+        if (w_on) {
+            uint4* wd = (uint4*)&Ws[buf][lr * MF_LDK + lk];
+            wd[0] = wr[0];
+            wd[1] = wr[1];
+        }
+    };
+
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / MF_BK;
+    gload(0);
+    lstore(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * MF_BK);
+#pragma unroll
+        for (int ks = 0; ks < MF_BK; ks += 32) {
+            const uint4 au = *(const uint4*)&As[buf][(wave * 16 + (lane & 15)) * MF_LDK + ks + 8 * (lane >> 4)];
+            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, au);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint4 bu = *(const uint4*)&Ws[buf][(t * 16 + (lane & 15)) * MF_LDK + ks + 8 * (lane >> 4)];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, bu), acc[t], 0, 0,
+                                                                 0);
+            }
+        }
+        if (kt + 1 < nk) lstore(buf ^ 1, (kt + 1) * MF_BK);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int col = n0 + t * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wave * 16 + 4 * (lane >> 4) + i;
+            const float v = acc[t][i];
+            const float u = __shfl_xor(v, 1, 64);     // partner column (n ^ 1), same row
+            if (row < a.R && (col & 1) == 0) epi_pair(a, row, col, v, u);
+        }
     }
 }
 
-hipError_t launch_rope_kv(float* qkv, const RowInfo* rows, int R, void* kv, int layer, const LayerDims& D,
-                          const float* cs, hipStream_t st) {
-    if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_rope_kv, dim3(R), dim3(256), 0, st, qkv, rows, R, kv, layer, D, cs);
+
+// ------------------------------------------------------------------------------------------
+// Decode-sized products, K split across the waves of a block.
+//
+// A block owns a few output columns; wave w takes the w-th slice of K, so each lane holds
+// one 16-byte chunk of K per column (chunk = 64 w + lane).  Activation chunks are loaded
+// first and weight chunks after them (loads retire in order, so the activations can be
+// used while the weights are still in flight); nothing waits on a barrier until the
+// cross-wave reduction at the end.  RMSNorm is folded in: the product is taken on
+// (x * g) and scaled by 1/rms(x) per row in the epilogue, the sum of squares coming from
+// the same chunks.
+// ------------------------------------------------------------------------------------------
+
+// Sum N values per lane over the 64 lanes of a wave.  Transposed reduction: each step
+// halves the values a lane keeps (exchanging the other half with the partner lane), so
+// after log2(N) steps lane L holds one value and a final butterfly finishes the sum.
+// Returns the sum of value index (L >> (6 - log2 N)) in lane L (all lanes of a group).
+template <int N>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[N], int lane) {
+    static_assert((N & (N - 1)) == 0 && N <= 64, "N must be a power of two <= 64");
+    constexpr int LOG = (N == 1) ? 0 : (N == 2) ? 1 : (N == 4) ? 2 : (N == 8) ? 3 : (N == 16) ? 4 : (N == 32) ? 5 : 6;
+    int n = N;
+#pragma unroll
+    for (int st = 0; st < LOG; ++st) {
+        const int m = 32 >> st;
+        const bool upper = (lane & m) != 0;
+        n >>= 1;
+        const int um = upper ? -1 : 0;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            if (i < n) {
+                // select by masks on the values (a conditional operator here becomes an
+                // indexed access over the whole array)
+                const int lo = __float_as_int(v[i]), hi = __float_as_int(v[i + n]);
+                const float send = __int_as_float((lo & um) | (hi & ~um));
+                const float keep = __int_as_float((hi & um) | (lo & ~um));
+                v[i] = keep + __shfl_xor(send, m, 64);
+            }
+        }
+    }
+    float r = v[0];
+#pragma unroll
+    for (int m = 32 >> LOG; m > 0; m >>= 1) r += __shfl_xor(r, m, 64);
+    return r;
+}
+
+constexpr int KS_CPB = 8;          // output columns per block (vector-ALU kernel)
+
+template <bool WBF, int RM, int HEAD>
+__global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
+    constexpr int EPC = WBF ? 8 : 4;
+    constexpr int ESZ = WBF ? 2 : 4;
+    constexpr int NV = KS_CPB * RM;     // values per lane to reduce
+    __shared__ float red[8][NV];
+    __shared__ float ssr[8][RM];
+    const int K = a.K, R = a.R;
+    const int nch = K / EPC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int n0 = blockIdx.x * KS_CPB;
+    const int ch = wave * 64 + lane;
+    const bool act = ch < nch;
+    const int k0 = (act ? ch : nch - 1) * EPC;
+
+    // epilogue context of the thread that will finish (row er, columns n0+ec, n0+ec+1)
+    const bool ethr = threadIdx.x < KS_CPB / 2 * RM;
+    const int er = threadIdx.x % RM, ec = 2 * (threadIdx.x / RM);
+    EpiCtx ectx{};
+    if (ethr && er < R) ectx = epi_prepare(a, er, n0 + ec);
+
+    // activation chunks (rows past R repeat row R-1; their results are never written)
+    float av[RM][EPC];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        const int rr = r < R ? r : R - 1;
+        const int ar = a.a_rows ? a.a_rows[rr].hrow : rr;
+        const float4* ap = (const float4*)(a.A + (int64_t)ar * a.lda + k0);
+#pragma unroll
+        for (int e = 0; e < EPC / 4; ++e) {
+            const float4 t = ap[e];
+            av[r][4 * e] = t.x; av[r][4 * e + 1] = t.y; av[r][4 * e + 2] = t.z; av[r][4 * e + 3] = t.w;
+        }
+    }
+    float gv[EPC];
+    if (a.norm_w) {
+        const float4* gp = (const float4*)(a.norm_w + k0);
+#pragma unroll
+        for (int e = 0; e < EPC / 4; ++e) {
+            const float4 t = gp[e];
+            gv[4 * e] = t.x; gv[4 * e + 1] = t.y; gv[4 * e + 2] = t.z; gv[4 * e + 3] = t.w;
+        }
+    }
+    uint4 w[KS_CPB];
+#pragma unroll
+    for (int c = 0; c < KS_CPB; ++c) w[c] = *(const uint4*)((const char*)a.W + ((size_t)(n0 + c) * K + k0) * ESZ);
+
+    const float amask = act ? 1.0f : 0.0f;   // lanes past the end of K contribute nothing
+    float ss[RM];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        ss[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            const float x = av[r][e] * amask;
+            ss[r] = fmaf(x, x, ss[r]);
+            av[r][e] = a.norm_w ? x * gv[e] : x;
+        }
+    }
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KS_CPB; ++c) {
+        const uint32_t u[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+        float wf[EPC];
+        if constexpr (WBF) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wf[2 * e] = bf_lo(u[e]);
+                wf[2 * e + 1] = bf_hi(u[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wf[e] = __uint_as_float(u[e]);
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[c * RM + r] = fmaf(wf[e], av[r][e], acc[c * RM + r]);
+    }
+    // value index c*RM + r ends up in lanes whose top log2(NV) bits equal it
+    const float tot = wave_transpose_sum<NV>(acc, lane);
+    constexpr int SH = (NV == 64) ? 0 : (NV == 32) ? 1 : (NV == 16) ? 2 : (NV == 8) ? 3 : (NV == 4) ? 4 : (NV == 2) ? 5 : 6;
+    if ((lane & ((1 << SH) - 1)) == 0) red[wave][lane >> SH] = tot;
+    if (a.norm_w) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const float t = wave_sum(ss[r]);
+            if (lane == 0) ssr[wave][r] = t;
+        }
+    }
+    __syncthreads();
+    if (ethr && er < R) {
+        float v0 = 0.f, v1 = 0.f, sq = 0.f;
+        for (int ww = 0; ww < nw; ++ww) {
+            v0 += red[ww][ec * RM + er];
+            v1 += red[ww][(ec + 1) * RM + er];
+            if (a.norm_w) sq += ssr[ww][er];
+        }
+        if (a.norm_w) {
+            const float inv = 1.0f / sqrtf(sq / (float)K + a.eps);
+            v0 *= inv;
+            v1 *= inv;
+        }
+        epi_apply(a, ectx, er, n0 + ec, v0, v1);
+    }
+}
+
+// Matrix-core version for 9..32 rows: the block owns 16 columns; wave w takes the w-th
+// K slice in steps of 32 (one v_mfma_f32_16x16x32_bf16 per 16-row tile and step).
+// Activation fragments (rows l%16 of each tile, k 8*(l/16)..) are loaded first, scaled by
+// g, rounded to bf16; weight fragments W[n0 + l%16][k ...] follow.  Partial tiles of the
+// waves are summed through LDS.
+template <int S, int MT, bool NORM, int HEAD>
+__global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
+    __shared__ float red[16][MT][64][4];
+    __shared__ float ssr[16][MT * 16];
+    const int K = a.K, R = a.R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int kq = 8 * (lane >> 4);
+    const int kb = wave * (32 * S) + kq;   // host: K == nw * 32 * S
+
+    // epilogue context for the rows this lane finishes (waves < MT own one tile each)
+    EpiCtx ectx[4];
+    const int ecol = n0 + (lane & 15);
+    if (wave < MT && (ecol & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wave * 16 + 4 * (lane >> 4) + i;
+            if (row < R) ectx[i] = epi_prepare(a, row, ecol);
+        }
+    }
+    // activation fragments: row (tile*16 + l%16), k = kb + 32 s .. +8; rows past R repeat R-1
+    float x[MT][S][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        int row = mt * 16 + (lane & 15);
+        row = row < R ? row : R - 1;
+        const float* ap = a.A + (int64_t)(a.a_rows ? a.a_rows[row].hrow : row) * a.lda + kb;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+            const float4 x0 = *(const float4*)(ap + 32 * s2), x1 = *(const float4*)(ap + 32 * s2 + 4);
+            x[mt][s2][0] = x0.x; x[mt][s2][1] = x0.y; x[mt][s2][2] = x0.z; x[mt][s2][3] = x0.w;
+            x[mt][s2][4] = x1.x; x[mt][s2][5] = x1.y; x[mt][s2][6] = x1.z; x[mt][s2][7] = x1.w;
+        }
+    }
+    float gn[NORM ? S : 1][8];
+    if constexpr (NORM) {
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+            const float4 g0 = *(const float4*)(a.norm_w + kb + 32 * s2);
+            const float4 g1 = *(const float4*)(a.norm_w + kb + 32 * s2 + 4);
+            gn[s2][0] = g0.x; gn[s2][1] = g0.y; gn[s2][2] = g0.z; gn[s2][3] = g0.w;
+            gn[s2][4] = g1.x; gn[s2][5] = g1.y; gn[s2][6] = g1.z; gn[s2][7] = g1.w;
+        }
+    }
+    uint4 wv[S];
+    const uint16_t* wp = (const uint16_t*)a.W + (int64_t)(n0 + (lane & 15)) * K + kb;
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) wv[s2] = *(const uint4*)(wp + 32 * s2);
+
+    float ss[MT];
+    bf16x8_t af[MT][S];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        ss[mt] = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+            uint32_t p[4];
+            if constexpr (NORM) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss[mt] = fmaf(x[mt][s2][e], x[mt][s2][e], ss[mt]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x0 = x[mt][s2][2 * e], x1 = x[mt][s2][2 * e + 1];
+                if constexpr (NORM) {
+                    x0 *= gn[NORM ? s2 : 0][2 * e];
+                    x1 *= gn[NORM ? s2 : 0][2 * e + 1];
+                }
+                p[e] = pack_bf2(x0, x1);
+            }
+            af[mt][s2] = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+        }
+    }
+    f32x4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) {
+        const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, wv[s2]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt][s2], bf, acc[mt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][mt][lane][i] = acc[mt][i];
+        float t = ss[mt];
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        if (lane < 16) ssr[wave][mt * 16 + lane] = t;
+    }
+    __syncthreads();
+    if (wave < MT) {
+        const int mt = wave;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int ww = 0; ww < nw; ++ww)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += red[ww][mt][lane][i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = mt * 16 + 4 * (lane >> 4) + i;
+            float y = v[i];
+            if constexpr (NORM) {
+                float sq = 0.f;
+                for (int ww = 0; ww < nw; ++ww) sq += ssr[ww][row];
+                y *= 1.0f / sqrtf(sq / (float)K + a.eps);
+            }
+            const float u = __shfl_xor(y, 1, 64);
+            if (row < R && (ecol & 1) == 0) epi_apply(a, ectx[i], row, ecol, y, u);
+        }
+    }
+}
+
+static bool use_mfma(const GemmArgs& a) {
+    return a.wbf16 && a.mfma_min_rows > 0 && a.R >= a.mfma_min_rows && a.K % MF_BK == 0 && a.N % 64 == 0 &&
+           (a.norm_w == nullptr || a.rms_ws != nullptr);
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+    if (a.R <= 0) return hipSuccess;
+    const int epc = a.wbf16 ? 8 : 4;
+    // decode-sized rows, vector ALUs (rows <= 8, and below the matrix-core threshold)
+    if (a.R <= 8 && (a.mfma_min_rows == 0 || a.R < a.mfma_min_rows || !a.wbf16) && a.K % epc == 0 &&
+        a.N % KS_CPB == 0 && (a.K / epc + 63) / 64 <= 8 && a.K % 4 == 0) {
+        const int nw = (a.K / epc + 63) / 64;
+        const dim3 grid(a.N / KS_CPB), block(64 * nw);
+        const int rm = a.R <= 1 ? 1 : a.R <= 2 ? 2 : a.R <= 4 ? 4 : 8;
+#define NV_KS(WB, RMV)                                                                                        \
+    do {                                                                                                     \
+        if (a.head) hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 1>), grid, block, 0, st, a);       \
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 0>), grid, block, 0, st, a);              \
+    } while (0)
+        if (a.wbf16) {
+            if (rm == 1) NV_KS(true, 1); else if (rm == 2) NV_KS(true, 2); else if (rm == 4) NV_KS(true, 4); else NV_KS(true, 8);
+        } else {
+            if (rm == 1) NV_KS(false, 1); else if (rm == 2) NV_KS(false, 2); else if (rm == 4) NV_KS(false, 4); else NV_KS(false, 8);
+        }
+#undef NV_KS
+        return hipGetLastError();
+    }
+    // decode-sized rows on the matrix cores (rows <= 32): K split across the waves, S k-steps each
+    if (a.wbf16 && a.R <= 32 && a.mfma_min_rows > 0 && a.R >= a.mfma_min_rows && a.N % 16 == 0) {
+        int S = 0;
+        for (int cand : {3, 8, 1})
+            if (a.K % (32 * cand) == 0 && a.K / (32 * cand) <= 16 && !(cand == 8 && a.norm_w)) {
+                S = cand;
+                break;
+            }
+        if (S > 0) {
+            const int nw = a.K / (32 * S);
+            const dim3 grid(a.N / 16), block(64 * nw);
+#define NV_MKS2(SV, MTV, NV_)                                                                                  \
+    do {                                                                                                      \
+        if (a.head) hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 1>), grid, block, 0, st, a); \
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 0>), grid, block, 0, st, a);        \
+    } while (0)
+#define NV_MKS(SV, MTV)                                                                                        \
+    do {                                                                                                      \
+        if (a.norm_w) NV_MKS2(SV, MTV, true); else NV_MKS2(SV, MTV, false);                                   \
+    } while (0)
+            if (nw >= 2 || a.R <= 16) {
+                if (a.R <= 16) {
+                    if (S == 3) NV_MKS(3, 1); else if (S == 8) NV_MKS2(8, 1, false); else NV_MKS(1, 1);
+                } else {
+                    if (S == 3) NV_MKS(3, 2); else if (S == 8) NV_MKS2(8, 2, false); else NV_MKS(1, 2);
+                }
+#undef NV_MKS
+#undef NV_MKS2
+                return hipGetLastError();
+            }
+        }
+    }
+    if (use_mfma(a)) {
+        if (a.norm_w) {
+            hipLaunchKernelGGL(k_row_rms, dim3((a.R + 3) / 4), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.eps,
+                               a.rms_ws);
+        }
+        const unsigned mt = (unsigned)((a.R + MF_BM - 1) / MF_BM);
+        if (a.R <= MF_BM) {
+            if (a.head)
+                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<16, 1>), dim3(a.N / 16, mt), dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<16, 0>), dim3(a.N / 16, mt), dim3(256), 0, st, a);
+        } else {
+            if (a.head)
+                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<64, 1>), dim3(a.N / 64, mt), dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<64, 0>), dim3(a.N / 64, mt), dim3(256), 0, st, a);
+        }
+        return hipGetLastError();
+    }
+    {
+        const int epc = a.wbf16 ? 8 : 4;
+        const int need = (a.K / epc + 63) / 64;
+        const int ch = need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+        const int cpw = a.N >= 4096 ? 4 : 2;
+        const size_t shm = ((size_t)a.R * a.K + GV_RMAX) * sizeof(float);
+        if (a.R <= GV_RMAX && ch > 0 && a.K % epc == 0 && a.N % (4 * cpw) == 0 && shm <= 160 * 1024) {
+            const dim3 grid(a.N / (4 * cpw));
+#define NV_GV(WB, CP, C, HD)                                                                                  \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemv<WB, CP, C, HD>), grid, dim3(256), shm, st, a)
+#define NV_GV_CH(WB, CP, HD)                                                                                  \
+    switch (ch) {                                                                                            \
+        case 1: NV_GV(WB, CP, 1, HD); break;                                                                 \
+        case 2: NV_GV(WB, CP, 2, HD); break;                                                                 \
+        case 3: NV_GV(WB, CP, 3, HD); break;                                                                 \
+        case 4: NV_GV(WB, CP, 4, HD); break;                                                                 \
+        default: NV_GV(WB, CP, 8, HD); break;                                                                \
+    }
+            if (a.wbf16) {
+                if (cpw == 4) { if (a.head) { NV_GV_CH(true, 4, 1) } else { NV_GV_CH(true, 4, 0) } }
+                else { if (a.head) { NV_GV_CH(true, 2, 1) } else { NV_GV_CH(true, 2, 0) } }
+            } else {
+                if (cpw == 4) { if (a.head) { NV_GV_CH(false, 4, 1) } else { NV_GV_CH(false, 4, 0) } }
+                else { if (a.head) { NV_GV_CH(false, 2, 1) } else { NV_GV_CH(false, 2, 0) } }
+            }
+#undef NV_GV_CH
+#undef NV_GV
+            return hipGetLastError();
+        }
+    }
+    const int rt = gv_row_tile(a.K);
+    const size_t shm = ((size_t)rt * a.K + GV_RT_MAX) * sizeof(float);
+    dim3 grid(a.N / GV_COLS);
+    if (a.wbf16) {
+        if (a.head)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<true, 1>), grid, dim3(256), shm, st, a);
+        else
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<true, 0>), grid, dim3(256), shm, st, a);
+    } else {
+        if (a.head)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<false, 1>), grid, dim3(256), shm, st, a);
+        else
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<false, 0>), grid, dim3(256), shm, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -273,9 +988,9 @@ constexpr int AT_MAX_ROWS = 32;     // rows per item
 __host__ __device__ inline int at_tile(int hd) { return hd > 64 ? 32 : 64; }
 constexpr int AT_RPW = AT_MAX_ROWS / 4;
 
-__global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowInfo* rows, const float* qkv,
+__global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowInfo* rows, const float* q,
                                               const void* kv, int layer, LayerDims D, float* part_ml,
-                                              float* part_o) {
+                                              float* part_o, float* out) {
     extern __shared__ float sm[];
     const AttnItem it = items[blockIdx.x];
     const int hd = D.hd;
@@ -287,7 +1002,7 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
     const float scale = 1.0f / sqrtf((float)hd);
     for (int idx = threadIdx.x; idx < it.nrows * hd; idx += blockDim.x) {
         const int r = idx / hd, e = idx - r * hd;
-        Qs[idx] = qkv[(int64_t)(it.row0 + r) * 3 * D.d + it.head * hd + e] * scale;
+        Qs[idx] = q[(int64_t)(it.row0 + r) * D.d + it.head * hd + e] * scale;
     }
     const int seq = rows[it.row0].seq;
     const int64_t kb = kv_base(D, seq, layer, 0, it.head);
@@ -346,6 +1061,12 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
     for (int i = 0; i < AT_RPW; ++i) {
         const int r = wave + 4 * i;
         if (r >= it.nrows) continue;
+        if (it.nsplit == 1) {      // unsplit key range: finished here, the combine pass skips the row
+            float* orow = out + (int64_t)(it.row0 + r) * D.d + it.head * hd;
+            if (d0 < hd) orow[d0] = o0[i] / l[i];
+            if (d1 < hd) orow[d1] = o1[i] / l[i];
+            continue;
+        }
         const int64_t slot = it.part + r;
         if (lane == 0) {
             part_ml[2 * slot] = m[i];
@@ -356,38 +1077,59 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
     }
 }
 
-__global__ void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
-                               const float* part_o, float* out) {
+// Merge the split partials of one row (all heads): (max, sum) pairs of every (head, split)
+// are staged in LDS in parallel, turned into weights exp(max - M_head), then each thread
+// forms the weighted sums for its dims with independent loads.  Rows whose key range was
+// not split were written by the attention kernel and are skipped.
+constexpr int COMB_MAX = 4096;   // (head, split) pairs per row held in LDS
+
+__global__ __launch_bounds__(256) void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
+                                                      const float* part_o, float* out) {
+    __shared__ float w[COMB_MAX];
+    __shared__ float ls[COMB_MAX];
+    __shared__ float lsum[64];
     const int i = blockIdx.x;
     if (i >= R) return;
     const CombineInfo c = ci[i];
-    for (int idx = threadIdx.x; idx < D.H * D.hd; idx += blockDim.x) {
-        const int h = idx / D.hd, e = idx - h * D.hd;
+    if (c.nsplit == 1) return;
+    const int ns = c.nsplit, H = D.H, hd = D.hd;
+    for (int idx = threadIdx.x; idx < H * ns; idx += blockDim.x) {
+        const int64_t slot = c.base + (int64_t)idx * c.nrows + c.off;   // idx = h * ns + s
+        const float2 ml = *(const float2*)(part_ml + 2 * slot);
+        w[idx] = ml.x;
+        ls[idx] = ml.y;
+    }
+    __syncthreads();
+    if (threadIdx.x < H) {
+        const int h = threadIdx.x;
         float M = -INFINITY;
-        for (int s = 0; s < c.nsplit; ++s) {
-            const int64_t slot = c.base + (int64_t)(h * c.nsplit + s) * c.nrows + c.off;
-            M = fmaxf(M, part_ml[2 * slot]);
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, w[h * ns + sp]);
+        float L = 0.f;
+        for (int sp = 0; sp < ns; ++sp) {
+            const float ms = w[h * ns + sp];
+            const float wt = ms == -INFINITY ? 0.f : expf(ms - M);
+            w[h * ns + sp] = wt;
+            L += wt * ls[h * ns + sp];
         }
-        float Ls = 0.f, acc = 0.f;
-        for (int s = 0; s < c.nsplit; ++s) {
-            const int64_t slot = c.base + (int64_t)(h * c.nsplit + s) * c.nrows + c.off;
-            const float ms = part_ml[2 * slot];
-            if (ms == -INFINITY) continue;
-            const float w = expf(ms - M);
-            Ls += w * part_ml[2 * slot + 1];
-            acc += w * part_o[slot * D.hd + e];
-        }
-        out[(int64_t)i * D.d + idx] = acc / Ls;
+        lsum[h] = L;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < H * hd; idx += blockDim.x) {
+        const int h = idx / hd, e = idx - h * hd;
+        float O = 0.f;
+#pragma unroll 8
+        for (int sp = 0; sp < ns; ++sp)
+            O += w[h * ns + sp] * part_o[(c.base + (int64_t)(h * ns + sp) * c.nrows + c.off) * hd + e];
+        out[(int64_t)i * D.d + idx] = O / lsum[h];
     }
 }
 
-hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* qkv, const void* kv,
-                       int layer, const LayerDims& D, float* part_ml, float* part_o, hipStream_t st) {
+hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
+                       int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st) {
     if (n_items <= 0) return hipSuccess;
     const int tile = at_tile(D.hd);
     const size_t shm = ((size_t)tile * (D.hd + 1) + (size_t)tile * D.hd + (size_t)AT_MAX_ROWS * D.hd) * sizeof(float);
-    hipLaunchKernelGGL(k_attn, dim3(n_items), dim3(256), shm, st, items, rows, qkv, kv, layer, D, part_ml,
-                       part_o);
+    hipLaunchKernelGGL(k_attn, dim3(n_items), dim3(256), shm, st, items, rows, q, kv, layer, D, part_ml, part_o, out);
     return hipGetLastError();
 }
 
@@ -395,6 +1137,214 @@ hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
                                const float* part_o, float* out, hipStream_t st) {
     if (R <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_attn_combine, dim3(R), dim3(256), 0, st, ci, R, D, part_ml, part_o, out);
+    return hipGetLastError();
+}
+
+
+// ------------------------------------------------------------------------------------------
+// Decode attention: up to ATTN_DEC_ROWS consecutive positions of one sequence against the
+// keys [lo, hi) of one head (one split of that row block's key range).  A key is read by
+// hd/8 lanes, 16 bytes (8 dims) each, so one wave instruction covers 64/(hd/8) keys with
+// fully used 16-byte loads of the K and V rows.  Each lane slot keeps an online-softmax
+// state (max, sum, 8 output dims) per row over the keys it saw; slots, then the block's
+// four waves, are merged.  With one split the output is written directly; otherwise the
+// split's partial state is written and a separate combine pass (k_attn_combine) merges
+// the splits: the kernel boundary makes the partials visible without a device-scope
+// fence, which costs more than the whole kernel on this part.
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void sm_merge(float& m, float& l, float* o, float m2, float l2, const float* o2, int n) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    const float a1 = expf(m - M), a2 = expf(m2 - M);
+    l = a1 * l + a2 * l2;
+    for (int e = 0; e < n; ++e) o[e] = a1 * o[e] + a2 * o2[e];
+    m = M;
+}
+
+template <int HD, bool KVBF, int RM>
+__global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const RowInfo* rows, const float* q,
+                                                  const void* kv, int layer, LayerDims D, float* part_ml,
+                                                  float* part_o, float* out) {
+    constexpr int DPL = 8;
+    constexpr int LPK = HD / DPL;       // lanes per key
+    constexpr int KPI = 64 / LPK;       // keys per wave instruction
+    constexpr int NIT = ATTN_DEC_ITERS; // key groups per wave: a split holds at most 4 * KPI * NIT keys
+    __shared__ float red[4][RM][HD + 2];
+    const AttnItem it = items[blockIdx.x];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPK, dl = lane - g * LPK;
+    const int nr = it.nrows;
+    const int seq = rows[it.row0].seq;
+    const int64_t kb = kv_base(D, seq, layer, 0, it.head) + dl * DPL;
+    const int64_t vb = kv_base(D, seq, layer, 1, it.head) + dl * DPL;
+
+    // queries first, then every key/value group of this wave, all in flight before any use
+    const float scale = 1.0f / sqrtf((float)HD);
+    float qv[RM][DPL];
+    int qpos[RM];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        qpos[r] = -1;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) qv[r][e] = 0.f;
+        if (r < nr) {
+            const float* qp = q + (int64_t)(it.row0 + r) * D.d + it.head * HD + dl * DPL;
+            const float4 a0 = *(const float4*)qp, a1 = *(const float4*)(qp + 4);
+            qv[r][0] = a0.x * scale; qv[r][1] = a0.y * scale; qv[r][2] = a0.z * scale; qv[r][3] = a0.w * scale;
+            qv[r][4] = a1.x * scale; qv[r][5] = a1.y * scale; qv[r][6] = a1.z * scale; qv[r][7] = a1.w * scale;
+            qpos[r] = rows[it.row0 + r].pos;
+        }
+    }
+
+    uint4 kr[NIT], vr[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int key = it.lo + (i * 4 + wave) * KPI + g;
+        if (key < it.hi) {
+            if constexpr (KVBF) {
+                kr[i] = *(const uint4*)((const uint16_t*)kv + kb + (int64_t)key * HD);
+                vr[i] = *(const uint4*)((const uint16_t*)kv + vb + (int64_t)key * HD);
+            } else {
+                kr[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD);
+                vr[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD);
+            }
+        }
+    }
+    uint4 kr2[KVBF ? 1 : NIT], vr2[KVBF ? 1 : NIT];   // fp32 keys need a second 16-byte load
+    if constexpr (!KVBF) {
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const int key = it.lo + (i * 4 + wave) * KPI + g;
+            if (key < it.hi) {
+                kr2[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD + 4);
+                vr2[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD + 4);
+            }
+        }
+    }
+    float m[RM], l[RM], o[RM][DPL];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[r][e] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int key = it.lo + (i * 4 + wave) * KPI + g;
+        if (it.lo + (i * 4 + wave) * KPI >= it.hi) break;      // wave-uniform
+        const bool kin = key < it.hi;
+        float kf[DPL], vf[DPL];
+        if constexpr (KVBF) {
+            const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+            const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[2 * e] = bf_lo(kw[e]); kf[2 * e + 1] = bf_hi(kw[e]);
+                vf[2 * e] = bf_lo(vw[e]); vf[2 * e + 1] = bf_hi(vw[e]);
+            }
+        } else {
+            kf[0] = __uint_as_float(kr[i].x); kf[1] = __uint_as_float(kr[i].y);
+            kf[2] = __uint_as_float(kr[i].z); kf[3] = __uint_as_float(kr[i].w);
+            kf[4] = __uint_as_float(kr2[i].x); kf[5] = __uint_as_float(kr2[i].y);
+            kf[6] = __uint_as_float(kr2[i].z); kf[7] = __uint_as_float(kr2[i].w);
+            vf[0] = __uint_as_float(vr[i].x); vf[1] = __uint_as_float(vr[i].y);
+            vf[2] = __uint_as_float(vr[i].z); vf[3] = __uint_as_float(vr[i].w);
+            vf[4] = __uint_as_float(vr2[i].x); vf[5] = __uint_as_float(vr2[i].y);
+            vf[6] = __uint_as_float(vr2[i].z); vf[7] = __uint_as_float(vr2[i].w);
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            if (r < nr) {
+                float sc = 0.f;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) sc = fmaf(qv[r][e], kf[e], sc);
+                sc = group_sum<LPK>(sc);
+                if (kin && key <= qpos[r]) {
+                    const float mn = fmaxf(m[r], sc);
+                    const float alpha = expf(m[r] - mn);
+                    const float p = expf(sc - mn);
+                    l[r] = l[r] * alpha + p;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e] * alpha);
+                    m[r] = mn;
+                }
+            }
+        }
+    }
+    // merge the key slots of the wave
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        if (r < nr) {
+#pragma unroll
+            for (int off = LPK; off < 64; off <<= 1) {
+                float o2[DPL];
+                const float m2 = __shfl_xor(m[r], off, 64), l2 = __shfl_xor(l[r], off, 64);
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) o2[e] = __shfl_xor(o[r][e], off, 64);
+                sm_merge(m[r], l[r], o[r], m2, l2, o2, DPL);
+            }
+            if (g == 0) {
+                if (dl == 0) {
+                    red[wave][r][0] = m[r];
+                    red[wave][r][1] = l[r];
+                }
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) red[wave][r][2 + dl * DPL + e] = o[r][e];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nr * HD; idx += blockDim.x) {
+        const int r = idx / HD, e = idx - r * HD;
+        float M = -INFINITY;
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][r][0]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+            for (int w = 0; w < 4; ++w) {
+                const float a = expf(red[w][r][0] - M);
+                L += a * red[w][r][1];
+                O += a * red[w][r][2 + e];
+            }
+        }
+        if (it.nsplit == 1) {
+            out[(int64_t)(it.row0 + r) * D.d + it.head * HD + e] = O / L;
+        } else {
+            const int64_t slot = it.part + r;
+            part_o[slot * HD + e] = O;
+            if (e == 0) {
+                part_ml[2 * slot] = M;
+                part_ml[2 * slot + 1] = L;
+            }
+        }
+    }
+}
+
+
+hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
+                           const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o, float* out,
+                           hipStream_t st) {
+    if (n_items <= 0) return hipSuccess;
+#define NV_DEC(HDV, BF, RMV)                                                                                  \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_dec<HDV, BF, RMV>), dim3(n_items), dim3(256), 0, st, items, rows, q, \
+                       kv, layer, D, part_ml, part_o, out)
+#define NV_DEC_R(HDV, BF)                                                                                     \
+    do {                                                                                                     \
+        if (max_rows <= 1) NV_DEC(HDV, BF, 1);                                                               \
+        else if (max_rows <= 2) NV_DEC(HDV, BF, 2);                                                          \
+        else if (max_rows <= 4) NV_DEC(HDV, BF, 4);                                                          \
+        else NV_DEC(HDV, BF, 8);                                                                             \
+    } while (0)
+    if (D.hd == 128) {
+        if (D.kv_bf16) NV_DEC_R(128, true); else NV_DEC_R(128, false);
+    } else if (D.hd == 64) {
+        if (D.kv_bf16) NV_DEC_R(64, true); else NV_DEC_R(64, false);
+    } else {
+        if (D.kv_bf16) NV_DEC_R(32, true); else NV_DEC_R(32, false);
+    }
+#undef NV_DEC_R
+#undef NV_DEC
     return hipGetLastError();
 }
 
@@ -441,49 +1391,59 @@ hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float*
 }
 
 // ------------------------------------------------------------------------------------------
-// Inverse-CDF sampling of softmax(logits) in token-id order, in float64:
-//   e_i = exp(z_i - max z), Z = sum e_i, token = smallest i with u * Z < sum_{j<=i} e_j.
-// Thread t owns a contiguous id range; range sums are prefixed serially (so that the
-// prefix of range t+1 is exactly prefix_t + S_t) and the range holding u*Z is scanned.
+// Inverse-CDF sampling of softmax(logits) in token-id order:
+//   e_i = exp(z_i - max z) (float32 exp), Z = sum e_i in float64,
+//   token = smallest i with u * Z < sum_{j<=i} e_j (float64 comparisons).
+// 1024 threads; thread t owns a contiguous id range.  The range sums are prefixed by a
+// fixed-order block scan (so prefix_{t+1} = prefix_t + S_t exactly), and the thread whose
+// range holds u*Z walks it.
 // ------------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_sample(const float* logits, int64_t ld, const int* seqs, int n, int V,
-                                                const float* uniforms, int* tok_out) {
-    __shared__ double sd[257];
-    __shared__ float sf[256];
+constexpr int SMP_THREADS = 1024;
+
+__global__ __launch_bounds__(SMP_THREADS) void k_sample(const float* logits, int64_t ld, const int* seqs, int n,
+                                                        int V, const float* uniforms, int* tok_out) {
+    __shared__ float smax[SMP_THREADS / 64];
+    __shared__ double wsum[SMP_THREADS / 64];
     __shared__ int found;
     const int seq = seqs[blockIdx.x];
     const float* z = logits + (int64_t)seq * ld;
-    const int t = threadIdx.x;
-    const int chunk = (V + 255) / 256;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int chunk = (V + SMP_THREADS - 1) / SMP_THREADS;
     const int b = min(V, t * chunk), e = min(V, b + chunk);
     float mx = -INFINITY;
     for (int i = b; i < e; ++i) mx = fmaxf(mx, z[i]);
-    sf[t] = mx;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (t < s) sf[t] = fmaxf(sf[t], sf[t + s]);
-        __syncthreads();
-    }
-    const double M = (double)sf[0];
-    double S = 0.0;
-    for (int i = b; i < e; ++i) S += exp((double)z[i] - M);
-    sd[t + 1] = S;
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
     if (t == 0) found = 0x7fffffff;
     __syncthreads();
-    if (t == 0) {
-        sd[0] = 0.0;
-        for (int i = 1; i <= 256; ++i) sd[i] += sd[i - 1];
+    float M = smax[0];
+    for (int w = 1; w < SMP_THREADS / 64; ++w) M = fmaxf(M, smax[w]);
+    double S = 0.0;
+    for (int i = b; i < e; ++i) S += (double)expf(z[i] - M);
+    // inclusive scan of S over the wave (fixed order), then over the waves
+    double inc = S;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
     }
+    if (lane == 63) wsum[wave] = inc;
     __syncthreads();
-    const double Z = sd[256];
+    double wpre = 0.0, Z = 0.0;
+    for (int w = 0; w < SMP_THREADS / 64; ++w) {
+        if (w < wave) wpre += wsum[w];
+        Z += wsum[w];
+    }
+    double exc = __shfl_up(inc, 1, 64);       // inclusive sum of the previous lane
+    if (lane == 0) exc = 0.0;
+    const double hi = wpre + inc, lo = wpre + exc;   // lo_t == hi_{t-1}: same operands, same order
     const double target = (double)uniforms[seq * 4 + 3] * Z;
-    const double lo = sd[t], hi = sd[t + 1];
     if (b < e && lo <= target && target < hi) {
         double cum = lo;
         int tok = e - 1;
         for (int i = b; i < e; ++i) {
-            cum += exp((double)z[i] - M);
+            cum += (double)expf(z[i] - M);
             if (target < cum) {
                 tok = i;
                 break;
@@ -496,7 +1456,7 @@ __global__ __launch_bounds__(256) void k_sample(const float* logits, int64_t ld,
         int tok = found;
         if (tok == 0x7fffffff) {  // u*Z at or past the rounded total: last id with nonzero mass
             tok = V - 1;
-            while (tok > 0 && exp((double)z[tok] - M) == 0.0) --tok;
+            while (tok > 0 && expf(z[tok] - M) == 0.0f) --tok;
         }
         tok_out[seq] = tok;
     }
@@ -505,10 +1465,36 @@ __global__ __launch_bounds__(256) void k_sample(const float* logits, int64_t ld,
 hipError_t launch_sample(const float* logits, int64_t ld, const int* seqs, int n, int V, const float* uniforms,
                          int* tok_out, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sample, dim3(n), dim3(256), 0, st, logits, ld, seqs, n, V, uniforms, tok_out);
+    hipLaunchKernelGGL(k_sample, dim3(n), dim3(SMP_THREADS), 0, st, logits, ld, seqs, n, V, uniforms, tok_out);
     return hipGetLastError();
 }
 
-hipError_t init_kernel_attributes() { return hipSuccess; }
+template <bool WB, int CP, int C, int HD>
+static hipError_t gv_attr() {
+    return hipFuncSetAttribute((const void*)k_gemv<WB, CP, C, HD>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               160 * 1024);
+}
+
+template <bool WB, int CP, int HD>
+static hipError_t gv_attr_all() {
+    hipError_t e;
+    if ((e = gv_attr<WB, CP, 1, HD>()) != hipSuccess) return e;
+    if ((e = gv_attr<WB, CP, 2, HD>()) != hipSuccess) return e;
+    if ((e = gv_attr<WB, CP, 3, HD>()) != hipSuccess) return e;
+    if ((e = gv_attr<WB, CP, 4, HD>()) != hipSuccess) return e;
+    return gv_attr<WB, CP, 8, HD>();
+}
+
+hipError_t init_kernel_attributes() {
+    hipError_t e;
+    if ((e = gv_attr_all<true, 4, 0>()) != hipSuccess) return e;
+    if ((e = gv_attr_all<true, 4, 1>()) != hipSuccess) return e;
+    if ((e = gv_attr_all<true, 2, 0>()) != hipSuccess) return e;
+    if ((e = gv_attr_all<true, 2, 1>()) != hipSuccess) return e;
+    if ((e = gv_attr_all<false, 4, 0>()) != hipSuccess) return e;
+    if ((e = gv_attr_all<false, 4, 1>()) != hipSuccess) return e;
+    if ((e = gv_attr_all<false, 2, 0>()) != hipSuccess) return e;
+    return gv_attr_all<false, 2, 1>();
+}
 
 }  // namespace nv

@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -28,6 +29,8 @@ namespace {
 
 constexpr int kMaxExits = 4;
 constexpr int kAttnRowsPerItem = 32;
+constexpr int kDecodeRows = 64;          // launch groups up to this many rows use decode attention
+constexpr int kAttnBlocksTarget = 512;   // decode attention: aim for about this many blocks
 constexpr size_t kAlign = 256;
 
 struct LayerPtrs {
@@ -58,6 +61,8 @@ struct Chunk {
     int seq, pos0, nrows;
 };
 
+constexpr size_t kEventPairs = 8192;
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Sizes of everything the model keeps in device memory.
@@ -66,7 +71,7 @@ struct Plan {
     size_t embed = 0, layer_w = 0, exit_w = 0;
     size_t hidden = 0, kv = 0, rope = 0;
     int R_max = 0, part_cap = 0, items_cap = 0;
-    size_t qkv = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0;
+    size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0;
     size_t tables = 0, small = 0, logits = 0;
     size_t total = 0;
 };
@@ -135,11 +140,13 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.R_max = (int)rmax;
     p.part_cap = (int)(rmax * H * 4);
     p.items_cap = p.part_cap;
-    p.qkv = align_up(rmax * 3 * d * 4);
+    p.qbuf = align_up(rmax * d * 4);
+
     p.attn_o = align_up(rmax * d * 4);
     p.mlp = align_up(rmax * F * 4);
     p.part_ml = align_up((size_t)p.part_cap * 2 * 4);
     p.part_o = align_up((size_t)p.part_cap * hd * 4);
+    p.rms = align_up(rmax * 4);
     p.tables = align_up(rmax * sizeof(RowInfo) * 2 + rmax * sizeof(CombineInfo) +
                         (size_t)p.items_cap * sizeof(AttnItem) + rmax * 4);
     // uniforms, router outputs, stop flags, tokens in/out, head lists
@@ -147,8 +154,8 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
               2 * align_up((size_t)max_batch * (4 + 2 * sizeof(RowInfo))) + align_up((size_t)max_batch * 32) +
               2 * align_up((size_t)max_batch * 4);
     p.logits = align_up((size_t)max_batch * V * 4);
-    p.total = p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.hidden + p.kv + p.rope + p.qkv + p.attn_o +
-              p.mlp + p.part_ml + p.part_o + p.tables + p.small + p.logits + kAlign;
+    p.total = p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
+              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + kAlign;
     return p;
 }
 
@@ -172,11 +179,14 @@ struct nv_model {
     float* Hs = nullptr;
     void* kv = nullptr;
     float* rope = nullptr;
-    float* qkv = nullptr;
+    float* qbuf = nullptr;     // [R_max][d] rotated queries
+
     float* attn_o = nullptr;
     float* mlp = nullptr;
     float* part_ml = nullptr;
     float* part_o = nullptr;
+    float* rms_ws = nullptr;   // [R_max] per-row inverse RMS for the matrix-core GEMM
+    int mfma_min_rows = 9;     // chunks of at least this many rows use the matrix cores
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
     // goes up in one copy.  step: [uniforms MB*4 f32][pending tokens MB i32][current rows MB]
@@ -209,6 +219,15 @@ struct nv_model {
     std::vector<SeqHost> seqs;
     std::vector<double> last_w;   // [max_batch][4]
     std::string err;
+
+    // optional per-class kernel timing with HIP events on the work stream
+    bool timing = false;
+    std::vector<hipEvent_t> ev;   // pairs
+    std::vector<int> ev_kind;
+    std::vector<double> ev_bytes;
+    size_t ev_used = 0;
+    double t_ms[NV_TIME_CLASSES] = {0}, t_bytes[NV_TIME_CLASSES] = {0};
+    int64_t t_n[NV_TIME_CLASSES] = {0};
 
     LayerDims dims() const {
         LayerDims D;
@@ -259,6 +278,54 @@ bool pread_all(int fd, void* dst, size_t n, size_t off) {
     return true;
 }
 
+// Accumulate the durations of recorded event pairs (the stream must be idle).
+nv_status resolve_timing(nv_model* m) {
+    for (size_t i = 0; i < m->ev_used; ++i) {
+        float ms = 0.f;
+        NV_HIP(m, hipEventElapsedTime(&ms, m->ev[2 * i], m->ev[2 * i + 1]));
+        const int k = m->ev_kind[i];
+        m->t_ms[k] += ms;
+        m->t_bytes[k] += m->ev_bytes[i];
+        m->t_n[k] += 1;
+    }
+    m->ev_used = 0;
+    return NV_OK;
+}
+
+// Issue one launch; with timing on, bracket it with events and note its algorithmic bytes.
+template <class F>
+nv_status timed(nv_model* m, int kind, double bytes, F&& launch) {
+    if (!m->timing) {
+        NV_HIP(m, launch());
+        return NV_OK;
+    }
+    if (m->ev_used == kEventPairs) {
+        NV_HIP(m, hipStreamSynchronize(m->st));
+        nv_status s = resolve_timing(m);
+        if (s != NV_OK) return s;
+    }
+    const size_t i = m->ev_used++;
+    NV_HIP(m, hipEventRecord(m->ev[2 * i], m->st));
+    NV_HIP(m, launch());
+    NV_HIP(m, hipEventRecord(m->ev[2 * i + 1], m->st));
+    m->ev_kind[i] = kind;
+    m->ev_bytes[i] = bytes;
+    return NV_OK;
+}
+
+double gemm_bytes(const nv_model* m, const GemmArgs& g) {
+    const double es = m->plan.es;
+    const double nout = g.epi == EPI_SWIGLU ? g.N / 2 : g.N;
+    const double out_rw = g.epi == EPI_RESID ? 2.0 : 1.0;
+    return (double)g.N * g.K * es + (double)g.R * g.K * 4.0 + (double)g.R * nout * 4.0 * out_rw;
+}
+
+#define NV_TRY(expr)                      \
+    do {                                  \
+        nv_status s_ = (expr);            \
+        if (s_ != NV_OK) return s_;       \
+    } while (0)
+
 nv_status stage_sync(nv_model* m) {
     if (m->stage_busy) {
         NV_HIP(m, hipStreamSynchronize(m->st));
@@ -275,7 +342,17 @@ struct Tables {
     CombineInfo* comb;
     AttnItem* items;
     int R, n_items;
+    bool dec;          // decode-sized group: attention combines its splits in-kernel
+    int max_rows;      // most rows in one decode-attention row block
+    bool any_split;    // some row's key range was split (the combine pass is needed)
+    double kv_bytes;   // keys and values the attention items read
 };
+
+int c_max_ctx(const std::vector<Chunk>& chunks) {
+    int mx = 0;
+    for (const Chunk& c : chunks) mx = std::max(mx, c.pos0 + c.nrows);
+    return mx;
+}
 
 nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t) {
     nv_status s = stage_sync(m);
@@ -296,50 +373,107 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
             hrows[r].hrow = c.seq * m->max_ctx + c.pos0 + i;
             hrows[r].pad = 0;
         }
-    // attention items: the key range of each block of <= 32 rows is split into pieces of
-    // split_len keys; the split length doubles until the partial slots fit.
-    int split_len = R <= 64 ? 64 : 512;
-    for (;;) {
-        long slots = 0, items = 0;
-        for (const Chunk& c : chunks)
+    int n_items = 0;
+    const bool dec = R <= kDecodeRows;
+    if (dec) {
+        // decode-sized group: row blocks of ATTN_DEC_ROWS rows; each block's key range is cut
+        // into nsplit pieces (at least 64 keys each, about 512 blocks in all) whose partial
+        // softmax states the combine pass merges
+        int nrb = 0;
+        for (const Chunk& c : chunks) nrb += (c.nrows + ATTN_DEC_ROWS - 1) / ATTN_DEC_ROWS;
+        const int want = std::max(1, (kAttnBlocksTarget + m->H * nrb - 1) / (m->H * nrb));
+        // keys per split: at most what one block's waves hold in flight
+        const int max_keys = 4 * ATTN_DEC_ITERS * (64 / (m->hd / 8));
+        int slot = 0, row0 = 0, rbi = 0;
+        t->max_rows = 0;
+        for (const Chunk& c : chunks) {
+            for (int rb = 0; rb < c.nrows; rb += ATTN_DEC_ROWS, ++rbi) {
+                const int nr = std::min(ATTN_DEC_ROWS, c.nrows - rb);
+                t->max_rows = std::max(t->max_rows, nr);
+                const int ctx = c.pos0 + rb + nr;
+                const int ns = std::max((ctx + max_keys - 1) / max_keys, std::min(want, (ctx + 63) / 64));
+                if (ns * m->H > ATTN_COMB_MAX) return fail(m, NV_ECAPACITY, "internal: too many attention splits");
+                const int per = (ctx + ns - 1) / ns;
+                for (int h = 0; h < m->H; ++h)
+                    for (int s2 = 0; s2 < ns; ++s2) {
+                        AttnItem& it = hitems[n_items++];
+                        it.row0 = row0 + rb;
+                        it.nrows = nr;
+                        it.head = h;
+                        it.lo = s2 * per;
+                        it.hi = std::min(ctx, (s2 + 1) * per);
+                        it.part = slot + (h * ns + s2) * nr;
+                        it.split = s2;
+                        it.nsplit = ns;
+                        it.pad[0] = it.pad[1] = it.pad[2] = it.pad[3] = 0;
+                    }
+                for (int i = 0; i < nr; ++i) {
+                    CombineInfo& ci = hcomb[row0 + rb + i];
+                    ci.base = slot;
+                    ci.off = i;
+                    ci.nsplit = ns;
+                    ci.nrows = nr;
+                }
+                slot += m->H * ns * nr;
+            }
+            row0 += c.nrows;
+        }
+        if (slot > P.part_cap || n_items > P.items_cap)
+            return fail(m, NV_ECAPACITY, "internal: attention partials exceed the workspace");
+    } else {
+        // long chunks: row blocks of 32 rows sharing LDS key tiles; the key range is split
+        // into pieces of split_len keys (doubling until the partial slots fit), combined by
+        // a separate pass
+        int split_len = 512;
+        for (;;) {
+            long slots = 0, items = 0;
+            for (const Chunk& c : chunks)
+                for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
+                    int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
+                    int ctx = c.pos0 + rb + nr;
+                    int ns = (ctx + split_len - 1) / split_len;
+                    slots += (long)m->H * ns * nr;
+                    items += (long)m->H * ns;
+                }
+            if (slots <= P.part_cap && items <= P.items_cap &&
+                (long)m->H * ((c_max_ctx(chunks) + split_len - 1) / split_len) <= ATTN_COMB_MAX)
+                break;
+            split_len *= 2;
+        }
+        int slot = 0, row0 = 0;
+        for (const Chunk& c : chunks) {
             for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
                 int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
                 int ctx = c.pos0 + rb + nr;
                 int ns = (ctx + split_len - 1) / split_len;
-                slots += (long)m->H * ns * nr;
-                items += (long)m->H * ns;
-            }
-        if (slots <= P.part_cap && items <= P.items_cap) break;
-        split_len *= 2;
-    }
-    int n_items = 0, slot = 0, row0 = 0;
-    for (const Chunk& c : chunks) {
-        for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
-            int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
-            int ctx = c.pos0 + rb + nr;
-            int ns = (ctx + split_len - 1) / split_len;
-            for (int h = 0; h < m->H; ++h)
-                for (int s2 = 0; s2 < ns; ++s2) {
-                    AttnItem& it = hitems[n_items++];
-                    it.row0 = row0 + rb;
-                    it.nrows = nr;
-                    it.head = h;
-                    it.lo = s2 * split_len;
-                    it.hi = std::min(ctx, (s2 + 1) * split_len);
-                    it.part = slot + (h * ns + s2) * nr;
-                    it.pad0 = it.pad1 = 0;
+                for (int h = 0; h < m->H; ++h)
+                    for (int s2 = 0; s2 < ns; ++s2) {
+                        AttnItem& it = hitems[n_items++];
+                        it.row0 = row0 + rb;
+                        it.nrows = nr;
+                        it.head = h;
+                        it.lo = s2 * split_len;
+                        it.hi = std::min(ctx, (s2 + 1) * split_len);
+                        it.part = slot + (h * ns + s2) * nr;
+                        it.split = s2;
+                        it.nsplit = ns;
+                        it.pad[0] = it.pad[1] = it.pad[2] = it.pad[3] = 0;
+                    }
+                for (int i = 0; i < nr; ++i) {
+                    CombineInfo& ci = hcomb[row0 + rb + i];
+                    ci.base = slot;
+                    ci.off = i;
+                    ci.nsplit = ns;
+                    ci.nrows = nr;
                 }
-            for (int i = 0; i < nr; ++i) {
-                CombineInfo& ci = hcomb[row0 + rb + i];
-                ci.base = slot;
-                ci.off = i;
-                ci.nsplit = ns;
-                ci.nrows = nr;
+                slot += m->H * ns * nr;
             }
-            slot += m->H * ns * nr;
+            row0 += c.nrows;
         }
-        row0 += c.nrows;
     }
+    t->dec = dec;
+    t->any_split = false;
+    for (int i = 0; i < n_items; ++i) t->any_split |= hitems[i].nsplit > 1;
     size_t bytes = (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max + sizeof(AttnItem) * (size_t)n_items;
     NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, bytes, hipMemcpyHostToDevice, m->st));
     m->stage_busy = true;
@@ -348,6 +482,9 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
     t->items = (AttnItem*)(m->d_tables + (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max);
     t->R = R;
     t->n_items = n_items;
+    double kvb = 0;
+    for (int i = 0; i < n_items; ++i) kvb += (double)(hitems[i].hi - hitems[i].lo);
+    t->kv_bytes = kvb * 2.0 * m->hd * m->plan.kes;
     return NV_OK;
 }
 
@@ -361,6 +498,8 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.eps = m->cfg.norm_eps;
         g.wbf16 = m->bf16 ? 1 : 0;
         g.R = t.R;
+        g.rms_ws = m->rms_ws;
+        g.mfma_min_rows = m->mfma_min_rows;
         // q, k, v = RMSNorm(x) W_qkv^T
         g.A = m->Hs;
         g.lda = d;
@@ -369,15 +508,36 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.W = W.wqkv;
         g.N = 3 * d;
         g.K = d;
-        g.epi = EPI_STORE;
-        g.out = m->qkv;
-        g.ldo = 3 * d;
+        g.epi = EPI_QKV;
+        g.out = nullptr;
+        g.ldo = 0;
         g.o_rows = nullptr;
-        NV_HIP(m, launch_gemm(g, m->st));
-        NV_HIP(m, launch_rope_kv(m->qkv, t.rows, t.R, m->kv, l, D, m->rope, m->st));
-        NV_HIP(m, launch_attn(t.items, t.n_items, t.rows, m->qkv, m->kv, l, D, m->part_ml, m->part_o, m->st));
-        NV_HIP(m, launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st));
+        g.q_out = m->qbuf;
+        g.kv = m->kv;
+        g.rope = m->rope;
+        g.layer = l;
+        g.D = D;
+        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+        if (t.dec) {
+            NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
+                return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
+                                       m->part_o, m->attn_o, m->st);
+            }));
+            if (t.any_split)
+                NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
+                    return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
+                }));
+        } else {
+            NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
+                return launch_attn(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o, m->attn_o,
+                                   m->st);
+            }));
+            NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
+                return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
+            }));
+        }
         // x += o W_o^T
+        g.epi = EPI_RESID;
         g.A = m->attn_o;
         g.lda = d;
         g.a_rows = nullptr;
@@ -389,7 +549,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->Hs;
         g.ldo = d;
         g.o_rows = t.rows;
-        NV_HIP(m, launch_gemm(g, m->st));
+        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
         // u = silu(RMSNorm(x) W_g^T) * (RMSNorm(x) W_u^T)
         g.A = m->Hs;
         g.lda = d;
@@ -402,7 +562,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->mlp;
         g.ldo = m->F;
         g.o_rows = nullptr;
-        NV_HIP(m, launch_gemm(g, m->st));
+        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
         // x += u W_d^T
         g.A = m->mlp;
         g.lda = m->F;
@@ -415,7 +575,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->Hs;
         g.ldo = d;
         g.o_rows = t.rows;
-        NV_HIP(m, launch_gemm(g, m->st));
+        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
     }
     return NV_OK;
 }
@@ -491,6 +651,7 @@ void nv_free(nv_model* m) {
     if (m->st) (void)hipStreamSynchronize(m->st);
     if (m->own_arena && m->arena) (void)hipFree(m->arena);
     if (m->h_stage) (void)hipHostFree(m->h_stage);
+    for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
     if (m->h_stepblk) (void)hipHostFree(m->h_stepblk);
     if (m->h_gatelist) (void)hipHostFree(m->h_gatelist);
     if (m->h_headlist) (void)hipHostFree(m->h_headlist);
@@ -584,11 +745,14 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->Hs = (float*)m->take(P.hidden);
     m->kv = m->take(P.kv);
     m->rope = (float*)m->take(P.rope);
-    m->qkv = (float*)m->take(P.qkv);
+    m->qbuf = (float*)m->take(P.qbuf);
+
     m->attn_o = (float*)m->take(P.attn_o);
     m->mlp = (float*)m->take(P.mlp);
     m->part_ml = (float*)m->take(P.part_ml);
     m->part_o = (float*)m->take(P.part_o);
+    m->rms_ws = (float*)m->take(P.rms);
+    if (const char* e = std::getenv("NVIUM_MFMA_MIN_ROWS")) m->mfma_min_rows = std::atoi(e);
     m->d_tables = m->take(P.tables);
     m->d_stepblk = m->take(m->stepblk_bytes());
     m->d_gatelist = m->take(m->list_bytes());
@@ -651,13 +815,32 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
         }
         off += rows * row_bytes;
     };
+    // W_q, W_k, W_v are adjacent in the file; device row 2p + i of the fused matrix is
+    // original row part*d + h*hd + j + i*hd/2 (p = part*d/2 + h*hd/2 + j), so RoPE partners
+    // land in adjacent output columns of the QKV product
+    std::vector<char> qkv_file(3 * d * d * es), qkv_dev(3 * d * d * es);
+    auto copy_qkv = [&](void* dst) {
+        off = align_up(off);
+        for (int part = 0; part < 3 && io_ok; ++part) {
+            off = align_up(off);
+            if (!pread_all(fd, qkv_file.data() + part * d * d * es, d * d * es, off)) io_ok = false;
+            off += d * d * es;
+        }
+        if (!io_ok || herr != hipSuccess) return;
+        const size_t half = m->hd / 2, row = d * es;
+        for (size_t pr = 0; pr < 3 * d / 2; ++pr) {
+            const size_t part = pr / (d / 2), pp = pr % (d / 2), h = pp / half, j = pp % half;
+            const size_t src0 = part * d + h * m->hd + j;
+            std::memcpy(qkv_dev.data() + (2 * pr) * row, qkv_file.data() + src0 * row, row);
+            std::memcpy(qkv_dev.data() + (2 * pr + 1) * row, qkv_file.data() + (src0 + half) * row, row);
+        }
+        herr = hipMemcpy(dst, qkv_dev.data(), qkv_dev.size(), hipMemcpyHostToDevice);
+    };
     copy_tensor(m->embed, V * d * es);
     for (int l = 0; l < m->L && io_ok && herr == hipSuccess; ++l) {
         LayerPtrs& W = m->layers[l];
         copy_tensor(W.attn_norm, d * 4);
-        copy_tensor(W.wqkv, d * d * es);
-        copy_tensor((char*)W.wqkv + d * d * es, d * d * es);
-        copy_tensor((char*)W.wqkv + 2 * d * d * es, d * d * es);
+        copy_qkv(W.wqkv);
         copy_tensor(W.wo, d * d * es);
         copy_tensor(W.mlp_norm, d * 4);
         copy_interleaved(W.wgu, F, d * es, 0);
@@ -674,6 +857,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     if (!io_ok) return fail(m, NV_EIO, "weights file read failed");
     NV_HIP(m, herr);
     NV_HIP(m, launch_rope_table(m->rope, max_ctx, m->hd, c.rope_base, m->st));
+
     NV_HIP(m, hipStreamSynchronize(m->st));
     m->seqs.assign(max_batch, SeqHost());
     m->last_w.assign((size_t)max_batch * 4, NAN);
@@ -749,8 +933,10 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
     }
     NV_HIP(m, hipMemcpyAsync(m->d_stepblk, hb, m->stepblk_bytes(), hipMemcpyHostToDevice, m->st));
     const float* d_unif = nv_model::unif(m->d_stepblk);
-    NV_HIP(m, launch_embed(m->tok_in(m->d_stepblk), m->cur_rows(m->d_stepblk), n, m->embed, m->bf16, m->Hs, m->d,
-                           m->st));
+    NV_TRY(timed(m, NV_TIME_OTHER, (double)n * m->d * (m->plan.es + 4), [&] {
+        return launch_embed(m->tok_in(m->d_stepblk), m->cur_rows(m->d_stepblk), n, m->embed, m->bf16, m->Hs, m->d,
+                            m->st);
+    }));
 
     std::vector<int> active(n), exit_of(n, kMaxExits);
     for (int i = 0; i < n; ++i) active[i] = i;
@@ -777,9 +963,10 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
                 m->lrows(gl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
             }
             NV_HIP(m, hipMemcpyAsync(m->d_gatelist, gl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
-            NV_HIP(m, launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs,
-                                  m->d, m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop,
-                                  m->st));
+            NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
+                return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
+                                   m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
+            }));
             NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
             NV_HIP(m, hipStreamSynchronize(m->st));
             m->stage_busy = false;
@@ -818,15 +1005,21 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
             g.out = m->logits;
             g.ldo = m->V;
             g.o_rows = m->lorows(m->d_headlist);
-            NV_HIP(m, launch_gemm(g, m->st));
-            NV_HIP(m, launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif,
-                                    m->d_tok_out, m->st));
+            g.head = 1;
+            g.rms_ws = m->rms_ws;
+            g.mfma_min_rows = m->mfma_min_rows;
+            NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+            NV_TRY(timed(m, NV_TIME_OTHER, (double)ns * m->V * 4, [&] {
+                return launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif,
+                                     m->d_tok_out, m->st);
+            }));
         }
     }
     NV_HIP(m, hipMemcpyAsync(htok_out, m->d_tok_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipMemcpyAsync(hw, m->d_w, (size_t)n * 32, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipStreamSynchronize(m->st));
     m->stage_busy = false;
+    if (m->timing) NV_TRY(resolve_timing(m));
     for (int i = 0; i < n; ++i) {
         SeqHost& S = m->seqs[i];
         const int e = exit_of[i];
@@ -937,6 +1130,37 @@ nv_status nv_debug_hidden(nv_model* m, int32_t seq, int32_t pos0, int32_t n, flo
     NV_HIP(m, hipStreamSynchronize(m->st));
     NV_HIP(m, hipMemcpy(out, m->Hs + ((size_t)seq * m->max_ctx + pos0) * m->d, (size_t)n * m->d * 4,
                         hipMemcpyDeviceToHost));
+    return NV_OK;
+}
+
+nv_status nv_timing_enable(nv_model* m, int32_t on) {
+    if (!m) return NV_EINVAL;
+    if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    if (on && m->ev.empty()) {
+        m->ev.resize(2 * kEventPairs);
+        m->ev_kind.resize(kEventPairs);
+        m->ev_bytes.resize(kEventPairs);
+        for (auto& e : m->ev) NV_HIP(m, hipEventCreate(&e));
+    }
+    m->ev_used = 0;
+    for (int k = 0; k < NV_TIME_CLASSES; ++k) {
+        m->t_ms[k] = m->t_bytes[k] = 0;
+        m->t_n[k] = 0;
+    }
+    m->timing = on != 0;
+    return NV_OK;
+}
+
+nv_status nv_timing_read(nv_model* m, double* ms, double* bytes, int64_t* launches) {
+    if (!m || !ms || !bytes || !launches) return m ? fail(m, NV_EINVAL, "null pointer") : NV_EINVAL;
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    NV_TRY(resolve_timing(m));
+    for (int k = 0; k < NV_TIME_CLASSES; ++k) {
+        ms[k] = m->t_ms[k];
+        bytes[k] = m->t_bytes[k];
+        launches[k] = m->t_n[k];
+    }
     return NV_OK;
 }
 

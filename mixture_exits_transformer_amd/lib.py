@@ -57,7 +57,10 @@ _SIGS = {
     "nv_debug_kv": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _F32P,
                                    _F32P]),
     "nv_debug_hidden": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _F32P]),
+    "nv_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "nv_timing_read": (ctypes.c_int, [_P, _F64P, _F64P, ctypes.POINTER(ctypes.c_int64)]),
 }
+TIME_CLASSES = ("block_gemm", "attention", "exit_head", "other")
 EXPORTED = tuple(_SIGS)
 
 
@@ -212,3 +215,17 @@ def nv_debug_hidden(h: Handle, seq: int, pos0: int, n: int) -> np.ndarray:
     out = np.empty((n, h.cfg.d_model), np.float32)
     _check(h.ptr, library().nv_debug_hidden(h.ptr, seq, pos0, n, _ptr(out, ctypes.c_float)))
     return out
+
+
+def nv_timing_enable(h: Handle, on: bool = True) -> None:
+    _check(h.ptr, library().nv_timing_enable(h.ptr, 1 if on else 0))
+
+
+def nv_timing_read(h: Handle) -> dict:
+    """{class: (device ms, algorithmic bytes, launches)} since nv_timing_enable."""
+    ms = np.zeros(4, np.float64)
+    by = np.zeros(4, np.float64)
+    n = np.zeros(4, np.int64)
+    _check(h.ptr, library().nv_timing_read(h.ptr, _ptr(ms, ctypes.c_double), _ptr(by, ctypes.c_double),
+                                           _ptr(n, ctypes.c_int64)))
+    return {c: (float(ms[i]), float(by[i]), int(n[i])) for i, c in enumerate(TIME_CLASSES)}

@@ -172,12 +172,33 @@ def shape_key(m: ModelShape) -> str:
     return hashlib.sha1(repr(m).encode()).hexdigest()[:12]
 
 
+def _tensor_key(m: ModelShape) -> str:
+    """Key of the tensor values alone (the gate biases live in the header)."""
+    from dataclasses import replace
+    return shape_key(replace(m, gate_bias=(0.0, 0.0, 0.0)))
+
+
 def cached_weights(m: ModelShape, cache_dir: str = None) -> str:
-    """Path of the weights file for `m`, writing it once per cache directory."""
+    """Path of the weights file for `m`, writing it once per cache directory.  A model
+    that differs from a cached one only in its gate biases is made by copying that file
+    and rewriting the header's bias field."""
+    import shutil
     cache_dir = cache_dir or os.environ.get("NVIUM_WEIGHTS_DIR") or os.path.join(
         tempfile.gettempdir(), "nvium_weights")
     os.makedirs(cache_dir, exist_ok=True)
-    path = os.path.join(cache_dir, f"nvium-{m.n_layers}x{m.d_model}-{m.wdtype}-{shape_key(m)}.nvw")
-    if not os.path.exists(path) or os.path.getsize(path) != file_size(m):
-        write_weights(m, path)
+    stem = f"nvium-{m.n_layers}x{m.d_model}-{m.wdtype}-{_tensor_key(m)}"
+    path = os.path.join(cache_dir, f"{stem}-{shape_key(m)}.nvw")
+    size = file_size(m)
+    if os.path.exists(path) and os.path.getsize(path) == size:
+        return path
+    sibling = next((os.path.join(cache_dir, f) for f in sorted(os.listdir(cache_dir))
+                    if f.startswith(stem + "-") and f.endswith(".nvw")
+                    and os.path.getsize(os.path.join(cache_dir, f)) == size), None)
+    if sibling is None:
+        return write_weights(m, path)
+    tmp = path + f".tmp{os.getpid()}"
+    shutil.copyfile(sibling, tmp)
+    with open(tmp, "r+b") as f:
+        f.write(header_bytes(m))
+    os.replace(tmp, path)
     return path

@@ -37,10 +37,31 @@ class StepCheck:
     unexplained: List[str] = field(default_factory=list)
     max_logit_rel: float = 0.0
     max_gate_abs: float = 0.0
+    max_cdf_shift: float = 0.0
+    logit_explained: int = 0
+    gate_explained: int = 0
+
+    def summary(self) -> str:
+        return (f"steps {self.steps} exits equal {self.exit_equal} tokens equal {self.token_equal} "
+                f"near-boundary(1e-5) {self.near_boundary} within-cdf-shift {self.logit_explained} "
+                f"within-gate-shift {self.gate_explained} "
+                f"max logit rel {self.max_logit_rel:.2e} max gate abs {self.max_gate_abs:.2e} "
+                f"max cdf shift {self.max_cdf_shift:.2e}")
+
+
+def cdf_shift(g_logits, pi_oracle) -> float:
+    """Largest gap between the CDF implied by the device's logits and the oracle's CDF
+    (float64, token-id order)."""
+    z = np.asarray(g_logits, np.float64)
+    e = np.exp(z - z.max())
+    return float(np.max(np.abs(np.cumsum(e / e.sum()) - np.cumsum(pi_oracle))))
 
 
 def check_step(t: int, o: om.StepOut, g_tok: int, g_exit: int, g_logits, g_w, res: StepCheck,
-               band: float = BAND) -> None:
+               band: float = BAND, logit_band: bool = False) -> None:
+    """logit_band: for reduced-precision paths, also accept a token difference when the
+    draw lies within the CDF shift that the device's (tolerance-checked) logits imply, and
+    an exit difference when the draw lies between the device's and the oracle's gate value."""
     res.steps += 1
     u = o.u
     # gates: the device reports w for every gate it walked
@@ -52,8 +73,11 @@ def check_step(t: int, o: om.StepOut, g_tok: int, g_exit: int, g_logits, g_w, re
     else:
         k = min(g_exit, o.exit) - 1              # the gate where the two walks part
         dist = abs(float(u[k]) - o.w[k])
+        wshift = abs(float(g_w[k]) - o.w[k]) if (logit_band and np.isfinite(g_w[k])) else 0.0
         if dist < band:
             res.near_boundary += 1
+        elif dist <= wshift:                     # the draw lies between the two gate values
+            res.gate_explained += 1
         else:
             res.unexplained.append(f"step {t}: exit device {g_exit} oracle {o.exit} (gate distance {dist:.3g})")
             return
@@ -69,8 +93,12 @@ def check_step(t: int, o: om.StepOut, g_tok: int, g_exit: int, g_logits, g_w, re
     u4 = float(u[3])
     d1 = om.boundary_distances(o, g_tok, g_exit)["token"]
     d2 = min(abs(u4 - (F[want - 1] if want > 0 else 0.0)), abs(F[want] - u4))
+    shift = cdf_shift(g_logits, pi) if (logit_band and g_logits is not None) else 0.0
+    res.max_cdf_shift = max(res.max_cdf_shift, shift)
     if min(d1, d2) < band:
         res.near_boundary += 1
+    elif min(d1, d2) < shift:
+        res.logit_explained += 1
     else:
         res.unexplained.append(f"step {t}: token device {g_tok} oracle {want} (cdf distance {min(d1, d2):.3g})")
 

@@ -1,0 +1,92 @@
+"""Parity of the bf16 path (matrix-core GEMM for chunks of >= 16 rows, bf16 KV) with
+the oracle on a tiny bf16 model: logits and KV within 2e-2 relative; exits equal
+unless a draw is within 1e-5 of a gate; tokens equal unless the draw is within the
+CDF shift that the tolerance-checked logits imply (counted and reported)."""
+import numpy as np
+import pytest
+
+from oracle import model as om
+from synth import cached_weights, tiny_variant
+from tests.parity import StepCheck, check_step, rel, run_forced
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+BF16_TINY = tiny_variant(wdtype="bf16", ffn=384)
+STOP, GO = 0.0, np.float32(1.0 - 2.0 ** -24)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mixture_exits_transformer_amd.lib as L
+    L.library()
+    return L
+
+
+def _forced_u(pattern, rng):
+    U = rng.random((len(pattern), 4)).astype(np.float32)
+    for t, e in enumerate(pattern):
+        if e == 0:
+            continue                      # free draw
+        U[t, :3] = GO
+        if e < 4:
+            U[t, e - 1] = STOP
+    return U
+
+
+@pytest.mark.parametrize("prompt_len,pattern", [
+    (64, [0] * 24),                             # prefill of 63 rows (64-row tiles, 16-column blocks)
+    (100, [1] * 18 + [4] + [2] * 20 + [3, 4]),  # prefill of 99 rows (64-column blocks); 19- and 22-row chunks
+    (9, [1] * 70 + [4]),                        # a 71-row chunk at segments 2..4 (two row tiles)
+])
+def test_tiny_bf16_parity(lib, weights_dir, prompt_len, pattern):
+    path = cached_weights(BF16_TINY, weights_dir)
+    M = om.OracleModel(path)
+    rng = np.random.default_rng(prompt_len)
+    prompt = rng.integers(0, M.V, size=prompt_len)
+    U = _forced_u(pattern, rng)
+    max_ctx = prompt_len + len(pattern)
+    outs, st = om.generate(M, prompt, U, max_ctx=max_ctx)
+    h = lib.nv_load(path, 1, max_ctx)
+    try:
+        lib.nv_prefill(h, 0, prompt)
+        recs = run_forced(h, lib, outs)
+        res = StepCheck()
+        for t, (o, (tok, ex, lg, gw)) in enumerate(zip(outs, recs)):
+            if pattern[t]:
+                assert ex == pattern[t]
+            check_step(t, o, tok, ex, lg, gw, res, logit_band=True)
+        print("\nbf16 tiny:", res.summary())
+        assert not res.unexplained, res.unexplained
+        assert res.max_logit_rel < TOL
+        lib.nv_flush(h)
+        n = prompt_len - 1 + len(pattern)
+        worst = 0.0
+        for l in range(M.L):
+            k, v = lib.nv_debug_kv(h, 0, l, 0, n)
+            worst = max(worst, rel(k, st.kv.K[l, :n]), rel(v, st.kv.V[l, :n]))
+        print("bf16 tiny KV worst rel", worst)
+        assert worst < TOL
+    finally:
+        lib.nv_free(h)
+
+
+def test_mfma_and_valu_paths_agree(lib, weights_dir, monkeypatch):
+    """The same chunks through the matrix-core GEMM and through the vector-ALU GEMM give
+    the same KV to bf16 rounding."""
+    path = cached_weights(BF16_TINY, weights_dir)
+    rng = np.random.default_rng(5)
+    prompt = rng.integers(0, BF16_TINY.vocab, size=40)
+    kvs = []
+    for thr in ("16", "0"):
+        monkeypatch.setenv("NVIUM_MFMA_MIN_ROWS", thr)
+        h = lib.nv_load(path, 1, 48)
+        try:
+            lib.nv_prefill(h, 0, prompt)
+            kvs.append([lib.nv_debug_kv(h, 0, l, 0, 39) for l in range(BF16_TINY.n_layers)])
+        finally:
+            lib.nv_free(h)
+    for (k1, v1), (k2, v2) in zip(*kvs):
+        assert rel(k1, k2) < 1e-2 and rel(v1, v2) < 1e-2
