@@ -10,9 +10,10 @@ head and the draw.  Inputs are resident in device memory before timing starts.
 
 Printed: one JSON line.  `value` = generated tokens/s over the timed steps.
 Beside it: the same kernels with every intermediate gate closed (all tokens exit at
-4, standard decode), per-kernel-class device time from HIP events in a second,
-identical pass (roofline of the block GEMM against 8 TB/s), and the CPU oracle
-timed on a bounded sample of the same decode.
+4, standard decode), per-kernel device time from a second, identical pass (device
+wall-clock stamps per block for the decode GEMMs and attention, HIP events for the
+rest; roofline of the dominant block GEMM against 8 TB/s), and the CPU oracle timed
+on a bounded sample of the same decode.
 """
 from __future__ import annotations
 
@@ -46,13 +47,17 @@ def run_decode(lib, h, prompt, U, steps, warmup):
 
 
 def timing_pass(lib, h, prompt, U, steps):
+    """The same decode again with per-launch device timing: the stream is drained
+    before each launch, and the launch is timed by per-block wall-clock stamps (or HIP
+    events for kernels without stamps) on the work stream."""
     lib.nv_prefill(h, 0, prompt)
     lib.nv_timing_enable(h, True)
     for t in range(steps):
         lib.nv_step(h, U[t:t + 1])
     res = lib.nv_timing_read(h)
+    ker = lib.nv_timing_kernels(h)
     lib.nv_timing_enable(h, False)
-    return res
+    return res, ker
 
 
 def cpu_baseline(wl, path, prompt, U, budget_s):
@@ -90,10 +95,12 @@ def main():
     ap.add_argument("--no-baseline", action="store_true", help="skip the exit-4-forced run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with one 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path "
-              f"is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path "
+              f"runs on a single GPU", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -115,7 +122,7 @@ def main():
     path = cached_weights(wl.model)
     h = lib.nv_load(path, 1, max_ctx)
     dt, exits = run_decode(lib, h, prompt, U, steps, warmup)
-    tim = timing_pass(lib, h, prompt, U, steps)
+    tim, ker = timing_pass(lib, h, prompt, U, steps)
     lib.nv_free(h)
     tok_s = steps / dt
 
@@ -128,8 +135,11 @@ def main():
         assert set(ex4) == {4}
         base = steps / dt4
 
-    ms, by, nl = tim["block_gemm"]
+    # dominant kernel: the block-GEMM symbol with the most device time
+    gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
+    _, nl, ms, by, kname = gemms[0]
     achieved = by / (ms * 1e-3) / 1e9
+    top = sorted(ker, key=lambda k: -k[2])[:8]
     hist = np.bincount(np.asarray(exits), minlength=5)[1:]
     out = {
         "metric": "generated tokens/s, 1.5B bs=1, vs exit-4-forced decode; achieved HBM GB/s",
@@ -146,11 +156,16 @@ def main():
         "data": "synthetic: uniform-random token ids, seeded uniforms, random-init N(0,0.02) weights",
         "config": {"workload": f"{wl.name}: {wl.note}", "batch": wl.batch, "prompt": len(prompt),
                    "decode_steps": steps},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_valu (transformer-block skinny GEMMs)",
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
                      "bytes_per_launch": round(by / max(nl, 1))},
+        "block_gemm_all": {"achieved_GBps": round(tim["block_gemm"][1] / (tim["block_gemm"][0] * 1e-3) / 1e9, 1),
+                           "launches": tim["block_gemm"][2]},
+        "top_kernels": [{"kernel": k[4], "class": k[0], "launches": k[1],
+                         "avg_us": round(k[2] / max(k[1], 1) * 1e3, 3),
+                         "GBps": round(k[3] / (k[2] * 1e-3) / 1e9, 1) if k[2] > 0 else None} for k in top],
         "kernel_classes_ms_per_step": {k: round(v[0] / steps, 4) for k, v in tim.items()},
         "exit4_forced_tokens_per_s": round(base, 2) if base else None,
         "speedup_vs_exit4": round(tok_s / base - 1.0, 4) if base else None,
@@ -160,6 +175,13 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, path, prompt, U[:steps], args.cpu_budget)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = 1 << 30
     print(json.dumps(out), flush=True)
 
 

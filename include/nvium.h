@@ -157,6 +157,11 @@ nv_status nv_timing_enable(nv_model *m, int32_t on);
  * bytes and launches[k] launches of class k, for k < NV_TIME_CLASSES. */
 nv_status nv_timing_read(nv_model *m, double *ms, double *bytes, int64_t *launches);
 
+/* The same totals per kernel symbol, as text: one line per kernel,
+ * "class<TAB>launches<TAB>device ms<TAB>algorithmic bytes<TAB>symbol\n" (symbols as
+ * profilers print them).  NV_ECAPACITY if `cap` bytes cannot hold it. */
+nv_status nv_timing_kernels(nv_model *m, char *out, size_t cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,4 +7,4 @@ from . import lib  # noqa: F401
 from .lib import (NvError, nv_debug_frontiers, nv_debug_gates, nv_debug_hidden,  # noqa: F401
                   nv_debug_kv, nv_debug_logits, nv_flush, nv_free, nv_last_error, nv_load,
                   nv_mem_required, nv_prefill, nv_step, nv_step_forced, nv_timing_enable,
-                  nv_timing_read)
+                  nv_timing_kernels, nv_timing_read)

@@ -6,6 +6,7 @@
 namespace nv {
 
 struct RowInfo;
+struct CombineInfo;
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
 
@@ -42,6 +43,15 @@ struct GemmArgs {
     const float* rope;    // [max_ctx][hd/2] (cos, sin)
     int layer;
     LayerDims D;
+    // Timing only: when set, block b stores its start and end (device wall-clock ticks) at
+    // stamp[2b] and stamp[2b + 1] (vector-ALU and matrix-core decode kernels).
+    unsigned long long* stamp;
+    // Single-row attention output merged on the fly (vector-ALU path, R == 1): when set,
+    // the activation row is the merge of the split partials described by comb[0]
+    // (rows whose key range was not split are read from A).
+    const struct CombineInfo* comb;
+    const float* part_ml;
+    const float* part_o;
 };
 
 // One row of a chunk: position `pos` of sequence `seq`; hrow = seq * max_ctx + pos
@@ -74,7 +84,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // (row block, head); split partials are merged by launch_attn_combine.
 constexpr int ATTN_DEC_ROWS = 8;
 constexpr int ATTN_DEC_ITERS = 4;
-constexpr int ATTN_COMB_MAX = 4096;      // (head, split) pairs per row the combine pass holds   // key groups per wave: a split covers <= 16 * (512 / head_dim) keys
+constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds   // key groups per wave: a split covers <= 16 * (512 / head_dim) keys
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
                            float* out, hipStream_t st);
@@ -90,5 +100,13 @@ hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float*
 hipError_t launch_sample(const float* logits, int64_t ld, const int* seqs, int n, int V,
                          const float* uniforms, int* tok_out, hipStream_t st);
 hipError_t init_kernel_attributes();
+// Timing: the next launch stamps `start` at its start; every launch stamps `stop` at its
+// end, until cleared with (nullptr, nullptr).
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+const char* last_launch_name();   // symbol of the last kernel issued while timing
+// Timing: block-stamp buffer the next stamped kernels write (nullptr: none).
+void set_launch_stamp(unsigned long long* stamps);
+constexpr int STAMP_BLOCKS = 8192;  // largest grid the timing stamps cover
+hipError_t launch_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec, hipStream_t st);
 
 }  // namespace nv

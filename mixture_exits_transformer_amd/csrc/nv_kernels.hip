@@ -6,9 +6,41 @@
 // causal chunks of deferred rows follow section 2, part "Inferenz: Piggybacking".
 #include "nv_internal.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
+#include <stdio.h>
 
 namespace nv {
+
+// Measurement events for the next launches (set by the runtime's timing mode).  The
+// dispatch packet itself stamps them, so they bracket the kernel's execution only.
+static thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
+static thread_local unsigned long long* t_stamp = nullptr;
+
+void set_launch_stamp(unsigned long long* stamps) { t_stamp = stamps; }
+
+// Symbol of the last kernel a launch wrapper issued while timing (as profilers print it).
+static thread_local char t_name[160];
+
+const char* last_launch_name() { return t_name; }
+
+
+
+#define NV_LAUNCH(K, G, B, SHM, ST, ...)                                                     \
+    do {                                                                                     \
+        if (t_ev_stop) {                                                                     \
+            hipExtLaunchKernelGGL((K), G, B, SHM, ST, t_ev_start, t_ev_stop, 0, __VA_ARGS__);  \
+            t_ev_start = nullptr;                                                            \
+        } else {                                                                             \
+            hipLaunchKernelGGL((K), G, B, SHM, ST, __VA_ARGS__);                             \
+        }                                                                                    \
+    } while (0)
 
 // ------------------------------------------------------------------------------------------
 // small helpers
@@ -87,7 +119,7 @@ __global__ void k_rope_table(float* cs, int max_ctx, int hd, double base) {
 
 hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStream_t st) {
     int64_t n = (int64_t)max_ctx * (hd / 2);
-    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cs, max_ctx, hd,
+    NV_LAUNCH(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cs, max_ctx, hd,
                        (double)base);
     return hipGetLastError();
 }
@@ -110,7 +142,7 @@ __global__ void k_embed(const int* tokens, const RowInfo* rows, int n, const voi
 hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const void* E, int wbf16, float* Hs, int d,
                         hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_embed, dim3(n), dim3(256), 0, st, tokens, rows, n, E, wbf16, Hs, d);
+    NV_LAUNCH(k_embed, dim3(n), dim3(256), 0, st, tokens, rows, n, E, wbf16, Hs, d);
     return hipGetLastError();
 }
 
@@ -165,6 +197,55 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, floa
     }
 }
 
+
+
+// Kernel-span stamps for timing mode: each block stores its start and end (device
+// wall clock) at stamp[2 * block], stamp[2 * block + 1]; k_stamp_reduce folds them.
+__device__ __forceinline__ unsigned long long stamp_begin(const unsigned long long* stamp) {
+    return stamp ? (unsigned long long)wall_clock64() : 0ull;
+}
+
+__device__ __forceinline__ void stamp_end(unsigned long long* stamp, unsigned long long t0) {
+    if (stamp) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            stamp[2 * blockIdx.x] = t0;
+            stamp[2 * blockIdx.x + 1] = (unsigned long long)wall_clock64();
+        }
+    }
+}
+
+// (first start, last end) over the block stamps of one launch into rec[0..1]; the stamp
+// slots are reset to (max, 0) for the next launch.
+__global__ __launch_bounds__(256) void k_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec) {
+    __shared__ unsigned long long lo[256], hi[256];
+    unsigned long long a = ~0ull, b = 0ull;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        a = min(a, stamps[2 * i]);
+        b = max(b, stamps[2 * i + 1]);
+        stamps[2 * i] = ~0ull;
+        stamps[2 * i + 1] = 0ull;
+    }
+    lo[threadIdx.x] = a;
+    hi[threadIdx.x] = b;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) {
+            lo[threadIdx.x] = min(lo[threadIdx.x], lo[threadIdx.x + s]);
+            hi[threadIdx.x] = max(hi[threadIdx.x], hi[threadIdx.x + s]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        rec[0] = lo[0];
+        rec[1] = hi[0];
+    }
+}
+
+hipError_t launch_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec, hipStream_t st) {
+    hipLaunchKernelGGL(k_stamp_reduce, dim3(1), dim3(256), 0, st, stamps, n, rec);
+    return hipGetLastError();
+}
 
 // What the epilogue of one (row, column pair) needs from memory, fetched early so the
 // epilogue itself issues no dependent loads.
@@ -622,13 +703,15 @@ __device__ __forceinline__ float wave_transpose_sum(float (&v)[N], int lane) {
 
 constexpr int KS_CPB = 8;          // output columns per block (vector-ALU kernel)
 
-template <bool WBF, int RM, int HEAD>
+template <bool WBF, int RM, int HEAD, bool COMB = false>
 __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
+    static_assert(!COMB || RM == 1, "the fused attention merge handles one row");
     constexpr int EPC = WBF ? 8 : 4;
     constexpr int ESZ = WBF ? 2 : 4;
     constexpr int NV = KS_CPB * RM;     // values per lane to reduce
     __shared__ float red[8][NV];
     __shared__ float ssr[8][RM];
+    const unsigned long long t_begin = stamp_begin(a.stamp);
     const int K = a.K, R = a.R;
     const int nch = K / EPC;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -645,15 +728,18 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 
     // activation chunks (rows past R repeat row R-1; their results are never written)
     float av[RM][EPC];
+    const CombineInfo cmb = COMB ? a.comb[0] : CombineInfo{0, 0, 1, 1};
+    if (!COMB || cmb.nsplit == 1) {
 #pragma unroll
-    for (int r = 0; r < RM; ++r) {
-        const int rr = r < R ? r : R - 1;
-        const int ar = a.a_rows ? a.a_rows[rr].hrow : rr;
-        const float4* ap = (const float4*)(a.A + (int64_t)ar * a.lda + k0);
+        for (int r = 0; r < RM; ++r) {
+            const int rr = r < R ? r : R - 1;
+            const int ar = a.a_rows ? a.a_rows[rr].hrow : rr;
+            const float4* ap = (const float4*)(a.A + (int64_t)ar * a.lda + k0);
 #pragma unroll
-        for (int e = 0; e < EPC / 4; ++e) {
-            const float4 t = ap[e];
-            av[r][4 * e] = t.x; av[r][4 * e + 1] = t.y; av[r][4 * e + 2] = t.z; av[r][4 * e + 3] = t.w;
+            for (int e = 0; e < EPC / 4; ++e) {
+                const float4 t = ap[e];
+                av[r][4 * e] = t.x; av[r][4 * e + 1] = t.y; av[r][4 * e + 2] = t.z; av[r][4 * e + 3] = t.w;
+            }
         }
     }
     float gv[EPC];
@@ -668,6 +754,49 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
     uint4 w[KS_CPB];
 #pragma unroll
     for (int c = 0; c < KS_CPB; ++c) w[c] = *(const uint4*)((const char*)a.W + ((size_t)(n0 + c) * K + k0) * ESZ);
+
+    if constexpr (COMB) {
+        if (cmb.nsplit > 1) {
+            // this lane's 8 dims (e0..e0+7 of head h) of the attention output: online merge of
+            // the split partials (max m_s, sum l_s, unnormalised output o_s), 8 splits per batch
+            const int hd = a.D.hd;
+            const int h = k0 / hd, e0 = k0 - h * hd;
+            const int ns = cmb.nsplit;
+            const int64_t base = cmb.base + (int64_t)h * ns * cmb.nrows + cmb.off;
+            float M = -INFINITY, L = 0.f, O[EPC];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) O[e] = 0.f;
+            for (int s0 = 0; s0 < ns; s0 += 8) {
+                float2 ml[8];
+                float ob[8][EPC];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int sp = s0 + j < ns ? s0 + j : ns - 1;
+                    const int64_t slot = base + (int64_t)sp * cmb.nrows;
+                    ml[j] = *(const float2*)(a.part_ml + 2 * slot);
+                    const float4* op = (const float4*)(a.part_o + slot * hd + e0);
+#pragma unroll
+                    for (int q4 = 0; q4 < EPC / 4; ++q4) {
+                        const float4 t = op[q4];
+                        ob[j][4 * q4] = t.x; ob[j][4 * q4 + 1] = t.y; ob[j][4 * q4 + 2] = t.z; ob[j][4 * q4 + 3] = t.w;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (s0 + j < ns && ml[j].x != -INFINITY) {
+                        const float Mn = fmaxf(M, ml[j].x);
+                        const float ca = expf(M - Mn), cb = expf(ml[j].x - Mn);
+                        L = ca * L + cb * ml[j].y;
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) O[e] = ca * O[e] + cb * ob[j][e];
+                        M = Mn;
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) av[0][e] = O[e] / L;
+        }
+    }
 
     const float amask = act ? 1.0f : 0.0f;   // lanes past the end of K contribute nothing
     float ss[RM];
@@ -729,6 +858,7 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
         }
         epi_apply(a, ectx, er, n0 + ec, v0, v1);
     }
+    stamp_end(a.stamp, t_begin);
 }
 
 // Matrix-core version for 9..32 rows: the block owns 16 columns; wave w takes the w-th
@@ -740,6 +870,7 @@ template <int S, int MT, bool NORM, int HEAD>
 __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
     __shared__ float red[16][MT][64][4];
     __shared__ float ssr[16][MT * 16];
+    const unsigned long long t_begin = stamp_begin(a.stamp);
     const int K = a.K, R = a.R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int n0 = blockIdx.x * 16;
@@ -848,6 +979,7 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
             if (row < R && (ecol & 1) == 0) epi_apply(a, ectx[i], row, ecol, y, u);
         }
     }
+    stamp_end(a.stamp, t_begin);
 }
 
 static bool use_mfma(const GemmArgs& a) {
@@ -858,6 +990,15 @@ static bool use_mfma(const GemmArgs& a) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.R <= 0) return hipSuccess;
     const int epc = a.wbf16 ? 8 : 4;
+    GemmArgs b = a;
+    b.stamp = t_stamp;
+    if (a.comb) {   // single row, attention output merged on the fly (vector-ALU path only)
+        const int nw = (a.K / epc + 63) / 64;
+        if (a.R != 1 || !a.wbf16 || a.K % epc || a.N % KS_CPB || nw > 8 || a.D.hd % 8) return hipErrorInvalidValue;
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<true, 1, 0, true>(nv::GemmArgs)");
+        NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<true, 1, 0, true>), dim3(a.N / KS_CPB), dim3(64 * nw), 0, st, b);
+        return hipGetLastError();
+    }
     // decode-sized rows, vector ALUs (rows <= 8, and below the matrix-core threshold)
     if (a.R <= 8 && (a.mfma_min_rows == 0 || a.R < a.mfma_min_rows || !a.wbf16) && a.K % epc == 0 &&
         a.N % KS_CPB == 0 && (a.K / epc + 63) / 64 <= 8 && a.K % 4 == 0) {
@@ -866,9 +1007,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         const int rm = a.R <= 1 ? 1 : a.R <= 2 ? 2 : a.R <= 4 ? 4 : 8;
 #define NV_KS(WB, RMV)                                                                                        \
     do {                                                                                                     \
-        if (a.head) hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 1>), grid, block, 0, st, a);       \
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 0>), grid, block, 0, st, a);              \
+        if (a.head) NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 1>), grid, block, 0, st, b);       \
+        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 0>), grid, block, 0, st, b);              \
     } while (0)
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<%s, %d, %d>(nv::GemmArgs)",
+                                a.wbf16 ? "true" : "false", rm, a.head ? 1 : 0);
         if (a.wbf16) {
             if (rm == 1) NV_KS(true, 1); else if (rm == 2) NV_KS(true, 2); else if (rm == 4) NV_KS(true, 4); else NV_KS(true, 8);
         } else {
@@ -890,14 +1033,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
             const dim3 grid(a.N / 16), block(64 * nw);
 #define NV_MKS2(SV, MTV, NV_)                                                                                  \
     do {                                                                                                      \
-        if (a.head) hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 1>), grid, block, 0, st, a); \
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 0>), grid, block, 0, st, a);        \
+        if (a.head) NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 1>), grid, block, 0, st, b); \
+        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 0>), grid, block, 0, st, b);        \
     } while (0)
 #define NV_MKS(SV, MTV)                                                                                        \
     do {                                                                                                      \
         if (a.norm_w) NV_MKS2(SV, MTV, true); else NV_MKS2(SV, MTV, false);                                   \
     } while (0)
             if (nw >= 2 || a.R <= 16) {
+                if (t_ev_stop)
+                    snprintf(t_name, sizeof(t_name), "void nv::k_gemm_mfma_ks<%d, %d, %s, %d>(nv::GemmArgs)", S,
+                             a.R <= 16 ? 1 : 2, a.norm_w ? "true" : "false", a.head ? 1 : 0);
                 if (a.R <= 16) {
                     if (S == 3) NV_MKS(3, 1); else if (S == 8) NV_MKS2(8, 1, false); else NV_MKS(1, 1);
                 } else {
@@ -911,20 +1057,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
     if (use_mfma(a)) {
         if (a.norm_w) {
-            hipLaunchKernelGGL(k_row_rms, dim3((a.R + 3) / 4), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.eps,
+            NV_LAUNCH(k_row_rms, dim3((a.R + 3) / 4), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.eps,
                                a.rms_ws);
         }
         const unsigned mt = (unsigned)((a.R + MF_BM - 1) / MF_BM);
+        if (t_ev_stop)
+            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_mfma<%d, %d>(nv::GemmArgs)",
+                     a.norm_w ? "nv::k_row_rms + " : "", a.R <= MF_BM ? 16 : 64, a.head ? 1 : 0);
         if (a.R <= MF_BM) {
             if (a.head)
-                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<16, 1>), dim3(a.N / 16, mt), dim3(256), 0, st, a);
+                NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma<16, 1>), dim3(a.N / 16, mt), dim3(256), 0, st, a);
             else
-                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<16, 0>), dim3(a.N / 16, mt), dim3(256), 0, st, a);
+                NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma<16, 0>), dim3(a.N / 16, mt), dim3(256), 0, st, a);
         } else {
             if (a.head)
-                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<64, 1>), dim3(a.N / 64, mt), dim3(256), 0, st, a);
+                NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma<64, 1>), dim3(a.N / 64, mt), dim3(256), 0, st, a);
             else
-                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_mfma<64, 0>), dim3(a.N / 64, mt), dim3(256), 0, st, a);
+                NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma<64, 0>), dim3(a.N / 64, mt), dim3(256), 0, st, a);
         }
         return hipGetLastError();
     }
@@ -937,7 +1086,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         if (a.R <= GV_RMAX && ch > 0 && a.K % epc == 0 && a.N % (4 * cpw) == 0 && shm <= 160 * 1024) {
             const dim3 grid(a.N / (4 * cpw));
 #define NV_GV(WB, CP, C, HD)                                                                                  \
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemv<WB, CP, C, HD>), grid, dim3(256), shm, st, a)
+    NV_LAUNCH(HIP_KERNEL_NAME(k_gemv<WB, CP, C, HD>), grid, dim3(256), shm, st, a)
 #define NV_GV_CH(WB, CP, HD)                                                                                  \
     switch (ch) {                                                                                            \
         case 1: NV_GV(WB, CP, 1, HD); break;                                                                 \
@@ -960,17 +1109,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
     const int rt = gv_row_tile(a.K);
     const size_t shm = ((size_t)rt * a.K + GV_RT_MAX) * sizeof(float);
+    if (t_ev_stop)
+        snprintf(t_name, sizeof(t_name), "void nv::k_gemm_valu<%s, %d>(nv::GemmArgs)", a.wbf16 ? "true" : "false",
+                 a.head ? 1 : 0);
     dim3 grid(a.N / GV_COLS);
     if (a.wbf16) {
         if (a.head)
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<true, 1>), grid, dim3(256), shm, st, a);
+            NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_valu<true, 1>), grid, dim3(256), shm, st, a);
         else
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<true, 0>), grid, dim3(256), shm, st, a);
+            NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_valu<true, 0>), grid, dim3(256), shm, st, a);
     } else {
         if (a.head)
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<false, 1>), grid, dim3(256), shm, st, a);
+            NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_valu<false, 1>), grid, dim3(256), shm, st, a);
         else
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_valu<false, 0>), grid, dim3(256), shm, st, a);
+            NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_valu<false, 0>), grid, dim3(256), shm, st, a);
     }
     return hipGetLastError();
 }
@@ -1077,51 +1229,51 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
     }
 }
 
-// Merge the split partials of one row (all heads): (max, sum) pairs of every (head, split)
-// are staged in LDS in parallel, turned into weights exp(max - M_head), then each thread
-// forms the weighted sums for its dims with independent loads.  Rows whose key range was
-// not split were written by the attention kernel and are skipped.
-constexpr int COMB_MAX = 4096;   // (head, split) pairs per row held in LDS
+// Merge the split partials of one (row, head): the (max, sum) pairs of its splits are
+// staged in LDS, turned into weights exp(max - M), and each thread forms the weighted sum
+// of one output dim with independent loads.  Rows whose key range was not split were
+// written by the attention kernel and are skipped.
+constexpr int COMB_MAX = 4096;   // splits of one (row, head) held in LDS
 
-__global__ __launch_bounds__(256) void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
-                                                      const float* part_o, float* out) {
+__global__ __launch_bounds__(128) void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
+                                                      const float* part_o, float* out, unsigned long long* stamp) {
+    const unsigned long long t_begin = stamp_begin(stamp);
     __shared__ float w[COMB_MAX];
     __shared__ float ls[COMB_MAX];
-    __shared__ float lsum[64];
-    const int i = blockIdx.x;
-    if (i >= R) return;
+    __shared__ float lsum;
+    const int i = blockIdx.x / D.H, h = blockIdx.x - i * D.H;
     const CombineInfo c = ci[i];
-    if (c.nsplit == 1) return;
-    const int ns = c.nsplit, H = D.H, hd = D.hd;
-    for (int idx = threadIdx.x; idx < H * ns; idx += blockDim.x) {
-        const int64_t slot = c.base + (int64_t)idx * c.nrows + c.off;   // idx = h * ns + s
-        const float2 ml = *(const float2*)(part_ml + 2 * slot);
-        w[idx] = ml.x;
-        ls[idx] = ml.y;
+    if (c.nsplit == 1) {
+        stamp_end(stamp, t_begin);
+        return;
+    }
+    const int ns = c.nsplit, hd = D.hd;
+    const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // slot of split 0; split s adds s * nrows
+    for (int sp = threadIdx.x; sp < ns; sp += blockDim.x) {
+        const float2 ml = *(const float2*)(part_ml + 2 * (base + (int64_t)sp * c.nrows));
+        w[sp] = ml.x;
+        ls[sp] = ml.y;
     }
     __syncthreads();
-    if (threadIdx.x < H) {
-        const int h = threadIdx.x;
+    if (threadIdx.x == 0) {
         float M = -INFINITY;
-        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, w[h * ns + sp]);
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, w[sp]);
         float L = 0.f;
         for (int sp = 0; sp < ns; ++sp) {
-            const float ms = w[h * ns + sp];
-            const float wt = ms == -INFINITY ? 0.f : expf(ms - M);
-            w[h * ns + sp] = wt;
-            L += wt * ls[h * ns + sp];
+            const float wt = w[sp] == -INFINITY ? 0.f : expf(w[sp] - M);
+            w[sp] = wt;
+            L += wt * ls[sp];
         }
-        lsum[h] = L;
+        lsum = L;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < H * hd; idx += blockDim.x) {
-        const int h = idx / hd, e = idx - h * hd;
+    for (int e = threadIdx.x; e < hd; e += blockDim.x) {
         float O = 0.f;
 #pragma unroll 8
-        for (int sp = 0; sp < ns; ++sp)
-            O += w[h * ns + sp] * part_o[(c.base + (int64_t)(h * ns + sp) * c.nrows + c.off) * hd + e];
-        out[(int64_t)i * D.d + idx] = O / lsum[h];
+        for (int sp = 0; sp < ns; ++sp) O += w[sp] * part_o[(base + (int64_t)sp * c.nrows) * hd + e];
+        out[(int64_t)i * D.d + h * hd + e] = O / lsum;
     }
+    stamp_end(stamp, t_begin);
 }
 
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
@@ -1129,14 +1281,14 @@ hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, 
     if (n_items <= 0) return hipSuccess;
     const int tile = at_tile(D.hd);
     const size_t shm = ((size_t)tile * (D.hd + 1) + (size_t)tile * D.hd + (size_t)AT_MAX_ROWS * D.hd) * sizeof(float);
-    hipLaunchKernelGGL(k_attn, dim3(n_items), dim3(256), shm, st, items, rows, q, kv, layer, D, part_ml, part_o, out);
+    NV_LAUNCH(k_attn, dim3(n_items), dim3(256), shm, st, items, rows, q, kv, layer, D, part_ml, part_o, out);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,
                                const float* part_o, float* out, hipStream_t st) {
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_attn_combine, dim3(R), dim3(256), 0, st, ci, R, D, part_ml, part_o, out);
+    NV_LAUNCH(k_attn_combine, dim3(R * D.H), dim3(128), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
     return hipGetLastError();
 }
 
@@ -1165,7 +1317,8 @@ __device__ __forceinline__ void sm_merge(float& m, float& l, float* o, float m2,
 template <int HD, bool KVBF, int RM>
 __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const RowInfo* rows, const float* q,
                                                   const void* kv, int layer, LayerDims D, float* part_ml,
-                                                  float* part_o, float* out) {
+                                                  float* part_o, float* out, unsigned long long* stamp) {
+    const unsigned long long t_begin = stamp_begin(stamp);
     constexpr int DPL = 8;
     constexpr int LPK = HD / DPL;       // lanes per key
     constexpr int KPI = 64 / LPK;       // keys per wave instruction
@@ -1319,6 +1472,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
             }
         }
     }
+    stamp_end(stamp, t_begin);
 }
 
 
@@ -1327,8 +1481,8 @@ hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, con
                            hipStream_t st) {
     if (n_items <= 0) return hipSuccess;
 #define NV_DEC(HDV, BF, RMV)                                                                                  \
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_attn_dec<HDV, BF, RMV>), dim3(n_items), dim3(256), 0, st, items, rows, q, \
-                       kv, layer, D, part_ml, part_o, out)
+    NV_LAUNCH(HIP_KERNEL_NAME(k_attn_dec<HDV, BF, RMV>), dim3(n_items), dim3(256), 0, st, items, rows, q, \
+                       kv, layer, D, part_ml, part_o, out, t_stamp)
 #define NV_DEC_R(HDV, BF)                                                                                     \
     do {                                                                                                     \
         if (max_rows <= 1) NV_DEC(HDV, BF, 1);                                                               \
@@ -1385,7 +1539,7 @@ __global__ __launch_bounds__(256) void k_gate(const RowInfo* rows, const int* se
 hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d, const float* gw, float bias,
                        const float* uniforms, int ucol, double* w_out, int* stop_out, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gate, dim3(n), dim3(256), 0, st, rows, seqs, n, Hs, d, gw, bias, uniforms, ucol, w_out,
+    NV_LAUNCH(k_gate, dim3(n), dim3(256), 0, st, rows, seqs, n, Hs, d, gw, bias, uniforms, ucol, w_out,
                        stop_out);
     return hipGetLastError();
 }
@@ -1400,6 +1554,7 @@ hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float*
 // ------------------------------------------------------------------------------------------
 
 constexpr int SMP_THREADS = 1024;
+constexpr int SMP_PER = 32;        // ids per thread held in registers (vocab <= 32768)
 
 __global__ __launch_bounds__(SMP_THREADS) void k_sample(const float* logits, int64_t ld, const int* seqs, int n,
                                                         int V, const float* uniforms, int* tok_out) {
@@ -1409,18 +1564,34 @@ __global__ __launch_bounds__(SMP_THREADS) void k_sample(const float* logits, int
     const int seq = seqs[blockIdx.x];
     const float* z = logits + (int64_t)seq * ld;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int chunk = (V + SMP_THREADS - 1) / SMP_THREADS;
-    const int b = min(V, t * chunk), e = min(V, b + chunk);
+    const int b = t * SMP_PER;
+    float zv[SMP_PER];
+#pragma unroll
+    for (int i = 0; i < SMP_PER; i += 4) {
+        if (b + i + 3 < V) {
+            const float4 v4 = *(const float4*)(z + b + i);
+            zv[i] = v4.x; zv[i + 1] = v4.y; zv[i + 2] = v4.z; zv[i + 3] = v4.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zv[i + j] = (b + i + j < V) ? z[b + i + j] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
-    for (int i = b; i < e; ++i) mx = fmaxf(mx, z[i]);
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) mx = fmaxf(mx, zv[i]);
     mx = wave_max(mx);
     if (lane == 0) smax[wave] = mx;
     if (t == 0) found = 0x7fffffff;
     __syncthreads();
     float M = smax[0];
     for (int w = 1; w < SMP_THREADS / 64; ++w) M = fmaxf(M, smax[w]);
+    float ev[SMP_PER];
     double S = 0.0;
-    for (int i = b; i < e; ++i) S += (double)expf(z[i] - M);
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+        ev[i] = expf(zv[i] - M);          // 0 for padding (z = -inf)
+        S += (double)ev[i];
+    }
     // inclusive scan of S over the wave (fixed order), then over the waves
     double inc = S;
 #pragma unroll
@@ -1439,13 +1610,14 @@ __global__ __launch_bounds__(SMP_THREADS) void k_sample(const float* logits, int
     if (lane == 0) exc = 0.0;
     const double hi = wpre + inc, lo = wpre + exc;   // lo_t == hi_{t-1}: same operands, same order
     const double target = (double)uniforms[seq * 4 + 3] * Z;
-    if (b < e && lo <= target && target < hi) {
+    if (b < V && lo <= target && target < hi) {
         double cum = lo;
-        int tok = e - 1;
-        for (int i = b; i < e; ++i) {
-            cum += (double)expf(z[i] - M);
-            if (target < cum) {
-                tok = i;
+        int tok = min(V, b + SMP_PER) - 1;
+#pragma unroll
+        for (int i = 0; i < SMP_PER; ++i) {
+            cum += (double)ev[i];
+            if (target < cum && b + i < V) {
+                tok = b + i;
                 break;
             }
         }
@@ -1465,7 +1637,7 @@ __global__ __launch_bounds__(SMP_THREADS) void k_sample(const float* logits, int
 hipError_t launch_sample(const float* logits, int64_t ld, const int* seqs, int n, int V, const float* uniforms,
                          int* tok_out, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sample, dim3(n), dim3(SMP_THREADS), 0, st, logits, ld, seqs, n, V, uniforms, tok_out);
+    NV_LAUNCH(k_sample, dim3(n), dim3(SMP_THREADS), 0, st, logits, ld, seqs, n, V, uniforms, tok_out);
     return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ bool read_header(const char* path, nv_config* c, std::string* err) {
     bool ok = L > 0 && d > 0 && c->n_heads > 0 && c->head_dim > 0 && c->n_heads * c->head_dim == d &&
               c->ffn > 0 && c->vocab > 0 && c->n_exits == kMaxExits && (c->wdtype == 0 || c->wdtype == 1) &&
               L % kMaxExits == 0 && (c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128) &&
-              d % 8 == 0 && c->ffn % 8 == 0 && c->vocab % 8 == 0;
+              d % 8 == 0 && c->ffn % 8 == 0 && c->vocab % 8 == 0 && c->vocab <= 32768;
     for (int k = 0; ok && k < kMaxExits; ++k) ok = c->exit_layer[k] == (k + 1) * (L / kMaxExits);
     if (!ok) {
         *err = "weights header describes an unsupported shape";
@@ -225,6 +225,18 @@ struct nv_model {
     std::vector<hipEvent_t> ev;   // pairs
     std::vector<int> ev_kind;
     std::vector<double> ev_bytes;
+    std::vector<std::string> ev_name;
+    unsigned long long* d_stamps = nullptr;   // [kEventPairs][2] device wall-clock spans
+    unsigned long long* d_blkstamps = nullptr;  // [STAMP_BLOCKS][2] per-block stamps of one launch
+    std::vector<int> ev_stamped;
+    double wall_khz = 0.0;
+    struct KStat {
+        std::string name;
+        int kind;
+        double ms, bytes;
+        int64_t n;
+    };
+    std::vector<KStat> kstats;
     size_t ev_used = 0;
     double t_ms[NV_TIME_CLASSES] = {0}, t_bytes[NV_TIME_CLASSES] = {0};
     int64_t t_n[NV_TIME_CLASSES] = {0};
@@ -280,21 +292,43 @@ bool pread_all(int fd, void* dst, size_t n, size_t off) {
 
 // Accumulate the durations of recorded event pairs (the stream must be idle).
 nv_status resolve_timing(nv_model* m) {
+    std::vector<unsigned long long> st(2 * m->ev_used);
+    if (m->ev_used) {
+        NV_HIP(m, hipMemcpy(st.data(), m->d_stamps, st.size() * 8, hipMemcpyDeviceToHost));
+    }
     for (size_t i = 0; i < m->ev_used; ++i) {
         float ms = 0.f;
         NV_HIP(m, hipEventElapsedTime(&ms, m->ev[2 * i], m->ev[2 * i + 1]));
+        // stamped kernels: first block start to last block end on the device clock
+        if (m->ev_stamped[i] && st[2 * i + 1] > st[2 * i]) ms = (float)((st[2 * i + 1] - st[2 * i]) / m->wall_khz);
         const int k = m->ev_kind[i];
         m->t_ms[k] += ms;
         m->t_bytes[k] += m->ev_bytes[i];
         m->t_n[k] += 1;
+        auto it = std::find_if(m->kstats.begin(), m->kstats.end(),
+                               [&](const nv_model::KStat& ks) { return ks.name == m->ev_name[i] && ks.kind == k; });
+        if (it == m->kstats.end()) {
+            m->kstats.push_back({m->ev_name[i], k, 0.0, 0.0, 0});
+            it = m->kstats.end() - 1;
+        }
+        it->ms += ms;
+        it->bytes += m->ev_bytes[i];
+        it->n += 1;
     }
     m->ev_used = 0;
+    // reset the spans: start = max, end = 0
+    std::vector<unsigned long long> init(2 * kEventPairs);
+    for (size_t i = 0; i < kEventPairs; ++i) {
+        init[2 * i] = ~0ull;
+        init[2 * i + 1] = 0ull;
+    }
+    NV_HIP(m, hipMemcpy(m->d_stamps, init.data(), init.size() * 8, hipMemcpyHostToDevice));
     return NV_OK;
 }
 
 // Issue one launch; with timing on, bracket it with events and note its algorithmic bytes.
 template <class F>
-nv_status timed(nv_model* m, int kind, double bytes, F&& launch) {
+nv_status timed(nv_model* m, int kind, double bytes, F&& launch, const char* name = nullptr) {
     if (!m->timing) {
         NV_HIP(m, launch());
         return NV_OK;
@@ -304,12 +338,21 @@ nv_status timed(nv_model* m, int kind, double bytes, F&& launch) {
         nv_status s = resolve_timing(m);
         if (s != NV_OK) return s;
     }
+    // drain the stream first: with work queued ahead, the start stamp would include the
+    // time the dispatch waits behind it
+    NV_HIP(m, hipStreamSynchronize(m->st));
     const size_t i = m->ev_used++;
-    NV_HIP(m, hipEventRecord(m->ev[2 * i], m->st));
-    NV_HIP(m, launch());
-    NV_HIP(m, hipEventRecord(m->ev[2 * i + 1], m->st));
+    m->ev_stamped[i] = 1;   // kernels that support stamps use them; others leave (max, 0)
+    set_launch_stamp(m->d_blkstamps);
+    set_launch_events(m->ev[2 * i], m->ev[2 * i + 1]);
+    const hipError_t le = launch();
+    set_launch_events(nullptr, nullptr);
+    set_launch_stamp(nullptr);
+    NV_HIP(m, le);
+    NV_HIP(m, launch_stamp_reduce(m->d_blkstamps, STAMP_BLOCKS, m->d_stamps + 2 * i, m->st));
     m->ev_kind[i] = kind;
     m->ev_bytes[i] = bytes;
+    m->ev_name[i] = name ? name : last_launch_name();
     return NV_OK;
 }
 
@@ -345,6 +388,7 @@ struct Tables {
     bool dec;          // decode-sized group: attention combines its splits in-kernel
     int max_rows;      // most rows in one decode-attention row block
     bool any_split;    // some row's key range was split (the combine pass is needed)
+    int max_split;     // most splits of one row's key range
     double kv_bytes;   // keys and values the attention items read
 };
 
@@ -392,7 +436,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
                 t->max_rows = std::max(t->max_rows, nr);
                 const int ctx = c.pos0 + rb + nr;
                 const int ns = std::max((ctx + max_keys - 1) / max_keys, std::min(want, (ctx + 63) / 64));
-                if (ns * m->H > ATTN_COMB_MAX) return fail(m, NV_ECAPACITY, "internal: too many attention splits");
+                if (ns > ATTN_COMB_MAX) return fail(m, NV_ECAPACITY, "internal: too many attention splits");
                 const int per = (ctx + ns - 1) / ns;
                 for (int h = 0; h < m->H; ++h)
                     for (int s2 = 0; s2 < ns; ++s2) {
@@ -436,7 +480,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
                     items += (long)m->H * ns;
                 }
             if (slots <= P.part_cap && items <= P.items_cap &&
-                (long)m->H * ((c_max_ctx(chunks) + split_len - 1) / split_len) <= ATTN_COMB_MAX)
+                (c_max_ctx(chunks) + split_len - 1) / split_len <= ATTN_COMB_MAX)
                 break;
             split_len *= 2;
         }
@@ -473,7 +517,11 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
     }
     t->dec = dec;
     t->any_split = false;
-    for (int i = 0; i < n_items; ++i) t->any_split |= hitems[i].nsplit > 1;
+    t->max_split = 1;
+    for (int i = 0; i < n_items; ++i) {
+        t->any_split |= hitems[i].nsplit > 1;
+        t->max_split = std::max(t->max_split, hitems[i].nsplit);
+    }
     size_t bytes = (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max + sizeof(AttnItem) * (size_t)n_items;
     NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, bytes, hipMemcpyHostToDevice, m->st));
     m->stage_busy = true;
@@ -487,6 +535,10 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
     t->kv_bytes = kvb * 2.0 * m->hd * m->plan.kes;
     return NV_OK;
 }
+
+// A single decode row whose key range has at most 32 splits: the O projection merges the
+// attention splits as it loads its activations (one launch less per layer).
+bool fuse_merge(const nv_model* m, const Tables& t) { return t.dec && t.R == 1 && m->bf16 && t.max_split <= 32; }
 
 // Run the layers of segment s (0-based) over the rows of the uploaded tables.
 nv_status run_segment(nv_model* m, int s, const Tables& t) {
@@ -522,19 +574,20 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                 return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
                                        m->part_o, m->attn_o, m->st);
-            }));
-            if (t.any_split)
+            }, "nv::k_attn_dec"));
+            // one row: the O projection merges the splits itself (no combine pass)
+            if (t.any_split && !fuse_merge(m, t))
                 NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
                     return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-                }));
+                }, "nv::k_attn_combine"));
         } else {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
                 return launch_attn(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o, m->attn_o,
                                    m->st);
-            }));
+            }, "nv::k_attn"));
             NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
                 return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-            }));
+            }, "nv::k_attn_combine"));
         }
         // x += o W_o^T
         g.epi = EPI_RESID;
@@ -543,6 +596,12 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.a_rows = nullptr;
         g.norm_w = nullptr;
         g.W = W.wo;
+        if (fuse_merge(m, t)) {
+            g.comb = t.comb;
+            g.part_ml = m->part_ml;
+            g.part_o = m->part_o;
+            g.D = D;
+        }
         g.N = d;
         g.K = d;
         g.epi = EPI_RESID;
@@ -550,6 +609,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.ldo = d;
         g.o_rows = t.rows;
         NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+        g.comb = nullptr;
         // u = silu(RMSNorm(x) W_g^T) * (RMSNorm(x) W_u^T)
         g.A = m->Hs;
         g.lda = d;
@@ -652,6 +712,8 @@ void nv_free(nv_model* m) {
     if (m->own_arena && m->arena) (void)hipFree(m->arena);
     if (m->h_stage) (void)hipHostFree(m->h_stage);
     for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
+    if (m->d_stamps) (void)hipFree(m->d_stamps);
+    if (m->d_blkstamps) (void)hipFree(m->d_blkstamps);
     if (m->h_stepblk) (void)hipHostFree(m->h_stepblk);
     if (m->h_gatelist) (void)hipHostFree(m->h_gatelist);
     if (m->h_headlist) (void)hipHostFree(m->h_headlist);
@@ -936,7 +998,7 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
     NV_TRY(timed(m, NV_TIME_OTHER, (double)n * m->d * (m->plan.es + 4), [&] {
         return launch_embed(m->tok_in(m->d_stepblk), m->cur_rows(m->d_stepblk), n, m->embed, m->bf16, m->Hs, m->d,
                             m->st);
-    }));
+    }, "nv::k_embed"));
 
     std::vector<int> active(n), exit_of(n, kMaxExits);
     for (int i = 0; i < n; ++i) active[i] = i;
@@ -966,7 +1028,7 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
             NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
                 return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
                                    m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
-            }));
+            }, "nv::k_gate"));
             NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
             NV_HIP(m, hipStreamSynchronize(m->st));
             m->stage_busy = false;
@@ -1012,7 +1074,7 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
             NV_TRY(timed(m, NV_TIME_OTHER, (double)ns * m->V * 4, [&] {
                 return launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif,
                                      m->d_tok_out, m->st);
-            }));
+            }, "nv::k_sample"));
         }
     }
     NV_HIP(m, hipMemcpyAsync(htok_out, m->d_tok_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
@@ -1141,9 +1203,24 @@ nv_status nv_timing_enable(nv_model* m, int32_t on) {
         m->ev.resize(2 * kEventPairs);
         m->ev_kind.resize(kEventPairs);
         m->ev_bytes.resize(kEventPairs);
+        m->ev_name.resize(kEventPairs);
+        m->ev_stamped.assign(kEventPairs, 0);
+        NV_HIP(m, hipMalloc((void**)&m->d_stamps, kEventPairs * 16));
+        NV_HIP(m, hipMalloc((void**)&m->d_blkstamps, (size_t)STAMP_BLOCKS * 16));
+        std::vector<unsigned long long> blk(2 * STAMP_BLOCKS);
+        for (int b = 0; b < STAMP_BLOCKS; ++b) {
+            blk[2 * b] = ~0ull;
+            blk[2 * b + 1] = 0ull;
+        }
+        NV_HIP(m, hipMemcpy(m->d_blkstamps, blk.data(), blk.size() * 8, hipMemcpyHostToDevice));
+        int khz = 0;
+        NV_HIP(m, hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, 0));
+        m->wall_khz = khz > 0 ? (double)khz : 1e5;
         for (auto& e : m->ev) NV_HIP(m, hipEventCreate(&e));
     }
     m->ev_used = 0;
+    m->kstats.clear();
+    if (on) NV_TRY(resolve_timing(m));   // also resets the device spans
     for (int k = 0; k < NV_TIME_CLASSES; ++k) {
         m->t_ms[k] = m->t_bytes[k] = 0;
         m->t_n[k] = 0;
@@ -1161,6 +1238,22 @@ nv_status nv_timing_read(nv_model* m, double* ms, double* bytes, int64_t* launch
         bytes[k] = m->t_bytes[k];
         launches[k] = m->t_n[k];
     }
+    return NV_OK;
+}
+
+nv_status nv_timing_kernels(nv_model* m, char* out, size_t cap) {
+    if (!m || !out || cap == 0) return m ? fail(m, NV_EINVAL, "null pointer") : NV_EINVAL;
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    NV_TRY(resolve_timing(m));
+    std::string txt;
+    char line[512];
+    for (const auto& ks : m->kstats) {
+        snprintf(line, sizeof(line), "%d\t%lld\t%.6f\t%.0f\t%s\n", ks.kind, (long long)ks.n, ks.ms, ks.bytes,
+                 ks.name.c_str());
+        txt += line;
+    }
+    if (txt.size() + 1 > cap) return fail(m, NV_ECAPACITY, "timing report buffer too small");
+    std::memcpy(out, txt.c_str(), txt.size() + 1);
     return NV_OK;
 }
 

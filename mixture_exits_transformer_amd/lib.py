@@ -59,6 +59,7 @@ _SIGS = {
     "nv_debug_hidden": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _F32P]),
     "nv_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "nv_timing_read": (ctypes.c_int, [_P, _F64P, _F64P, ctypes.POINTER(ctypes.c_int64)]),
+    "nv_timing_kernels": (ctypes.c_int, [_P, ctypes.c_char_p, ctypes.c_size_t]),
 }
 TIME_CLASSES = ("block_gemm", "attention", "exit_head", "other")
 EXPORTED = tuple(_SIGS)
@@ -229,3 +230,14 @@ def nv_timing_read(h: Handle) -> dict:
     _check(h.ptr, library().nv_timing_read(h.ptr, _ptr(ms, ctypes.c_double), _ptr(by, ctypes.c_double),
                                            _ptr(n, ctypes.c_int64)))
     return {c: (float(ms[i]), float(by[i]), int(n[i])) for i, c in enumerate(TIME_CLASSES)}
+
+
+def nv_timing_kernels(h: Handle) -> list:
+    """[(class, launches, device ms, algorithmic bytes, symbol)] since nv_timing_enable."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(h.ptr, library().nv_timing_kernels(h.ptr, buf, len(buf)))
+    out = []
+    for line in buf.value.decode().splitlines():
+        k, n, ms, by, name = line.split("\t", 4)
+        out.append((TIME_CLASSES[int(k)], int(n), float(ms), float(by), name))
+    return out
