@@ -27,6 +27,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("mixture_exits_transformer_amd/csrc/nv_kernels.hip",
+                  "mixture_exits_transformer_amd/csrc/nv_internal.h")
+
+
+def kernel_source_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(kname):
+    """HBM bytes per launch of `kname` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summaries under profiles/, or None when none covers this kernel or the kernel
+    sources changed since the counters were taken."""
+    import glob
+    want = kname.replace(", false>", ">")
+    sha = kernel_source_sha1()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                k, sep, v = line.partition(": ")
+                if sep and k in ("kernel", "kernel_source_sha1", "traffic_bytes_per_launch"):
+                    kv[k] = v.strip()
+        if kv.get("kernel", "").replace(", false>", ">") == want and kv.get("kernel_source_sha1") == sha:
+            return int(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return None
 
 
 def run_decode(lib, h, prompt, U, steps, warmup):
@@ -139,6 +169,7 @@ def main():
     gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
     _, nl, ms, by, kname = gemms[0]
     achieved = by / (ms * 1e-3) / 1e9
+    counted = counted_traffic(kname)
     top = sorted(ker, key=lambda k: -k[2])[:8]
     hist = np.bincount(np.asarray(exits), minlength=5)[1:]
     out = {
@@ -158,7 +189,9 @@ def main():
                    "decode_steps": steps},
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counted[0] if counted else None,
+                     "traffic_source": counted[1] if counted else None,
                      "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
                      "bytes_per_launch": round(by / max(nl, 1))},
         "block_gemm_all": {"achieved_GBps": round(tim["block_gemm"][1] / (tim["block_gemm"][0] * 1e-3) / 1e9, 1),
