@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("mixture_exits_transformer_amd/csrc/nv_kernels.hip",
+                  "mixture_exits_transformer_amd/csrc/nv_segment.hip",
+                  "mixture_exits_transformer_amd/csrc/nv_device.h",
                   "mixture_exits_transformer_amd/csrc/nv_internal.h")
 
 

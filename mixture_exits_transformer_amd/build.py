@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvium.so")
 ARCH = os.environ.get("NVIUM_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["nv_kernels.hip", "nv_runtime.cpp"]
+SOURCES = ["nv_kernels.hip", "nv_segment.hip", "nv_runtime.cpp"]
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # keep packed-fp32 instructions out of generated code

@@ -1,0 +1,119 @@
+// Device helpers shared by the kernels of libnvium.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nv_internal.h"
+
+namespace nv {
+
+// ------------------------------------------------------------------------------------------
+// small helpers
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t b = __float_as_uint(f);
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Cross-lane adds with DPP (no LDS traffic).  quad_perm [1,0,3,2] and [2,3,0,1] pair lanes
+// within a quad; row_half_mirror / row_mirror pair lane i with 7-i / 15-i of its 8 / 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of G lanes (G = 4, 8 or 16); every lane of a group gets the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    if constexpr (G >= 8) v += dpp_f<0x141>(v);
+    if constexpr (G >= 16) v += dpp_f<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float kv_load(const void* kv, int bf16, int64_t i) {
+    if (bf16) return __uint_as_float(((uint32_t)((const uint16_t*)kv)[i]) << 16);
+    return ((const float*)kv)[i];
+}
+
+__device__ __forceinline__ void kv_store(void* kv, int bf16, int64_t i, float v) {
+    if (bf16)
+        ((uint16_t*)kv)[i] = f2bf(v);
+    else
+        ((float*)kv)[i] = v;
+}
+
+// K (which = 0) or V (which = 1) of (seq, layer, head) at position 0.
+__device__ __forceinline__ int64_t kv_base(const LayerDims& D, int seq, int layer, int which, int head) {
+    return ((((int64_t)seq * D.L + layer) * 2 + which) * D.H + head) * (int64_t)D.max_ctx * D.hd;
+}
+
+// Kernel-span stamps for timing mode: each block stores its start and end (device
+// wall clock) at stamp[2 * block], stamp[2 * block + 1]; k_stamp_reduce folds them.
+__device__ __forceinline__ unsigned long long stamp_begin(const unsigned long long* stamp) {
+    return stamp ? (unsigned long long)wall_clock64() : 0ull;
+}
+
+__device__ __forceinline__ void stamp_end(unsigned long long* stamp, unsigned long long t0) {
+    if (stamp) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            stamp[2 * blockIdx.x] = t0;
+            stamp[2 * blockIdx.x + 1] = (unsigned long long)wall_clock64();
+        }
+    }
+}
+
+// Sum N values per lane over the 64 lanes of a wave.  Transposed reduction: each step
+// halves the values a lane keeps (exchanging the other half with the partner lane), so
+// after log2(N) steps lane L holds one value and a final butterfly finishes the sum.
+// Returns the sum of value index (L >> (6 - log2 N)) in lane L (all lanes of a group).
+template <int N>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[N], int lane) {
+    static_assert((N & (N - 1)) == 0 && N <= 64, "N must be a power of two <= 64");
+    constexpr int LOG = (N == 1) ? 0 : (N == 2) ? 1 : (N == 4) ? 2 : (N == 8) ? 3 : (N == 16) ? 4 : (N == 32) ? 5 : 6;
+    int n = N;
+#pragma unroll
+    for (int st = 0; st < LOG; ++st) {
+        const int m = 32 >> st;
+        const bool upper = (lane & m) != 0;
+        n >>= 1;
+        const int um = upper ? -1 : 0;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            if (i < n) {
+                // select by masks on the values (a conditional operator here becomes an
+                // indexed access over the whole array)
+                const int lo = __float_as_int(v[i]), hi = __float_as_int(v[i + n]);
+                const float send = __int_as_float((lo & um) | (hi & ~um));
+                const float keep = __int_as_float((hi & um) | (lo & ~um));
+                v[i] = keep + __shfl_xor(send, m, 64);
+            }
+        }
+    }
+    float r = v[0];
+#pragma unroll
+    for (int m = 32 >> LOG; m > 0; m >>= 1) r += __shfl_xor(r, m, 64);
+    return r;
+}
+
+}  // namespace nv

@@ -107,6 +107,67 @@ const char* last_launch_name();   // symbol of the last kernel issued while timi
 // Timing: block-stamp buffer the next stamped kernels write (nullptr: none).
 void set_launch_stamp(unsigned long long* stamps);
 constexpr int STAMP_BLOCKS = 8192;  // largest grid the timing stamps cover
+unsigned long long* current_launch_stamp();
+void current_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// ------------------------------------------------------------------------------------------
+// Persistent segment kernel (nv_segment.hip): every layer of one segment for a single
+// decode row in one cooperative launch.  Blocks exchange activations through buffers of
+// tagged values (high 32 bits: epoch of the write, low 32 bits: the fp32 value) that
+// consumers poll; see nv_segment.hip for the roles of the waves.
+// ------------------------------------------------------------------------------------------
+constexpr int SEG_THREADS = 512;    // 6 streaming waves + 2 control waves
+constexpr int SEG_NS = 6;           // streaming waves per block
+constexpr int SEG_DMAX = 1536;      // largest model width
+constexpr int SEG_FMAX = 4096;      // largest MLP width
+constexpr int SEG_HD = 128;         // head dimension
+constexpr int SEG_SMAX = 32;        // most key splits per head
+constexpr int SEG_QCOLS = 18;       // most QKV columns per block (3 per streaming wave)
+constexpr int SEG_OCOLS = 6;        // most O / down columns per block (1 per streaming wave)
+constexpr int SEG_GCOLS = 36;       // most gate/up columns per block (6 per streaming wave)
+constexpr int SEG_PHASES = 8;       // epoch stride per layer
+constexpr int SEG_LMAX = 16;        // most layers per segment
+
+struct SegLayerW {
+    const float* attn_norm;
+    const uint16_t* wqkv;   // [3d][d], RoPE partners in adjacent rows (see GemmArgs)
+    const uint16_t* wo;     // [d][d]
+    const float* mlp_norm;
+    const uint16_t* wgu;    // [2F][d], rows 2j / 2j+1 = gate j / up j
+    const uint16_t* wd;     // [d][F]
+};
+
+struct SegArgs {
+    SegLayerW lw[SEG_LMAX]; // weights of layers l0 .. l0 + nl - 1 (kernel arguments are read
+                            // through the scalar cache, away from the vector loads in flight)
+    int l0, nl;
+    LayerDims D;
+    float eps;
+    float* Hs;              // hidden-state rows; row `hrow` is read at l0 and written after the last layer
+    int64_t hrow;
+    int seq, pos;           // the row: position `pos` of sequence `seq`
+    void* kv;               // bf16 KV cache
+    const float* rope;      // [max_ctx][hd/2] (cos, sin)
+    uint64_t* tx0;          // [d]  layer input (written by the down projection)
+    uint64_t* tq;           // [d]  rotated query
+    uint64_t* tk;           // [d]  rotated key of `pos`, bf16-rounded
+    uint64_t* tv;           // [d]  value of `pos`, bf16-rounded
+    uint64_t* tpart;        // [H][SEG_SMAX][2 + hd] split partials (max, sum, output)
+    uint64_t* tatt;         // [d]  attention output
+    uint64_t* tx1;          // [d]  after the attention residual
+    uint64_t* tact;         // [F]  SwiGLU output
+    uint32_t* cnt;          // [H]  splits finished per head (monotonic)
+    uint32_t cnt_base;      // value of every cnt[h] when this launch starts
+    uint32_t* err;          // set to 1 when a wait gave up
+    uint32_t epoch;         // tags of this launch: epoch + SEG_PHASES * (l - l0) + phase
+    int S;                  // key splits per head
+    unsigned long long spin_ticks;   // a wait gives up after this many wall-clock ticks
+    unsigned long long* stamp;       // timing stamps (or null)
+};
+
+// Grid size for the model's shape (0: the shape does not fit the kernel).
+int segment_blocks(const LayerDims& D, int n_cu);
+hipError_t launch_segment(const SegArgs& a, int blocks, hipStream_t st);
 hipError_t launch_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec, hipStream_t st);
 
 }  // namespace nv

@@ -73,6 +73,7 @@ struct Plan {
     int R_max = 0, part_cap = 0, items_cap = 0;
     size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0;
     size_t tables = 0, small = 0, logits = 0;
+    size_t seg = 0;     // persistent segment kernel: tagged exchange buffers, counters, layer table
     size_t total = 0;
 };
 
@@ -154,8 +155,10 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
               2 * align_up((size_t)max_batch * (4 + 2 * sizeof(RowInfo))) + align_up((size_t)max_batch * 32) +
               2 * align_up((size_t)max_batch * 4);
     p.logits = align_up((size_t)max_batch * V * 4);
+    p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
+            align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up((size_t)c.n_heads * 4 + 4);
     p.total = p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
-              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + kAlign;
+              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
     return p;
 }
 
@@ -198,6 +201,17 @@ struct nv_model {
     int* d_stop = nullptr;
     int* d_tok_out = nullptr;
     float* logits = nullptr;
+
+    // persistent segment kernel (single decode rows); seg_nb == 0: not used
+    int seg_nb = 0;
+    uint64_t *seg_x0 = nullptr, *seg_q = nullptr, *seg_k = nullptr, *seg_v = nullptr, *seg_part = nullptr,
+             *seg_att = nullptr, *seg_x1 = nullptr, *seg_act = nullptr;
+    uint32_t* seg_cnt = nullptr;   // [H] then the error word
+    uint32_t seg_epoch = 8;        // next launch's first tag
+    uint32_t seg_cnt_host = 0;     // value of every seg_cnt[h] between launches
+    bool seg_ran = false;          // launched since the error word was last checked
+    unsigned long long seg_spin = 0;
+    char* seg_base = nullptr;
 
     char* h_stage = nullptr;   // pinned; mirrors the device table region
     size_t h_stage_bytes = 0;
@@ -640,6 +654,129 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
     return NV_OK;
 }
 
+// ------------------------------------------------------------------------------------------
+// Persistent segment kernel: one launch per segment for a single decode row.
+// ------------------------------------------------------------------------------------------
+
+// Zero the tagged exchange buffers and counters and restart the tags (the stream orders it
+// before the next launch).
+nv_status seg_reset(nv_model* m) {
+    const size_t tagged = (size_t)((char*)m->seg_cnt - m->seg_base) + align_up((size_t)m->H * 4 + 4);
+    NV_HIP(m, hipMemsetAsync(m->seg_base, 0, tagged, m->st));
+    m->seg_epoch = 8;
+    m->seg_cnt_host = 0;
+    return NV_OK;
+}
+
+nv_status seg_setup(nv_model* m) {
+    m->seg_nb = 0;
+    if (!m->bf16) return NV_OK;
+    // opt-in for now (NVIUM_SEGMENT=1): on the 1.5B shape it is not yet faster than the
+    // per-phase kernels
+    const char* e = std::getenv("NVIUM_SEGMENT");
+    if (!e || std::string(e) != "1") return NV_OK;
+    int dev = 0, ncu = 0, coop = 0, khz = 0;
+    NV_HIP(m, hipGetDevice(&dev));
+    NV_HIP(m, hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    NV_HIP(m, hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+    NV_HIP(m, hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+    const int nb = coop ? segment_blocks(m->dims(), ncu) : 0;
+    if (nb <= 0) return NV_OK;
+    char* p = m->seg_base;
+    auto carve = [&](size_t n) {
+        char* r = p;
+        p += align_up(n);
+        return r;
+    };
+    const size_t d = m->d;
+    m->seg_x0 = (uint64_t*)carve(d * 8);
+    m->seg_q = (uint64_t*)carve(d * 8);
+    m->seg_k = (uint64_t*)carve(d * 8);
+    m->seg_v = (uint64_t*)carve(d * 8);
+    m->seg_att = (uint64_t*)carve(d * 8);
+    m->seg_x1 = (uint64_t*)carve(d * 8);
+    m->seg_act = (uint64_t*)carve((size_t)m->F * 8);
+    m->seg_part = (uint64_t*)carve((size_t)m->H * SEG_SMAX * (2 + m->hd) * 8);
+    m->seg_cnt = (uint32_t*)carve((size_t)m->H * 4 + 4);
+    if ((size_t)(p - m->seg_base) > m->plan.seg) return fail(m, NV_ECAPACITY, "internal: segment buffers exceed the plan");
+    if (m->seg > SEG_LMAX) return NV_OK;
+    NV_TRY(seg_reset(m));
+    // a wait gives up after half a second of device time
+    m->seg_spin = (unsigned long long)(khz > 0 ? khz : 100000) * 500ull;
+    m->seg_nb = nb;
+    return NV_OK;
+}
+
+// After the stream is idle: a wait that gave up inside the segment kernel leaves the
+// handle unusable.
+nv_status seg_check(nv_model* m, const uint32_t* h_err) {
+    if (m->seg_ran && *h_err) {
+        m->dead = true;
+        return fail(m, NV_EDEVICE, "segment kernel: a cross-block wait gave up (blocks not co-resident?)");
+    }
+    m->seg_ran = false;
+    return NV_OK;
+}
+
+// Wait for the stream; then report a wait that gave up in a segment launch since the
+// last check.
+nv_status sync_and_check(nv_model* m) {
+    uint32_t* h_err = (uint32_t*)(m->h_out + (size_t)m->max_batch * 48);
+    if (m->seg_ran) NV_HIP(m, hipMemcpyAsync(h_err, m->seg_cnt + m->H, 4, hipMemcpyDeviceToHost, m->st));
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    m->stage_busy = false;
+    return seg_check(m, h_err);
+}
+
+// Key splits per head for a context of ctx keys: about 64 keys per split, as many as
+// the grid holds.
+int seg_splits(const nv_model* m, int ctx) {
+    const int cap = std::min(SEG_SMAX, m->seg_nb / m->H);
+    return std::max(1, std::min(cap, (ctx + 63) / 64));
+}
+
+nv_status run_segment_persistent(nv_model* m, int s, const Chunk& c) {
+    if (m->seg_epoch > 0xF0000000u || m->seg_cnt_host > 0xF0000000u) NV_TRY(seg_reset(m));
+    SegArgs a{};
+    for (int i = 0; i < m->seg; ++i) {
+        const LayerPtrs& W = m->layers[s * m->seg + i];
+        a.lw[i] = SegLayerW{W.attn_norm, (const uint16_t*)W.wqkv, (const uint16_t*)W.wo, W.mlp_norm,
+                            (const uint16_t*)W.wgu, (const uint16_t*)W.wd};
+    }
+    a.l0 = s * m->seg;
+    a.nl = m->seg;
+    a.D = m->dims();
+    a.eps = m->cfg.norm_eps;
+    a.Hs = m->Hs;
+    a.hrow = (int64_t)c.seq * m->max_ctx + c.pos0;
+    a.seq = c.seq;
+    a.pos = c.pos0;
+    a.kv = m->kv;
+    a.rope = m->rope;
+    a.tx0 = m->seg_x0;
+    a.tq = m->seg_q;
+    a.tk = m->seg_k;
+    a.tv = m->seg_v;
+    a.tpart = m->seg_part;
+    a.tatt = m->seg_att;
+    a.tx1 = m->seg_x1;
+    a.tact = m->seg_act;
+    a.cnt = m->seg_cnt;
+    a.cnt_base = m->seg_cnt_host;
+    a.err = m->seg_cnt + m->H;
+    a.epoch = m->seg_epoch;
+    a.S = seg_splits(m, c.pos0 + 1);
+    a.spin_ticks = m->seg_spin;
+    const double d = m->d, F = m->F, es = m->plan.es;
+    const double layer_bytes = (4 * d * d + 3 * d * F) * es + 2 * d * 4;
+    const double bytes = a.nl * (layer_bytes + (double)c.pos0 * 2 * d * es + 2 * d * es) + 2 * d * 4;
+    NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, bytes, [&] { return launch_segment(a, m->seg_nb, m->st); }, "nv::k_segment"));
+    m->seg_epoch += (uint32_t)(SEG_PHASES * (a.nl + 1));
+    m->seg_cnt_host += (uint32_t)(a.nl * a.S);
+    m->seg_ran = true;
+    return NV_OK;
+}
+
 // Run segment s over a list of chunks, splitting into launch groups that fit the
 // workspace.  Pieces of one sequence go in ascending position order and in separate
 // groups, so each piece sees the KV of the pieces before it.
@@ -665,6 +802,11 @@ nv_status run_chunks(nv_model* m, int s, const std::vector<Chunk>& chunks) {
             rows += p.nrows;
             done[i] = true;
             --left;
+        }
+        if (m->seg_nb > 0 && group.size() == 1 && group[0].nrows == 1) {
+            nv_status st = run_segment_persistent(m, s, group[0]);
+            if (st != NV_OK) return st;
+            continue;
         }
         Tables t;
         nv_status st = upload_tables(m, group, &t);
@@ -823,6 +965,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->d_stop = (int*)m->take((size_t)max_batch * 4);
     m->d_tok_out = (int*)m->take((size_t)max_batch * 4);
     m->logits = (float*)m->take(P.logits);
+    m->seg_base = m->take(P.seg);
     if (m->arena_off > P.total) return fail(m, NV_ECAPACITY, "internal: arena plan too small");
 
     m->h_stage_bytes = P.tables;
@@ -830,7 +973,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     NV_HIP(m, hipHostMalloc((void**)&m->h_stepblk, m->stepblk_bytes(), hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_gatelist, m->list_bytes(), hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_headlist, m->list_bytes(), hipHostMallocDefault));
-    NV_HIP(m, hipHostMalloc((void**)&m->h_out, (size_t)max_batch * 48, hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_out, (size_t)max_batch * 48 + 16, hipHostMallocDefault));
 
     // weights: file tensors -> pinned bounce buffer -> device (repacking W_gate/W_up rows)
     int fd = ::open(path, O_RDONLY);
@@ -919,6 +1062,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     if (!io_ok) return fail(m, NV_EIO, "weights file read failed");
     NV_HIP(m, herr);
     NV_HIP(m, launch_rope_table(m->rope, max_ctx, m->hd, c.rope_base, m->st));
+    NV_TRY(seg_setup(m));
 
     NV_HIP(m, hipStreamSynchronize(m->st));
     m->seqs.assign(max_batch, SeqHost());
@@ -959,8 +1103,7 @@ nv_status nv_prefill(nv_model* m, int32_t seq, const int32_t* tokens, int32_t n)
         for (int sg = 0; sg < kMaxExits; ++sg)
             if ((s = run_chunks(m, sg, ch)) != NV_OK) return s;
     }
-    NV_HIP(m, hipStreamSynchronize(m->st));
-    m->stage_busy = false;
+    NV_TRY(sync_and_check(m));
     S.n = np;
     for (int k = 0; k < kMaxExits; ++k) S.f[k] = np;
     for (int k = 0; k < 4; ++k) m->last_w[(size_t)seq * 4 + k] = NAN;
@@ -1079,8 +1222,7 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
     }
     NV_HIP(m, hipMemcpyAsync(htok_out, m->d_tok_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipMemcpyAsync(hw, m->d_w, (size_t)n * 32, hipMemcpyDeviceToHost, m->st));
-    NV_HIP(m, hipStreamSynchronize(m->st));
-    m->stage_busy = false;
+    NV_TRY(sync_and_check(m));
     if (m->timing) NV_TRY(resolve_timing(m));
     for (int i = 0; i < n; ++i) {
         SeqHost& S = m->seqs[i];
@@ -1124,9 +1266,7 @@ nv_status nv_flush(nv_model* m, int32_t seq) {
         if (!ch.empty() && (s = run_chunks(m, sg, ch)) != NV_OK) return s;
         for (int i : targets) m->seqs[i].f[sg] = m->seqs[i].n;
     }
-    NV_HIP(m, hipStreamSynchronize(m->st));
-    m->stage_busy = false;
-    return NV_OK;
+    return sync_and_check(m);
 }
 
 nv_status nv_debug_frontiers(nv_model* m, int32_t seq, int32_t* n_consumed, int32_t frontier[4]) {
