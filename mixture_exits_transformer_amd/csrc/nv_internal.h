@@ -152,12 +152,11 @@ struct SegArgs {
     uint64_t* tq;           // [d]  rotated query
     uint64_t* tk;           // [d]  rotated key of `pos`, bf16-rounded
     uint64_t* tv;           // [d]  value of `pos`, bf16-rounded
-    uint64_t* tpart;        // [H][SEG_SMAX][2 + hd] split partials (max, sum, output)
+    uint64_t* tpart;        // [H][SEG_SMAX][2 + hd] split partials (max, sum, output); split 0
+                            // of each head merges them
     uint64_t* tatt;         // [d]  attention output
     uint64_t* tx1;          // [d]  after the attention residual
     uint64_t* tact;         // [F]  SwiGLU output
-    uint32_t* cnt;          // [H]  splits finished per head (monotonic)
-    uint32_t cnt_base;      // value of every cnt[h] when this launch starts
     uint32_t* err;          // set to 1 when a wait gave up
     uint32_t epoch;         // tags of this launch: epoch + SEG_PHASES * (l - l0) + phase
     int S;                  // key splits per head

@@ -156,7 +156,7 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
               2 * align_up((size_t)max_batch * 4);
     p.logits = align_up((size_t)max_batch * V * 4);
     p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
-            align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up((size_t)c.n_heads * 4 + 4);
+            align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.total = p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
               p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
     return p;
@@ -206,9 +206,8 @@ struct nv_model {
     int seg_nb = 0;
     uint64_t *seg_x0 = nullptr, *seg_q = nullptr, *seg_k = nullptr, *seg_v = nullptr, *seg_part = nullptr,
              *seg_att = nullptr, *seg_x1 = nullptr, *seg_act = nullptr;
-    uint32_t* seg_cnt = nullptr;   // [H] then the error word
+    uint32_t* seg_err = nullptr;   // set by the kernel when a wait gave up
     uint32_t seg_epoch = 8;        // next launch's first tag
-    uint32_t seg_cnt_host = 0;     // value of every seg_cnt[h] between launches
     bool seg_ran = false;          // launched since the error word was last checked
     unsigned long long seg_spin = 0;
     char* seg_base = nullptr;
@@ -661,10 +660,9 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
 // Zero the tagged exchange buffers and counters and restart the tags (the stream orders it
 // before the next launch).
 nv_status seg_reset(nv_model* m) {
-    const size_t tagged = (size_t)((char*)m->seg_cnt - m->seg_base) + align_up((size_t)m->H * 4 + 4);
+    const size_t tagged = (size_t)((char*)m->seg_err - m->seg_base) + align_up(4);
     NV_HIP(m, hipMemsetAsync(m->seg_base, 0, tagged, m->st));
     m->seg_epoch = 8;
-    m->seg_cnt_host = 0;
     return NV_OK;
 }
 
@@ -697,7 +695,7 @@ nv_status seg_setup(nv_model* m) {
     m->seg_x1 = (uint64_t*)carve(d * 8);
     m->seg_act = (uint64_t*)carve((size_t)m->F * 8);
     m->seg_part = (uint64_t*)carve((size_t)m->H * SEG_SMAX * (2 + m->hd) * 8);
-    m->seg_cnt = (uint32_t*)carve((size_t)m->H * 4 + 4);
+    m->seg_err = (uint32_t*)carve(4);
     if ((size_t)(p - m->seg_base) > m->plan.seg) return fail(m, NV_ECAPACITY, "internal: segment buffers exceed the plan");
     if (m->seg > SEG_LMAX) return NV_OK;
     NV_TRY(seg_reset(m));
@@ -722,7 +720,7 @@ nv_status seg_check(nv_model* m, const uint32_t* h_err) {
 // last check.
 nv_status sync_and_check(nv_model* m) {
     uint32_t* h_err = (uint32_t*)(m->h_out + (size_t)m->max_batch * 48);
-    if (m->seg_ran) NV_HIP(m, hipMemcpyAsync(h_err, m->seg_cnt + m->H, 4, hipMemcpyDeviceToHost, m->st));
+    if (m->seg_ran) NV_HIP(m, hipMemcpyAsync(h_err, m->seg_err, 4, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipStreamSynchronize(m->st));
     m->stage_busy = false;
     return seg_check(m, h_err);
@@ -736,7 +734,7 @@ int seg_splits(const nv_model* m, int ctx) {
 }
 
 nv_status run_segment_persistent(nv_model* m, int s, const Chunk& c) {
-    if (m->seg_epoch > 0xF0000000u || m->seg_cnt_host > 0xF0000000u) NV_TRY(seg_reset(m));
+    if (m->seg_epoch > 0xF0000000u) NV_TRY(seg_reset(m));
     SegArgs a{};
     for (int i = 0; i < m->seg; ++i) {
         const LayerPtrs& W = m->layers[s * m->seg + i];
@@ -761,9 +759,7 @@ nv_status run_segment_persistent(nv_model* m, int s, const Chunk& c) {
     a.tatt = m->seg_att;
     a.tx1 = m->seg_x1;
     a.tact = m->seg_act;
-    a.cnt = m->seg_cnt;
-    a.cnt_base = m->seg_cnt_host;
-    a.err = m->seg_cnt + m->H;
+    a.err = m->seg_err;
     a.epoch = m->seg_epoch;
     a.S = seg_splits(m, c.pos0 + 1);
     a.spin_ticks = m->seg_spin;
@@ -772,7 +768,6 @@ nv_status run_segment_persistent(nv_model* m, int s, const Chunk& c) {
     const double bytes = a.nl * (layer_bytes + (double)c.pos0 * 2 * d * es + 2 * d * es) + 2 * d * 4;
     NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, bytes, [&] { return launch_segment(a, m->seg_nb, m->st); }, "nv::k_segment"));
     m->seg_epoch += (uint32_t)(SEG_PHASES * (a.nl + 1));
-    m->seg_cnt_host += (uint32_t)(a.nl * a.S);
     m->seg_ran = true;
     return NV_OK;
 }

@@ -48,34 +48,30 @@ constexpr int MG = SEG_GCOLS / SEG_NS;    // gate/up columns per streaming wave
 constexpr int NR = 4;                     // key rounds (4 keys each) a wave prefetches
 constexpr int NJ_D = SEG_DMAX / 128;      // tagged words per control lane, width d
 constexpr int NJ_F = SEG_FMAX / 128;      // ... width F
+constexpr int NJ_S = 4;                   // sampled words per control lane (<= 512 producers)
 
+// The staged input row of a phase lives in two planes so that a lane's 16-byte chunk
+// ch (8 values) is read as two conflict-free 16-byte LDS reads: values 8ch..8ch+3 at
+// xlo[4ch], values 8ch+4..8ch+7 at xhi[4ch].
 struct SegShared {
-    float xs[SEG_FMAX];         // staged input vector of the phase
-    float gs[SEG_DMAX];         // RMSNorm weight of the phase
+    float xlo[SEG_FMAX / 2], xhi[SEG_FMAX / 2];
     float dots[64];             // dot products of the block's columns
+    float ss[2];                // sums of squares of the staged row, one per control wave
     float qs[SEG_HD], kn[SEG_HD], vn[SEG_HD];
-    float wm[SEG_NS], wl[SEG_NS];
-    float wo[SEG_NS][SEG_HD];   // per-wave partial attention states
+    float wm[SEG_NS * 4], wl[SEG_NS * 4];   // softmax state per (wave, lane group)
+    float wo[SEG_NS * 4][SEG_HD];
     float xres[SEG_OCOLS];      // layer input on the block's O / down columns
     float x1own[SEG_OCOLS];     // after the attention residual, same columns
-    int last;                   // this block finished its head's splits last
     int bad;                    // a wait in this block gave up
 };
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint64_t tagv(uint32_t ep, float v) { return ((uint64_t)ep << 32) | __float_as_uint(v); }
 
 __device__ __forceinline__ void tstore(uint64_t* p, uint32_t ep, float v) {
     __hip_atomic_store(p, tagv(ep, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ uint64_t tload(const uint64_t* p) {
-    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Coherent loads through a buffer resource: one VGPR offset per lane and the per-load
-// displacement in an SGPR, so a wave can keep many loads in flight without a 64-bit
-// address per load.  Cache policy sc1 (agent scope), the same as the atomic loads above.
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
@@ -86,6 +82,7 @@ __device__ __forceinline__ uint64_t tload_b(__amdgpu_buffer_rsrc_t r, int voff, 
     return ((uint64_t)v.y << 32) | v.x;
 }
 
+
 // Block barrier that orders LDS only: global loads in flight stay in flight.
 __device__ __forceinline__ void seg_bar() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -93,46 +90,137 @@ __device__ __forceinline__ void seg_bar() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Sum over the 64 lanes (DPP within rows of 16, then the 4 row sums read as scalars).
+__device__ __forceinline__ float wave_total(float v) {
+    v = group_sum<16>(v);
+    const int iv = __float_as_int(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) + __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) + __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
+}
+
 __device__ __forceinline__ void give_up(SegShared& sh, uint32_t* err) {
     sh.bad = 1;
     __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Control waves: stage the n tagged words src[0..n) into dst once every tag equals ep.
-// Control wave wc (0 or 1) takes words (2j + wc) * 64 + lane.
+__device__ __forceinline__ bool timed_out(unsigned long long t_end) {
+    return (unsigned long long)wall_clock64() > t_end;
+}
+
+// Control waves: put value v of row index i into the LDS planes.
+__device__ __forceinline__ void plane_put(SegShared& sh, int i, float v) {
+    const int ch = i >> 3, e = i & 7;
+    (e < 4 ? sh.xlo : sh.xhi)[ch * 4 + (e & 3)] = v;
+}
+
+// Control waves: stage the n tagged words src[0..n) into the LDS planes once every tag
+// equals ep, multiplied by g[i] when g is set; sh.ss[wc] gets this wave's sum of squares
+// of the raw values.  Control wave wc takes words (2j + wc) * 64 + lane.  With
+// stride > 0 the wave first polls only every stride-th word (one per producer block),
+// which keeps 256 blocks from hammering the same few kilobytes.
 template <int NJ>
-__device__ void stage_tagged(const uint64_t* src, int n, uint32_t ep, float* dst, int wc, int lane,
+__device__ void stage_tagged(const uint64_t* src, int n, uint32_t ep, int stride, const float* g, int wc, int lane,
                              unsigned long long spin, SegShared& sh, uint32_t* err) {
     if (sh.bad) return;
     const unsigned long long t_end = (unsigned long long)wall_clock64() + spin;
     const __amdgpu_buffer_rsrc_t r = coh_rsrc(src);
-    const int voff = (wc * 64 + lane) * 8;
-    uint64_t v[NJ];
-    for (;;) {
-        bool ok = true;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int i = (2 * j + wc) * 64 + lane;
-            v[j] = i < n ? tload_b(r, voff, j * 1024) : tagv(ep, 0.f);
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) ok = ok && (uint32_t)(v[j] >> 32) == ep;
-        if (__all(ok)) break;
-        if ((unsigned long long)wall_clock64() > t_end) {
-            give_up(sh, err);
-            return;
-        }
-    }
+    float gv[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int i = (2 * j + wc) * 64 + lane;
-        if (i < n) dst[i] = __uint_as_float((uint32_t)v[j]);
+        gv[j] = (g && i < n) ? g[i] : 1.0f;
     }
+    if (stride > 0) {
+        const int ns = n / stride;
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < NJ_S; ++j) {
+                const int k = (2 * j + wc) * 64 + lane;
+                const uint64_t v = k < ns ? tload_b(r, k * stride * 8, 0) : tagv(ep, 0.f);
+                ok = ok && (uint32_t)(v >> 32) == ep;
+            }
+            if (__all(ok)) break;
+            if (timed_out(t_end)) {
+                give_up(sh, err);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    // bulk load, then reloads of the words whose tag is not yet this phase's
+    const int voff = (wc * 64 + lane) * 8;
+    uint64_t v[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int i = (2 * j + wc) * 64 + lane;
+        v[j] = i < n ? tload_b(r, voff, j * 1024) : tagv(ep, 0.f);
+    }
+    for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) ok = ok && (uint32_t)(v[j] >> 32) == ep;
+        if (__all(ok)) break;
+        if (timed_out(t_end)) {
+            give_up(sh, err);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int i = (2 * j + wc) * 64 + lane;
+            if (i < n && (uint32_t)(v[j] >> 32) != ep) v[j] = tload_b(r, voff, j * 1024);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int i = (2 * j + wc) * 64 + lane;
+        if (i < n) {
+            const float x = __uint_as_float((uint32_t)v[j]);
+            ss = fmaf(x, x, ss);
+            plane_put(sh, i, x * gv[j]);
+        }
+    }
+    ss = wave_total(ss);
+    if (lane == 0) sh.ss[wc] = ss;
 }
 
-// Control waves: plain loads of n floats (written before this launch) into dst.
-__device__ void stage_plain(const float* src, int n, float* dst, int wc, int lane) {
-    for (int i = (wc * 64 + lane) * 4; i < n; i += 512) *(float4*)(dst + i) = *(const float4*)(src + i);
+// Control waves: stage one head's SEG_HD tagged words into dst (lane: word wc*64 + lane).
+__device__ void stage_head(const uint64_t* src, uint32_t ep, float* dst, int wc, int lane, unsigned long long spin,
+                           SegShared& sh, uint32_t* err) {
+    if (sh.bad) return;
+    const unsigned long long t_end = (unsigned long long)wall_clock64() + spin;
+    const __amdgpu_buffer_rsrc_t r = coh_rsrc(src);
+    const int i = wc * 64 + lane;
+    uint64_t v;
+    for (;;) {
+        v = tload_b(r, i * 8, 0);
+        if (__all((uint32_t)(v >> 32) == ep)) break;
+        if (timed_out(t_end)) {
+            give_up(sh, err);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    dst[i] = __uint_as_float((uint32_t)v);
+}
+
+// Control waves: the same as stage_tagged from plain fp32 memory written before this launch.
+template <int NJ>
+__device__ void stage_plain(const float* src, int n, const float* g, int wc, int lane, SegShared& sh) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int i = (2 * j + wc) * 64 + lane;
+        if (i < n) {
+            const float x = src[i];
+            ss = fmaf(x, x, ss);
+            plane_put(sh, i, g ? x * g[i] : x);
+        }
+    }
+    ss = wave_total(ss);
+    if (lane == 0) sh.ss[wc] = ss;
 }
 
 // Streaming waves: issue this wave's weight chunks of the block's columns
@@ -158,40 +246,22 @@ __device__ __forceinline__ void w_issue(uint4 (&w)[MC][KC], const uint16_t* W, i
     }
 }
 
-// 1 / rms of the staged row xs[0..K) (every streaming wave computes it for itself).
-__device__ __forceinline__ float row_inv_rms(const SegShared& sh, int K, float eps, int lane) {
-    float ss = 0.f;
-    for (int i = lane * 4; i < K; i += 256) {
-        const float4 x = *(const float4*)(sh.xs + i);
-        ss = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, ss))));
-    }
-    ss = wave_sum(ss);
-    return 1.0f / sqrtf(ss / (float)K + eps);
-}
-
-// Streaming waves: dot products of this wave's columns with the staged row (RMSNormed
-// with gs and inv when norm), written to sh.dots[local column].
-template <int MC, int KC, int NP>
-__device__ __forceinline__ void w_dot(const uint4 (&w)[MC][KC], SegShared& sh, int K, bool norm, float inv, int ncols,
-                                      int wave, int lane) {
-    static_assert(NP >= MC && (NP & (NP - 1)) == 0, "NP: power of two >= MC");
-    float acc[NP];
+// Streaming waves: dot products of this wave's columns with the staged row (times
+// `scale`), written to sh.dots[local column].
+template <int MC, int KC>
+__device__ __forceinline__ void w_dot(const uint4 (&w)[MC][KC], SegShared& sh, int K, float scale, int ncols, int wave,
+                                      int lane) {
+    float acc[MC];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) acc[i] = 0.f;
+    for (int i = 0; i < MC; ++i) acc[i] = 0.f;
     const int nch = K >> 3;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
         const int ch = j * 64 + lane;
         if (ch < nch) {
-            float x[8];
-            const float4 x0 = *(const float4*)(sh.xs + ch * 8), x1 = *(const float4*)(sh.xs + ch * 8 + 4);
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-            if (norm) {
-                const float4 g0 = *(const float4*)(sh.gs + ch * 8), g1 = *(const float4*)(sh.gs + ch * 8 + 4);
-                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = x[e] * g[e] * inv;
-            }
+            const float4 lo = *(const float4*)(sh.xlo + ch * 4), hi = *(const float4*)(sh.xhi + ch * 4);
+            const float x[8] = {lo.x * scale, lo.y * scale, lo.z * scale, lo.w * scale,
+                                hi.x * scale, hi.y * scale, hi.z * scale, hi.w * scale};
 #pragma unroll
             for (int i = 0; i < MC; ++i) {
                 const uint32_t u[4] = {w[i][j].x, w[i][j].y, w[i][j].z, w[i][j].w};
@@ -203,12 +273,11 @@ __device__ __forceinline__ void w_dot(const uint4 (&w)[MC][KC], SegShared& sh, i
             }
         }
     }
-    const float tot = wave_transpose_sum<NP>(acc, lane);
-    constexpr int SH = (NP == 1) ? 6 : (NP == 2) ? 5 : (NP == 4) ? 4 : (NP == 8) ? 3 : 2;
-    if ((lane & ((1 << SH) - 1)) == 0) {
-        const int idx = lane >> SH;
-        const int c = wave + SEG_NS * idx;
-        if (idx < MC && c < ncols) sh.dots[c] = tot;
+#pragma unroll
+    for (int i = 0; i < MC; ++i) {
+        const float tot = wave_total(acc[i]);
+        const int c = wave + SEG_NS * i;
+        if (lane == 0 && c < ncols) sh.dots[c] = tot;
     }
 }
 
@@ -291,8 +360,9 @@ __device__ __forceinline__ void att_rounds(const uint4 (&kp)[NR], const uint4 (&
     }
 }
 
-// Streaming waves, attention phase: the wave's keys of the block's split; the wave's
-// softmax state (max, sum, output) goes to sh.wm / sh.wl / sh.wo.
+// Streaming waves, attention phase: the wave's keys of the block's split; the softmax
+// state (max, sum, output) of each lane group goes to slot wave * 4 + group of sh.wm /
+// sh.wl / sh.wo.
 __device__ void att_stream(const SegArgs& a, SegShared& sh, const AttItem& t, int layer, const uint4 (&kp)[NR],
                            const uint4 (&vp)[NR], int wave, int lane) {
     const float scale = 1.0f / sqrtf((float)SEG_HD);
@@ -321,28 +391,12 @@ __device__ void att_stream(const SegArgs& a, SegShared& sh, const AttItem& t, in
         sc = group_sum<16>(sc) * scale;
         att_update(m, l, o, sc, v, lane < 16);
     }
-    // merge the 4 lane groups (same dims, different keys)
+    const int slot = wave * 4 + (lane >> 4);
 #pragma unroll
-    for (int msk = 16; msk <= 32; msk <<= 1) {
-        const float m2 = __shfl_xor(m, msk, 64), l2 = __shfl_xor(l, msk, 64);
-        const float mn = fmaxf(m, m2);
-        const float c1 = (m == -INFINITY) ? 0.f : expf(m - mn);
-        const float c2 = (m2 == -INFINITY) ? 0.f : expf(m2 - mn);
-        l = c1 * l + c2 * l2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float o2 = __shfl_xor(o[e], msk, 64);
-            o[e] = c1 * o[e] + c2 * o2;
-        }
-        m = mn;
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sh.wo[wave][lane * 8 + e] = o[e];
-        if (lane == 0) {
-            sh.wm[wave] = m;
-            sh.wl[wave] = l;
-        }
+    for (int e = 0; e < 8; ++e) sh.wo[slot][(lane & 15) * 8 + e] = o[e];
+    if ((lane & 15) == 0) {
+        sh.wm[slot] = m;
+        sh.wl[slot] = l;
     }
 }
 
@@ -359,8 +413,8 @@ __device__ void seg_streamer(const SegArgs& a, SegShared& sh, int wave, int lane
         const SegLayerW& W = a.lw[li];
         // QKV
         seg_bar();
-        float inv = row_inv_rms(sh, d, a.eps, lane);
-        w_dot<MQ, KC_D, 4>(wq, sh, d, true, inv, cq, wave, lane);
+        float inv = 1.0f / sqrtf((sh.ss[0] + sh.ss[1]) / (float)d + a.eps);
+        w_dot<MQ, KC_D>(wq, sh, d, inv, cq, wave, lane);
         seg_bar();
         w_issue<1, KC_D>(wo, W.wo, d, b * co, co, wave, lane);
         // attention
@@ -368,23 +422,22 @@ __device__ void seg_streamer(const SegArgs& a, SegShared& sh, int wave, int lane
         if (t.on) att_stream(a, sh, t, l, kp, vp, wave, lane);
         seg_bar();
         w_issue<MG, KC_D>(wgu, W.wgu, d, b * cg, cg, wave, lane);
-        seg_bar();
         // O projection
         seg_bar();
-        w_dot<1, KC_D, 1>(wo, sh, d, false, 1.f, co, wave, lane);
+        w_dot<1, KC_D>(wo, sh, d, 1.0f, co, wave, lane);
         seg_bar();
         w_issue<1, KC_F>(wd, W.wd, F, b * co, co, wave, lane);
         // gate / up
         seg_bar();
-        inv = row_inv_rms(sh, d, a.eps, lane);
-        w_dot<MG, KC_D, 8>(wgu, sh, d, true, inv, cg, wave, lane);
+        inv = 1.0f / sqrtf((sh.ss[0] + sh.ss[1]) / (float)d + a.eps);
+        w_dot<MG, KC_D>(wgu, sh, d, inv, cg, wave, lane);
         seg_bar();
-        // (after the last layer: ncols 0 zeroes the registers without loading)
+        // (after the last layer: ncols 0 loads column 0 again, never used)
         const bool more = li + 1 < a.nl;
         w_issue<MQ, KC_D>(wq, a.lw[more ? li + 1 : li].wqkv, d, b * cq, more ? cq : 0, wave, lane);
         // down
         seg_bar();
-        w_dot<1, KC_F, 1>(wd, sh, F, false, 1.f, co, wave, lane);
+        w_dot<1, KC_F>(wd, sh, F, 1.0f, co, wave, lane);
         seg_bar();
         kv_issue(kp, vp, a, more ? l + 1 : l, t, t.lo, more, wave, lane);
     }
@@ -397,18 +450,18 @@ __device__ void seg_control(const SegArgs& a, SegShared& sh, int wc, int lane) {
     const int cq = 3 * d / NB, co = d / NB, cg = 2 * F / NB;
     const AttItem t = att_item(a);
     const unsigned long long spin = a.spin_ticks;
+    const int dd = wc * 64 + lane;   // head dimension this lane handles in the attention merges
     for (int li = 0; li < a.nl; ++li) {
         const int l = a.l0 + li;
         const SegLayerW& W = a.lw[li];
         const uint32_t ep = a.epoch + (uint32_t)(SEG_PHASES * li);
-        // ---- QKV: stage the layer input and the attention norm weight
+        // ---- QKV: stage the layer input times the attention norm weight
         if (li == 0) {
-            stage_plain(a.Hs + a.hrow * d, d, sh.xs, wc, lane);
+            stage_plain<NJ_D>(a.Hs + a.hrow * d, d, W.attn_norm, wc, lane, sh);
             if (wc == 0 && lane < co) sh.xres[lane] = a.Hs[a.hrow * d + b * co + lane];
         } else {
-            stage_tagged<NJ_D>(a.tx0, d, ep - SEG_PHASES + PH_X0, sh.xs, wc, lane, spin, sh, a.err);
+            stage_tagged<NJ_D>(a.tx0, d, ep - SEG_PHASES + PH_X0, co, W.attn_norm, wc, lane, spin, sh, a.err);
         }
-        stage_plain(W.attn_norm, d, sh.gs, wc, lane);
         seg_bar();
         seg_bar();
         // epilogue: column pair (2t, 2t+1) of the block = rotation partners
@@ -443,83 +496,71 @@ __device__ void seg_control(const SegArgs& a, SegShared& sh, int wc, int lane) {
         }
         // ---- attention: stage q (and the current key / value when this split holds them)
         if (t.on) {
-            stage_tagged<1>(a.tq + t.h * hd, hd, ep + PH_QKV, sh.qs, wc, lane, spin, sh, a.err);
+            stage_head(a.tq + t.h * hd, ep + PH_QKV, sh.qs, wc, lane, spin, sh, a.err);
             if (t.has_new) {
-                stage_tagged<1>(a.tk + t.h * hd, hd, ep + PH_QKV, sh.kn, wc, lane, spin, sh, a.err);
-                stage_tagged<1>(a.tv + t.h * hd, hd, ep + PH_QKV, sh.vn, wc, lane, spin, sh, a.err);
+                stage_head(a.tk + t.h * hd, ep + PH_QKV, sh.kn, wc, lane, spin, sh, a.err);
+                stage_head(a.tv + t.h * hd, ep + PH_QKV, sh.vn, wc, lane, spin, sh, a.err);
             }
         }
         seg_bar();
         seg_bar();
-        if (t.on && wc == 1) {
-            // the block's partial state over its keys: merge the streaming waves' states
-            // (lane: dims 2*lane, 2*lane + 1)
+        if (t.on) {
+            // the block's partial state over its keys (lane: head dimension dd), merged over
+            // the 4 lane groups of each streaming wave
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < SEG_NS; ++w) M = fmaxf(M, sh.wm[w]);
-            float L = 0.f, O0 = 0.f, O1 = 0.f;
+            for (int w = 0; w < SEG_NS * 4; ++w) M = fmaxf(M, sh.wm[w]);
+            float L = 0.f, O = 0.f;
 #pragma unroll
-            for (int w = 0; w < SEG_NS; ++w) {
-                if (sh.wm[w] != -INFINITY) {
-                    const float c = expf(sh.wm[w] - M);
-                    L += c * sh.wl[w];
-                    O0 += c * sh.wo[w][2 * lane];
-                    O1 += c * sh.wo[w][2 * lane + 1];
-                }
+            for (int w = 0; w < SEG_NS * 4; ++w) {
+                const float mw = sh.wm[w];
+                const float c = mw == -INFINITY ? 0.f : expf(mw - M);
+                L = fmaf(c, sh.wl[w], L);
+                O = fmaf(c, sh.wo[w][dd], O);
             }
             uint64_t* pt = a.tpart + ((int64_t)t.h * SEG_SMAX + t.s) * (2 + hd);
-            tstore(pt + 2 + 2 * lane, ep + PH_PART, O0);
-            tstore(pt + 3 + 2 * lane, ep + PH_PART, O1);
+            tstore(pt + 2 + dd, ep + PH_PART, O);
             if (lane == 0) {
                 tstore(pt, ep + PH_PART, M);
                 tstore(pt + 1, ep + PH_PART, L);
             }
-            __builtin_amdgcn_s_waitcnt(0);   // the partial is written before it is counted
-            int last = 0;
-            if (lane == 0) {
-                const uint32_t old = __hip_atomic_fetch_add(a.cnt + t.h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last = old + 1u == a.cnt_base + (uint32_t)((li + 1) * a.S);
-            }
-            last = __shfl(last, 0, 64);
-            if (lane == 0) sh.last = last;
-        }
-        seg_bar();
-        if (t.on && sh.last && !sh.bad) {
-            // the head's output: merge the S partials (lane of control wave wc: dim wc*64 + lane)
-            const int dd = wc * 64 + lane;
-            const uint64_t* ph = a.tpart + (int64_t)t.h * SEG_SMAX * (2 + hd);
-            const uint32_t e2 = ep + PH_PART;
-            const unsigned long long t_end = (unsigned long long)wall_clock64() + spin;
-            const __amdgpu_buffer_rsrc_t r = coh_rsrc(ph);
-            constexpr int SPLIT_BYTES = (2 + SEG_HD) * 8;
-            uint64_t ml[2], ov[SEG_SMAX];
-            for (;;) {
-                bool ok = true;
-                ml[0] = lane < a.S ? tload_b(r, lane * SPLIT_BYTES, 0) : tagv(e2, -INFINITY);
-                ml[1] = lane < a.S ? tload_b(r, lane * SPLIT_BYTES, 8) : tagv(e2, 0.f);
+            if (t.s == 0 && !sh.bad) {
+                // split 0 of each head merges the head's S partials (dimension dd)
+                const uint64_t* ph = a.tpart + (int64_t)t.h * SEG_SMAX * (2 + hd);
+                const uint32_t e2 = ep + PH_PART;
+                const unsigned long long t_end = (unsigned long long)wall_clock64() + spin;
+                const __amdgpu_buffer_rsrc_t r = coh_rsrc(ph);
+                constexpr int SPLIT_BYTES = (2 + SEG_HD) * 8;
+                uint64_t ml[2], ov[SEG_SMAX];
+                for (;;) {
+                    ml[0] = lane < a.S ? tload_b(r, lane * SPLIT_BYTES, 0) : tagv(e2, -INFINITY);
+                    ml[1] = lane < a.S ? tload_b(r, lane * SPLIT_BYTES, 8) : tagv(e2, 0.f);
 #pragma unroll
-                for (int s = 0; s < SEG_SMAX; ++s) ov[s] = s < a.S ? tload_b(r, (2 + dd) * 8, s * SPLIT_BYTES) : tagv(e2, 0.f);
-                ok = (uint32_t)(ml[0] >> 32) == e2 && (uint32_t)(ml[1] >> 32) == e2;
+                    for (int s = 0; s < SEG_SMAX; ++s)
+                        ov[s] = s < a.S ? tload_b(r, (2 + dd) * 8, s * SPLIT_BYTES) : tagv(e2, 0.f);
+                    bool ok = (uint32_t)(ml[0] >> 32) == e2 && (uint32_t)(ml[1] >> 32) == e2;
 #pragma unroll
-                for (int s = 0; s < SEG_SMAX; ++s) ok = ok && (uint32_t)(ov[s] >> 32) == e2;
-                if (__all(ok)) break;
-                if ((unsigned long long)wall_clock64() > t_end) {
-                    give_up(sh, a.err);
-                    break;
+                    for (int s = 0; s < SEG_SMAX; ++s) ok = ok && (uint32_t)(ov[s] >> 32) == e2;
+                    if (__all(ok)) break;
+                    if (timed_out(t_end)) {
+                        give_up(sh, a.err);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
                 }
-            }
-            // lane s < S holds split s's (max, sum): the weight of split s is exp(m_s - Mt)
-            const float ms = __uint_as_float((uint32_t)ml[0]), ls = __uint_as_float((uint32_t)ml[1]);
-            const float Mt = wave_max(lane < a.S ? ms : -INFINITY);
-            const float cs = (lane < a.S && ms != -INFINITY) ? expf(ms - Mt) : 0.f;
-            const float Lt = wave_sum(cs * ls);
-            float Ot = 0.f;
+                // lane s < S holds split s's (max, sum); split s weighs exp(m_s - Mt)
+                const float ms = __uint_as_float((uint32_t)ml[0]), ls = __uint_as_float((uint32_t)ml[1]);
+                const float Mt = wave_max(lane < a.S ? ms : -INFINITY);
+                const float cs = (lane < a.S && ms != -INFINITY) ? expf(ms - Mt) : 0.f;
+                const float Lt = wave_total(cs * ls);
+                float Ot = 0.f;
 #pragma unroll
-            for (int s = 0; s < SEG_SMAX; ++s) Ot = fmaf(__shfl(cs, s, 64), __uint_as_float((uint32_t)ov[s]), Ot);
-            tstore(a.tatt + t.h * hd + dd, ep + PH_ATT, Ot / Lt);
+                for (int s = 0; s < SEG_SMAX; ++s) Ot = fmaf(__shfl(cs, s, 64), __uint_as_float((uint32_t)ov[s]), Ot);
+                tstore(a.tatt + t.h * hd + dd, ep + PH_ATT, Ot / Lt);
+            }
         }
-        // ---- O projection: stage the attention output
-        stage_tagged<NJ_D>(a.tatt, d, ep + PH_ATT, sh.xs, wc, lane, spin, sh, a.err);
+        // ---- O projection: stage the attention output (no norm)
+        stage_tagged<NJ_D>(a.tatt, d, ep + PH_ATT, 64, nullptr, wc, lane, spin, sh, a.err);
         seg_bar();
         seg_bar();
         if (wc == 0 && lane < co) {
@@ -527,9 +568,8 @@ __device__ void seg_control(const SegArgs& a, SegShared& sh, int wc, int lane) {
             tstore(a.tx1 + b * co + lane, ep + PH_X1, x1);
             sh.x1own[lane] = x1;
         }
-        // ---- gate / up: stage x1 and the MLP norm weight
-        stage_tagged<NJ_D>(a.tx1, d, ep + PH_X1, sh.xs, wc, lane, spin, sh, a.err);
-        stage_plain(W.mlp_norm, d, sh.gs, wc, lane);
+        // ---- gate / up: stage x1 times the MLP norm weight
+        stage_tagged<NJ_D>(a.tx1, d, ep + PH_X1, co, W.mlp_norm, wc, lane, spin, sh, a.err);
         seg_bar();
         seg_bar();
         for (int tp = wc * 64 + lane; tp < cg / 2; tp += 128) {
@@ -537,7 +577,7 @@ __device__ void seg_control(const SegArgs& a, SegShared& sh, int wc, int lane) {
             tstore(a.tact + b * (cg / 2) + tp, ep + PH_ACT, g / (1.0f + expf(-g)) * u);
         }
         // ---- down: stage the SwiGLU output
-        stage_tagged<NJ_F>(a.tact, F, ep + PH_ACT, sh.xs, wc, lane, spin, sh, a.err);
+        stage_tagged<NJ_F>(a.tact, F, ep + PH_ACT, cg / 2, nullptr, wc, lane, spin, sh, a.err);
         seg_bar();
         seg_bar();
         if (wc == 0 && lane < co) {
@@ -553,10 +593,7 @@ __global__ __launch_bounds__(SEG_THREADS, 1) void k_segment(SegArgs a) {
     __shared__ SegShared sh;
     const unsigned long long t0 = stamp_begin(a.stamp);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (threadIdx.x == 0) {
-        sh.bad = 0;
-        sh.last = 0;
-    }
+    if (threadIdx.x == 0) sh.bad = 0;
     __syncthreads();
     if (wave < SEG_NS)
         seg_streamer(a, sh, wave, lane);
