@@ -12,5 +12,12 @@ Parity status per function (pins are in tests/test_oracle_*.py):
   generate_deferred                          pinned: bit-identity with sequential decoding,
                                              brute force over forced exit patterns
   head_logits (exits 1-3)                    pinned only through the same routines as exit 4
+  router_logit/gate, router MLP form         pinned: closed forms (zero output layer, zero first
+                                             layer, one active weight per layer)
+  adapter, head_logits, shared-head form     pinned: closed form with one active weight per
+                                             matrix; identity adapters give the textbook
+                                             forward's exit logits
+  sampling and deferral, second form         pinned: chi-square against pi_mix and p_k;
+                                             bit-identity with sequential decoding
 """
 from . import model, deferred  # noqa: F401

@@ -11,7 +11,9 @@ Citations are to the pages on "N-vium: Mixture-of-Exits Transformer for
 Accelerated Exact Generation" (arXiv 2605.13190):
   [Arch]      gist.science technical summary, section 2 "Methodik", part
               "Architektur": blocks ending in a router, router output w_k, the
-              equation for p_k with w_{N_V} = 1, the equation for pi_mix.
+              equation for p_k with w_{N_V} = 1, the equation for pi_mix; a
+              router MLP produces w_k; all exits share the final LM head, with
+              light adapter MLPs mapping intermediate states to its geometry.
   [Piggy]     same summary, section 2, part "Inferenz: Piggybacking": layers
               above the exit are deferred, their hidden states are concatenated
               with later tokens' states at those depths, KV becomes complete.
@@ -23,9 +25,12 @@ Accelerated Exact Generation" (arXiv 2605.13190):
   [Abstract]  the English abstract (quoted on the gptget.net and fugumt pages).
 
 Readings where the pages are silent (each is listed with its reason in the
-design notes): every exit has its own RMSNorm and LM head; the router is the
-linear gate sigmoid(g_k . h + b_k) on the un-normalised residual stream after
-the exit's last layer; LLaMA-2 layer = pre-norm RMSNorm, MHA with rotate-half
+design notes): in the first form every exit has its own RMSNorm and LM head and
+the router is the linear gate sigmoid(g_k . h + b_k) on the un-normalised
+residual stream after the exit's last layer; in the second form (the pages'
+own) the router is a one-hidden-layer MLP, sigmoid(w2_k . silu(W1_k h + b1_k) +
+b_k), and exit k < N_V reads the final RMSNorm + LM head through the residual
+adapter h + U_k silu(D_k h); LLaMA-2 layer = pre-norm RMSNorm, MHA with rotate-half
 RoPE on 0-based positions, scale 1/sqrt(hd), SwiGLU MLP, no linear biases;
 the exit is chosen by walking the gates with u_1..u_3 (stop at gate k iff
 u_k < w_k) and the token by inverse CDF with u_4 in token-id order (smallest
@@ -57,6 +62,9 @@ class OracleModel:
         eps, rope_base = struct.unpack_from("<2f", hdr, 44)
         self.exit_layers = list(struct.unpack_from("<4i", hdr, 52))
         self.gate_bias = [float(b) for b in struct.unpack_from("<4f", hdr, 68)]
+        head_form, self.adapter_dim, router_form, self.router_dim = struct.unpack_from("<4i", hdr, 84)
+        self.shared_head = head_form == 1
+        self.router_mlp = router_form == 1
         self.L, self.d, self.H, self.hd, self.F, self.V, self.n_exits = L, d, H, hd, F, V, nx
         self.eps, self.rope_base = float(eps), float(rope_base)
         self.bf16 = wd == 1
@@ -75,7 +83,7 @@ class OracleModel:
                 off[0] = o + 4 * n
             return arr.reshape(shape)
 
-        total = V * d * (1 + nx) + L * (4 * d * d + 3 * F * d)
+        total = V * d * (1 + (1 if self.shared_head else nx)) + L * (4 * d * d + 3 * F * d)
         self.f64 = total <= keep_f32_above
         cast = (lambda a: a.astype(np.float64)) if self.f64 else (lambda a: np.ascontiguousarray(a))
 
@@ -93,10 +101,28 @@ class OracleModel:
             self.wu.append(cast(take((F, d), True)))
             self.wd.append(cast(take((d, F), True)))
         self.gate_w, self.exit_norm, self.head = [], [], []
-        for _ in range(nx):
-            self.gate_w.append(take((d,), False).astype(np.float64))
-            self.exit_norm.append(take((d,), False).astype(np.float64))
-            self.head.append(cast(take((V, d), True)))
+        self.router_w1, self.router_b1, self.router_w2 = [], [], []
+        self.adapter_down, self.adapter_up = [], []
+        rr, r = self.router_dim, self.adapter_dim
+        for k in range(nx):
+            if self.router_mlp:
+                self.router_w1.append(take((rr, d), False).astype(np.float64))
+                self.router_b1.append(take((rr,), False).astype(np.float64))
+                self.router_w2.append(take((rr,), False).astype(np.float64))
+            else:
+                self.gate_w.append(take((d,), False).astype(np.float64))
+            if self.shared_head:
+                if k < nx - 1:
+                    self.adapter_down.append(take((r, d), True).astype(np.float64))
+                    self.adapter_up.append(take((d, r), True).astype(np.float64))
+            else:
+                self.exit_norm.append(take((d,), False).astype(np.float64))
+                self.head.append(cast(take((V, d), True)))
+        if self.shared_head:
+            self.final_norm = take((d,), False).astype(np.float64)
+            shared = cast(take((V, d), True))
+            self.head = [shared] * nx
+            self.exit_norm = [self.final_norm] * nx
         del raw
 
     def segment_layers(self, s: int) -> range:
@@ -201,11 +227,20 @@ def layer_rows(M: OracleModel, l: int, X: np.ndarray, pos: Sequence[int], kv: KV
 # --------------------------------------------------------------------------------------------
 
 
+def router_logit(M: OracleModel, k: int, h: np.ndarray) -> float:
+    """The router's pre-sigmoid output at exit k (0-based, k < N_V - 1) [Arch]: a linear
+    gate g_k . h + b_k, or the router MLP w2_k . silu(W1_k h + b1_k) + b_k."""
+    if M.router_mlp:
+        hidden = silu(M.router_w1[k] @ np.asarray(h, dtype=np.float64) + M.router_b1[k])
+        return float(np.dot(M.router_w2[k], hidden)) + M.gate_bias[k]
+    return float(np.dot(M.gate_w[k], h)) + M.gate_bias[k]
+
+
 def gate(M: OracleModel, k: int, h: np.ndarray) -> float:
-    """Router output w_k = sigmoid(g_k . h + b_k) for k < N_V - 1 (0-based); w_{N_V} = 1."""
+    """Router output w_k = sigmoid(router logit) for k < N_V - 1 (0-based); w_{N_V} = 1."""
     if k == M.n_exits - 1:
         return 1.0
-    z = float(np.dot(M.gate_w[k], h)) + M.gate_bias[k]
+    z = router_logit(M, k, h)
     if z >= 0:
         return 1.0 / (1.0 + math.exp(-z))
     ez = math.exp(z)                       # z = -inf gives exactly 0
@@ -221,8 +256,21 @@ def exit_probs(w: Sequence[float]) -> List[float]:
     return p
 
 
+def adapter(M: OracleModel, k: int, h: np.ndarray) -> np.ndarray:
+    """Adapter of intermediate exit k (shared head) [Arch, shared head]: a residual
+    bottleneck MLP h + U_k silu(D_k h) that maps the exit's hidden state towards the
+    geometry the final head expects; the last exit uses h as it is."""
+    h = np.asarray(h, dtype=np.float64)
+    if k == M.n_exits - 1:
+        return h
+    return h + M.adapter_up[k] @ silu(M.adapter_down[k] @ h)
+
+
 def head_logits(M: OracleModel, k: int, h: np.ndarray) -> np.ndarray:
-    """Logits of exit k: its own LM head applied to its own RMSNorm of h."""
+    """Logits of exit k: its own RMSNorm and LM head applied to h, or (shared head) the
+    final RMSNorm and LM head applied to the exit's adapter output."""
+    if M.shared_head:
+        return lin(rmsnorm(adapter(M, k, h), M.final_norm, M.eps), M.head[k])
     return lin(rmsnorm(h, M.exit_norm[k], M.eps), M.head[k])
 
 

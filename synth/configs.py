@@ -1,7 +1,9 @@
 """Named model shapes and decode workloads (pure data, no model arithmetic).
 
 Five workloads share one model family: a LLaMA-2-style decoder whose depth is cut
-into four equal segments, each ending in an exit (halting gate + own LM head).
+into four equal segments, each ending in an exit (halting gate + own LM head).  A sixth
+(E) uses the exit form of the N-vium pages instead: every exit reads the one final LM
+head through a light adapter MLP, and the halting gate is a small router MLP.
 
   T  tiny fp32 model, batch 1, 64-token prompt, 64 decode steps
   A  1.5B bf16 model, batch 1, 512-token prompt, 512 decode steps
@@ -9,6 +11,8 @@ into four equal segments, each ending in an exit (halting gate + own LM head).
   C  model A, 16 independent sequences, prompt lengths uniform in [256, 1024],
      256 decode steps each
   D  model A with exit mass skewed early, batch 1, 8192-token prompt, 256 steps
+  E  model A with a shared head + adapters (bottleneck 192) and router MLPs (hidden 64),
+     batch 1, 512-token prompt, 512 steps
 
 Gate biases.  Each intermediate gate is sigmoid(g_k . h + b_k); with the linear
 term at zero the conditional stop probability of gate k is sigmoid(b_k), and the
@@ -17,8 +21,10 @@ are the logits of the conditional stop probabilities that give the stated
 marginal masses at a zero linear term:
   masses (0.4, 0.25, 0.2, 0.15): conditional stops 0.4, 0.25/0.6, 0.2/0.35
   masses (0.6, 0.2, 0.1, 0.1):   conditional stops 0.6, 0.2/0.4,  0.1/0.2
-With g_k ~ N(0, 0.02^2) and a residual stream of norm ~0.8 the linear term is
-~N(0, 0.016^2), so the realised masses sit near the stated ones.
+With random-init weights the residual stream after a segment has norm ~85-180, so the
+linear term g_k . h (g_k ~ N(0, 0.02^2)) has a standard deviation near 2 and the
+realised masses differ from the stated ones; benchmarks report the realised exit
+histogram.
 """
 from __future__ import annotations
 
@@ -51,6 +57,11 @@ class ModelShape:
     rope_base: float = 1e4
     init_std: float = 0.02
     seed: int = 0
+    head: str = "own"                # "own": a norm + LM head per exit; "shared": one final
+                                     # norm + LM head, intermediate exits through an adapter
+    adapter_dim: int = 0             # adapter bottleneck width (head "shared")
+    router: str = "linear"           # "linear": sigmoid(g.h + b); "mlp": sigmoid(w2.silu(W1 h + b1) + b)
+    router_dim: int = 0              # router hidden width (router "mlp")
 
     @property
     def exit_layers(self) -> Tuple[int, ...]:
@@ -105,6 +116,10 @@ WORKLOADS = {
     "D": Workload("D", replace(M15B, gate_bias=BIAS_MASS_60_20_10_10), batch=1, prompt_len=8192,
                   decode_steps=256,
                   note="1.5B bf16, batch 1, prompt 8192, decode 256, exit mass ~[.6,.2,.1,.1]"),
+    "E": Workload("E", replace(M15B, head="shared", adapter_dim=192, router="mlp", router_dim=64), batch=1,
+                  prompt_len=512, decode_steps=512,
+                  note="1.5B bf16, shared LM head + adapters (192), router MLPs (64), batch 1, prompt 512, "
+                       "decode 512, exit mass ~[.4,.25,.2,.15]"),
 }
 
 

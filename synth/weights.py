@@ -18,7 +18,12 @@ oracle's own reader:
   48      float32  RoPE base
   52      int32[4] exit layer (1-based layer index after which exit k sits)
   68      float32[4] gate bias b_k (entry 4 is +inf: the last gate is fixed to 1)
-  84..255 zero
+  84      int32    head form: 0 = own norm + LM head per exit, 1 = shared final norm + LM
+                   head, intermediate exits through an adapter MLP
+  88      int32    adapter bottleneck r (head form 1)
+  92      int32    router form: 0 = linear gate, 1 = router MLP
+  96      int32    router hidden width rr (router form 1)
+  100..255 zero
   256...  tensors, each starting at a multiple of 256 bytes, in this order:
           embed      [V][d]       matrix dtype
           per layer l = 0..L-1:
@@ -28,14 +33,23 @@ oracle's own reader:
             wg, wu    [F][d]      matrix dtype
             wd        [d][F]      matrix dtype
           per exit k = 0..3:
-            gate_w    [d]         fp32 (zeros for the last exit: unused)
-            exit_norm [d]         fp32
-            head      [V][d]      matrix dtype
+            router form 0: gate_w [d]          fp32 (zeros for the last exit: unused)
+            router form 1: router_w1 [rr][d]   fp32 (zeros for the last exit)
+                           router_b1 [rr]      fp32 (zeros)
+                           router_w2 [rr]      fp32 (zeros for the last exit)
+            head form 0:   exit_norm [d]       fp32
+                           head      [V][d]    matrix dtype
+            head form 1, k < 3: adapter_down [r][d]  matrix dtype
+                                adapter_up   [d][r]  matrix dtype
+          head form 1, after the exits:
+            final_norm [d]        fp32
+            head       [V][d]     matrix dtype
 
 Values: tensor number i in the order above (0-based, norm vectors included) is
 drawn from numpy.random.default_rng([seed, i]).standard_normal(float32) * 0.02;
-RMSNorm weights are 1; the last exit's gate vector is 0.  bf16 matrices are the
-round-to-nearest-even bf16 of those float32 values.
+RMSNorm weights are 1; the last exit's gate vector (or router tensors) and router
+biases are 0.  bf16 matrices are the round-to-nearest-even bf16 of those float32
+values.
 """
 from __future__ import annotations
 
@@ -72,11 +86,29 @@ def tensor_specs(m: ModelShape) -> List[Tuple[str, Tuple[int, ...], str]]:
             (f"l{l}.wd", (d, F), "mat"),
         ]
     for k in range(m.n_exits):
-        specs += [
-            (f"x{k}.gate_w", (d,), "gate" if k < m.n_exits - 1 else "zero"),
-            (f"x{k}.exit_norm", (d,), "norm"),
-            (f"x{k}.head", (V, d), "mat"),
-        ]
+        last = k == m.n_exits - 1
+        if m.router == "mlp":
+            rr = m.router_dim
+            specs += [
+                (f"x{k}.router_w1", (rr, d), "zero" if last else "gate"),
+                (f"x{k}.router_b1", (rr,), "zero"),
+                (f"x{k}.router_w2", (rr,), "zero" if last else "gate"),
+            ]
+        else:
+            specs += [(f"x{k}.gate_w", (d,), "zero" if last else "gate")]
+        if m.head == "shared":
+            if not last:
+                specs += [
+                    (f"x{k}.adapter_down", (m.adapter_dim, d), "mat"),
+                    (f"x{k}.adapter_up", (d, m.adapter_dim), "mat"),
+                ]
+        else:
+            specs += [
+                (f"x{k}.exit_norm", (d,), "norm"),
+                (f"x{k}.head", (V, d), "mat"),
+            ]
+    if m.head == "shared":
+        specs += [("final_norm", (d,), "norm"), ("head", (V, d), "mat")]
     return specs
 
 
@@ -99,6 +131,8 @@ def header_bytes(m: ModelShape) -> bytes:
     hdr += struct.pack("<4i", *m.exit_layers)
     biases = list(m.gate_bias) + [float("inf")]
     hdr += struct.pack("<4f", *biases)
+    hdr += struct.pack("<4i", 1 if m.head == "shared" else 0, m.adapter_dim if m.head == "shared" else 0,
+                       1 if m.router == "mlp" else 0, m.router_dim if m.router == "mlp" else 0)
     return hdr + b"\0" * (HEADER_BYTES - len(hdr))
 
 
