@@ -55,6 +55,13 @@ typedef struct nv_config {
     float norm_eps, rope_base;
     int32_t exit_layer[4];          /* 1-based layer after which exit k sits */
     float gate_bias[4];             /* b_k; the last is +inf (w = 1) */
+    int32_t head_form;              /* 0: own RMSNorm + LM head per exit; 1: one final RMSNorm + LM
+                                       head, exits 1..3 reach it through the adapter MLP
+                                       h + U_k silu(D_k h) */
+    int32_t adapter_dim;            /* adapter bottleneck r (head_form 1) */
+    int32_t router_form;            /* 0: w_k = sigmoid(g_k . h + b_k); 1: router MLP,
+                                       w_k = sigmoid(w2_k . silu(W1_k h + b1_k) + b_k) */
+    int32_t router_dim;             /* router hidden width (router_form 1) */
 } nv_config;
 
 /* Device bytes nv_load needs for this weights file at this capacity

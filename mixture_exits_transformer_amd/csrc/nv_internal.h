@@ -8,7 +8,7 @@ namespace nv {
 struct RowInfo;
 struct CombineInfo;
 
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SILU = 4 };
 
 struct LayerDims {
     int L, d, H, hd, F, V, max_ctx, kv_bf16;
@@ -26,7 +26,7 @@ struct GemmArgs {
     const void* W;        // [N][K], fp32 or bf16 (wbf16)
     int N, K, R;
     int wbf16;
-    int epi;              // EPI_STORE: out = acc; EPI_RESID: out += acc;
+    int epi;              // EPI_STORE: out = acc; EPI_RESID: out += acc; EPI_SILU: out = silu(acc);
                           // EPI_SWIGLU: columns (2j, 2j+1) = (gate_j, up_j), out[j] = silu(g) * u
                           // EPI_QKV: columns (2p, 2p+1) are rotation partners (see below):
                           //   q -> RoPE -> q_out[row]; k -> RoPE -> KV cache; v -> KV cache
@@ -99,6 +99,13 @@ hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float*
                        double* w_out, int* stop_out, hipStream_t st);
 hipError_t launch_sample(const float* logits, int64_t ld, const int* seqs, int n, int V,
                          const float* uniforms, int* tok_out, hipStream_t st);
+// Router MLP gate: w = sigmoid(w2 . silu(W1 h + b1) + bias) in float64 (W1 [rr][d]);
+// hid: [n][rr] float64 scratch for the hidden units.
+hipError_t launch_gate_mlp(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d, const float* w1,
+                           const float* b1, const float* w2, int rr, float bias, const float* uniforms, int ucol,
+                           double* hid, double* w_out, int* stop_out, hipStream_t st);
+// dst row i = Hs row rows[i].hrow (d floats each).
+hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst, hipStream_t st);
 hipError_t init_kernel_attributes();
 // Timing: the next launch stamps `start` at its start; every launch stamps `stop` at its
 // end, until cleared with (nullptr, nullptr).

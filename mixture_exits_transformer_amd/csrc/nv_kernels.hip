@@ -137,6 +137,9 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, floa
     if (a.epi == EPI_STORE) {
         o[0] = v0;
         o[1] = v1;
+    } else if (a.epi == EPI_SILU) {
+        o[0] = v0 / (1.0f + expf(-v0));
+        o[1] = v1 / (1.0f + expf(-v1));
     } else {
         o[0] += v0;
         o[1] += v1;
@@ -234,6 +237,9 @@ __device__ __forceinline__ void epi_apply(const GemmArgs& a, const EpiCtx& e, in
         if (a.epi == EPI_STORE) {
             o[0] = v0;
             o[1] = v1;
+        } else if (a.epi == EPI_SILU) {
+            o[0] = v0 / (1.0f + expf(-v0));
+            o[1] = v1 / (1.0f + expf(-v1));
         } else {
             o[0] += v0;
             o[1] += v1;
@@ -1438,6 +1444,92 @@ hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float*
     if (n <= 0) return hipSuccess;
     NV_LAUNCH(k_gate, dim3(n), dim3(256), 0, st, rows, seqs, n, Hs, d, gw, bias, uniforms, ucol, w_out,
                        stop_out);
+    return hipGetLastError();
+}
+
+// Router MLP gate in two passes, all in float64.
+//  k_router_hidden: one wave per (row, hidden unit j): hid[row][j] = silu(W1[j] . h + b1[j]);
+//    lane l holds the float4 chunks 4l + 256t of h and of the W1 row (all in flight).
+//  k_router_out: w = sigmoid(w2 . hid[row] + bias); stop iff u < w.
+constexpr int GATE_MLP_MAX = 1024;
+constexpr int GATE_MLP_KD = 8;       // float4 chunks per lane: d <= 2048
+
+__global__ __launch_bounds__(256) void k_router_hidden(const RowInfo* rows, int n, const float* Hs, int d,
+                                                       const float* w1, const float* b1, int rr, double* hid) {
+    const int i = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (i >= n || j >= rr) return;
+    const float* h = Hs + (int64_t)rows[i].hrow * d;
+    const float* wr = w1 + (int64_t)j * d;
+    float4 hv[GATE_MLP_KD], wv[GATE_MLP_KD];
+#pragma unroll
+    for (int t = 0; t < GATE_MLP_KD; ++t) {
+        const int k = lane * 4 + 256 * t;
+        hv[t] = k < d ? *(const float4*)(h + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        wv[t] = k < d ? *(const float4*)(wr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int t = 0; t < GATE_MLP_KD; ++t) {
+        acc += (double)wv[t].x * (double)hv[t].x + (double)wv[t].y * (double)hv[t].y;
+        acc += (double)wv[t].z * (double)hv[t].z + (double)wv[t].w * (double)hv[t].w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) {
+        const double x = acc + (double)b1[j];
+        hid[(int64_t)i * rr + j] = x / (1.0 + exp(-x));
+    }
+}
+
+__global__ __launch_bounds__(64) void k_router_out(const int* seqs, int n, const double* hid, const float* w2, int rr,
+                                                   float bias, const float* uniforms, int ucol, double* w_out,
+                                                   int* stop_out) {
+    const int i = blockIdx.x;
+    if (i >= n) return;
+    const int lane = threadIdx.x;
+    double acc = 0.0;
+    for (int j = lane; j < rr; j += 64) acc += (double)w2[j] * hid[(int64_t)i * rr + j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) {
+        const double z = acc + (double)bias;
+        double w;
+        if (z >= 0.0) {
+            w = 1.0 / (1.0 + exp(-z));
+        } else {
+            const double ez = exp(z);
+            w = ez / (1.0 + ez);
+        }
+        const int seq = seqs[i];
+        w_out[seq * 4 + ucol] = w;
+        stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+    }
+}
+
+hipError_t launch_gate_mlp(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d, const float* w1,
+                           const float* b1, const float* w2, int rr, float bias, const float* uniforms, int ucol,
+                           double* hid, double* w_out, int* stop_out, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    if (rr < 1 || rr > GATE_MLP_MAX || d % 4 != 0 || d > 256 * GATE_MLP_KD) return hipErrorInvalidValue;
+    NV_LAUNCH(k_router_hidden, dim3(n, (rr + 3) / 4), dim3(256), 0, st, rows, n, Hs, d, w1, b1, rr, hid);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    NV_LAUNCH(k_router_out, dim3(n), dim3(64), 0, st, seqs, n, hid, w2, rr, bias, uniforms, ucol, w_out, stop_out);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst) {
+    const int i = blockIdx.x;
+    if (i >= n) return;
+    const float* src = Hs + (int64_t)rows[i].hrow * d;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) dst[(int64_t)i * d + k] = src[k];
+}
+
+hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    NV_LAUNCH(k_copy_rows, dim3(n), dim3(256), 0, st, rows, n, Hs, d, dst);
     return hipGetLastError();
 }
 

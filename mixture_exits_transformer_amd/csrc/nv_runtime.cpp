@@ -43,9 +43,14 @@ struct LayerPtrs {
 };
 
 struct ExitPtrs {
-    float* gate_w;
-    float* norm;
-    void* head;   // [V][d]
+    float* gate_w;          // linear router: [d]
+    float* router_w1;       // router MLP: [rr][d], [rr], [rr]
+    float* router_b1;
+    float* router_w2;
+    float* norm;            // RMSNorm before the head (the shared final norm in the shared form)
+    void* head;             // [V][d] (the shared head in the shared form)
+    void* adapter_down;     // shared form, exits 1..3: [r][d]
+    void* adapter_up;       // [d][r]
     float bias;
 };
 
@@ -68,11 +73,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Sizes of everything the model keeps in device memory.
 struct Plan {
     size_t es = 0, kes = 0;
-    size_t embed = 0, layer_w = 0, exit_w = 0;
+    size_t embed = 0, layer_w = 0, exit_w = 0, shared_head = 0;
     size_t hidden = 0, kv = 0, rope = 0;
     int R_max = 0, part_cap = 0, items_cap = 0;
     size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0;
-    size_t tables = 0, small = 0, logits = 0;
+    size_t tables = 0, small = 0, logits = 0, router_hid = 0;
     size_t seg = 0;     // persistent segment kernel: tagged exchange buffers, counters, layer table
     size_t total = 0;
 };
@@ -112,12 +117,23 @@ bool read_header(const char* path, nv_config* c, std::string* err) {
     std::memcpy(&c->rope_base, h + 48, 4);
     std::memcpy(c->exit_layer, h + 52, 16);
     std::memcpy(c->gate_bias, h + 68, 16);
+    int32_t forms[4];
+    std::memcpy(forms, h + 84, 16);
+    c->head_form = forms[0];
+    c->adapter_dim = forms[1];
+    c->router_form = forms[2];
+    c->router_dim = forms[3];
     const int L = c->n_layers, d = c->d_model;
     bool ok = L > 0 && d > 0 && c->n_heads > 0 && c->head_dim > 0 && c->n_heads * c->head_dim == d &&
               c->ffn > 0 && c->vocab > 0 && c->n_exits == kMaxExits && (c->wdtype == 0 || c->wdtype == 1) &&
               L % kMaxExits == 0 && (c->head_dim == 32 || c->head_dim == 64 || c->head_dim == 128) &&
               d % 8 == 0 && c->ffn % 8 == 0 && c->vocab % 8 == 0 && c->vocab <= 32768;
     for (int k = 0; ok && k < kMaxExits; ++k) ok = c->exit_layer[k] == (k + 1) * (L / kMaxExits);
+    ok = ok && (c->head_form == 0 || (c->head_form == 1 && c->adapter_dim > 0 && c->adapter_dim % 8 == 0 &&
+                                     c->adapter_dim <= 4096));
+    ok = ok && (c->head_form == 1 || c->adapter_dim == 0) && c->adapter_dim <= c->ffn;
+    ok = ok && (c->router_form == 0 || (c->router_form == 1 && c->router_dim > 0 && c->router_dim <= 1024));
+    ok = ok && (c->router_form == 1 || c->router_dim == 0);
     if (!ok) {
         *err = "weights header describes an unsupported shape";
         return false;
@@ -133,7 +149,12 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.embed = align_up(V * d * p.es);
     p.layer_w = align_up(d * 4) * 2 + align_up(3 * d * d * p.es) + align_up(d * d * p.es) +
                 align_up(2 * F * d * p.es) + align_up(d * F * p.es);
-    p.exit_w = align_up(d * 4) * 2 + align_up(V * d * p.es);
+    // per exit: router, then the own norm + head or the adapter; the shared norm + head once
+    const size_t rr = c.router_dim, r = c.adapter_dim;
+    const size_t router_w = c.router_form == 1 ? align_up(rr * d * 4) + 2 * align_up(rr * 4) : align_up(d * 4);
+    const size_t head_w = c.head_form == 1 ? 2 * align_up(r * d * p.es) : align_up(d * 4) + align_up(V * d * p.es);
+    p.exit_w = router_w + head_w;
+    p.shared_head = c.head_form == 1 ? align_up(d * 4) + align_up(V * d * p.es) : 0;
     p.hidden = align_up((size_t)max_batch * max_ctx * d * 4);
     p.kv = align_up((size_t)max_batch * L * 2 * H * max_ctx * hd * p.kes);
     p.rope = align_up((size_t)max_ctx * hd * 4);
@@ -157,7 +178,9 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.logits = align_up((size_t)max_batch * V * 4);
     p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
-    p.total = p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
+    p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
+    p.total = p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head + p.hidden + p.kv +
+              p.rope + p.qbuf + p.attn_o +
               p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
     return p;
 }
@@ -189,6 +212,7 @@ struct nv_model {
     float* part_ml = nullptr;
     float* part_o = nullptr;
     float* rms_ws = nullptr;   // [R_max] per-row inverse RMS for the matrix-core GEMM
+    double* router_hid = nullptr;   // [max_batch][router_dim] router MLP hidden units
     int mfma_min_rows = 9;     // chunks of at least this many rows use the matrix cores
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
@@ -883,6 +907,8 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->max_ctx = max_ctx;
     m->plan = make_plan(c, max_batch, max_ctx);
     const Plan& P = m->plan;
+    if (c.head_form == 1 && max_batch > P.R_max)
+        return fail(m, NV_ECAPACITY, "shared head: max_batch exceeds the row workspace");
     m->st = (hipStream_t)hip_stream;
 
     // check the file length before touching the device
@@ -904,8 +930,26 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
             adv(F * d * es);
             adv(d * F * es);
         }
+        const size_t rr = c.router_dim, r = c.adapter_dim;
         for (int k = 0; k < kMaxExits; ++k) {
-            adv(d * 4);
+            if (c.router_form == 1) {
+                adv(rr * d * 4);
+                adv(rr * 4);
+                adv(rr * 4);
+            } else {
+                adv(d * 4);
+            }
+            if (c.head_form == 1) {
+                if (k < kMaxExits - 1) {
+                    adv(r * d * es);
+                    adv(d * r * es);
+                }
+            } else {
+                adv(d * 4);
+                adv(V * d * es);
+            }
+        }
+        if (c.head_form == 1) {
             adv(d * 4);
             adv(V * d * es);
         }
@@ -935,11 +979,33 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
         W.wgu = m->take(2 * (size_t)m->F * m->d * P.es);
         W.wd = m->take((size_t)m->d * m->F * P.es);
     }
+    const size_t rr = c.router_dim, ra = c.adapter_dim;
     for (int k = 0; k < kMaxExits; ++k) {
-        m->exits[k].gate_w = (float*)m->take((size_t)m->d * 4);
-        m->exits[k].norm = (float*)m->take((size_t)m->d * 4);
-        m->exits[k].head = m->take((size_t)m->V * m->d * P.es);
-        m->exits[k].bias = c.gate_bias[k];
+        ExitPtrs& X = m->exits[k];
+        X = ExitPtrs{};
+        if (c.router_form == 1) {
+            X.router_w1 = (float*)m->take(rr * m->d * 4);
+            X.router_b1 = (float*)m->take(rr * 4);
+            X.router_w2 = (float*)m->take(rr * 4);
+        } else {
+            X.gate_w = (float*)m->take((size_t)m->d * 4);
+        }
+        if (c.head_form == 1) {
+            X.adapter_down = m->take(ra * m->d * P.es);
+            X.adapter_up = m->take(ra * m->d * P.es);
+        } else {
+            X.norm = (float*)m->take((size_t)m->d * 4);
+            X.head = m->take((size_t)m->V * m->d * P.es);
+        }
+        X.bias = c.gate_bias[k];
+    }
+    if (c.head_form == 1) {
+        float* fnorm = (float*)m->take((size_t)m->d * 4);
+        void* head = m->take((size_t)m->V * m->d * P.es);
+        for (int k = 0; k < kMaxExits; ++k) {
+            m->exits[k].norm = fnorm;
+            m->exits[k].head = head;
+        }
     }
     m->Hs = (float*)m->take(P.hidden);
     m->kv = m->take(P.kv);
@@ -960,6 +1026,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->d_stop = (int*)m->take((size_t)max_batch * 4);
     m->d_tok_out = (int*)m->take((size_t)max_batch * 4);
     m->logits = (float*)m->take(P.logits);
+    m->router_hid = (double*)m->take(P.router_hid);
     m->seg_base = m->take(P.seg);
     if (m->arena_off > P.total) return fail(m, NV_ECAPACITY, "internal: arena plan too small");
 
@@ -1048,9 +1115,27 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
         copy_tensor(W.wd, d * F * es);
     }
     for (int k = 0; k < kMaxExits && io_ok && herr == hipSuccess; ++k) {
-        copy_tensor(m->exits[k].gate_w, d * 4);
-        copy_tensor(m->exits[k].norm, d * 4);
-        copy_tensor(m->exits[k].head, V * d * es);
+        const ExitPtrs& X = m->exits[k];
+        if (c.router_form == 1) {
+            copy_tensor(X.router_w1, (size_t)c.router_dim * d * 4);
+            copy_tensor(X.router_b1, (size_t)c.router_dim * 4);
+            copy_tensor(X.router_w2, (size_t)c.router_dim * 4);
+        } else {
+            copy_tensor(X.gate_w, d * 4);
+        }
+        if (c.head_form == 1) {
+            if (k < kMaxExits - 1) {
+                copy_tensor(X.adapter_down, (size_t)c.adapter_dim * d * es);
+                copy_tensor(X.adapter_up, (size_t)c.adapter_dim * d * es);
+            }
+        } else {
+            copy_tensor(X.norm, d * 4);
+            copy_tensor(X.head, V * d * es);
+        }
+    }
+    if (c.head_form == 1 && io_ok && herr == hipSuccess) {
+        copy_tensor(m->exits[0].norm, d * 4);
+        copy_tensor(m->exits[0].head, V * d * es);
     }
     ::close(fd);
     (void)hipHostFree(bounce);
@@ -1105,6 +1190,91 @@ nv_status nv_prefill(nv_model* m, int32_t seq, const int32_t* tokens, int32_t n)
     return NV_OK;
 }
 
+// Logits and the inverse-CDF draw for sequences `seqs` (exit exit_of[i], 1-based) at their
+// current positions; logits go to row `seq` of the logits buffer.
+//   own heads:   the exit's RMSNorm and LM head on the hidden row (seqs share one exit);
+//   shared head: hidden rows are gathered (seqs ordered by exit), exits 1..3 add their
+//                adapter U silu(D h), then one pass of the final RMSNorm and LM head.
+static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std::vector<int>& exit_of,
+                           const float* d_unif) {
+    char* hl = m->h_headlist;
+    const int ns = (int)seqs.size();
+    for (int j = 0; j < ns; ++j) {
+        const int i = seqs[j];
+        nv_model::lseqs(hl)[j] = i;
+        m->lrows(hl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
+        m->lorows(hl)[j] = RowInfo{i, i, 0, 0};
+    }
+    NV_HIP(m, hipMemcpyAsync(m->d_headlist, hl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
+    const int ex0 = exit_of[seqs[0]] - 1;
+    GemmArgs g{};
+    g.eps = m->cfg.norm_eps;
+    g.wbf16 = m->bf16 ? 1 : 0;
+    g.rms_ws = m->rms_ws;
+    g.mfma_min_rows = m->mfma_min_rows;
+    if (m->cfg.head_form == 1) {
+        float* X = m->attn_o;   // [ns][d] gathered rows, then adapter outputs
+        float* S = m->mlp;      // [ns][r] adapter hidden units
+        const int d = m->d, r = m->cfg.adapter_dim;
+        NV_TRY(timed(m, NV_TIME_EXIT_HEAD, (double)ns * d * 8, [&] {
+            return launch_copy_rows(m->lrows(m->d_headlist), ns, m->Hs, d, X, m->st);
+        }, "nv::k_copy_rows"));
+        for (int j0 = 0; j0 < ns;) {
+            const int k = exit_of[seqs[j0]] - 1;
+            int j1 = j0;
+            while (j1 < ns && exit_of[seqs[j1]] - 1 == k) ++j1;
+            if (k < kMaxExits - 1) {
+                GemmArgs a = g;
+                a.A = X + (int64_t)j0 * d;
+                a.lda = d;
+                a.W = m->exits[k].adapter_down;
+                a.N = r;
+                a.K = d;
+                a.R = j1 - j0;
+                a.epi = EPI_SILU;
+                a.out = S + (int64_t)j0 * r;
+                a.ldo = r;
+                NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, a), [&] { return launch_gemm(a, m->st); }));
+                GemmArgs b = g;
+                b.A = S + (int64_t)j0 * r;
+                b.lda = r;
+                b.W = m->exits[k].adapter_up;
+                b.N = d;
+                b.K = r;
+                b.R = j1 - j0;
+                b.epi = EPI_RESID;
+                b.out = X + (int64_t)j0 * d;
+                b.ldo = d;
+                NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, b), [&] { return launch_gemm(b, m->st); }));
+            }
+            j0 = j1;
+        }
+        g.A = X;
+        g.lda = d;
+        g.a_rows = nullptr;
+    } else {
+        g.A = m->Hs;
+        g.lda = m->d;
+        g.a_rows = m->lrows(m->d_headlist);
+    }
+    g.norm_w = m->exits[ex0].norm;
+    g.W = m->exits[ex0].head;
+    g.N = m->V;
+    g.K = m->d;
+    g.R = ns;
+    g.epi = EPI_STORE;
+    g.out = m->logits;
+    g.ldo = m->V;
+    g.o_rows = m->lorows(m->d_headlist);
+    g.head = 1;
+    NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+    NV_TRY(timed(m, NV_TIME_OTHER, (double)ns * m->V * 4, [&] {
+        return launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif, m->d_tok_out,
+                             m->st);
+    }, "nv::k_sample"));
+    return NV_OK;
+}
+
 static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, int32_t* tok_out, int32_t* exit_out) {
     if (!m) return NV_EINVAL;
     if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
@@ -1144,6 +1314,7 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
     int* hstop = (int*)m->h_out;
     int* htok_out = (int*)(m->h_out + (size_t)m->max_batch * 4);
     double* hw = (double*)(m->h_out + (size_t)m->max_batch * 8);
+    std::vector<int> stopped;   // shared head: the step's stopping sequences, in exit order
     for (int sg = 0; sg < kMaxExits && !active.empty(); ++sg) {
         std::vector<Chunk> ch;
         for (int i : active) {
@@ -1163,10 +1334,19 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
                 m->lrows(gl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
             }
             NV_HIP(m, hipMemcpyAsync(m->d_gatelist, gl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
-            NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
-                return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
-                                   m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
-            }, "nv::k_gate"));
+            if (m->cfg.router_form == 1) {
+                const ExitPtrs& X = m->exits[sg];
+                NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8 + (double)m->cfg.router_dim * m->d * 4, [&] {
+                    return launch_gate_mlp(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
+                                           X.router_w1, X.router_b1, X.router_w2, m->cfg.router_dim, X.bias, d_unif,
+                                           sg, m->router_hid, m->d_w, m->d_stop, m->st);
+                }, "nv::k_router_hidden + nv::k_router_out"));
+            } else {
+                NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
+                    return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
+                                       m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
+                }, "nv::k_gate"));
+            }
             NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
             NV_HIP(m, hipStreamSynchronize(m->st));
             m->stage_busy = false;
@@ -1177,44 +1357,15 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
             stopping = active;
             active.clear();
         }
-        if (!stopping.empty()) {
-            // exit RMSNorm + the exit's own LM head for the stopping sequences, logits into
-            // row `seq` of the logits buffer, then the inverse-CDF draw
-            char* hl = m->h_headlist;
-            const int ns = (int)stopping.size();
-            for (int j = 0; j < ns; ++j) {
-                const int i = stopping[j];
-                exit_of[i] = sg + 1;
-                nv_model::lseqs(hl)[j] = i;
-                m->lrows(hl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
-                m->lorows(hl)[j] = RowInfo{i, i, 0, 0};
-            }
-            NV_HIP(m, hipMemcpyAsync(m->d_headlist, hl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
-            GemmArgs g{};
-            g.A = m->Hs;
-            g.lda = m->d;
-            g.a_rows = m->lrows(m->d_headlist);
-            g.norm_w = m->exits[sg].norm;
-            g.eps = m->cfg.norm_eps;
-            g.W = m->exits[sg].head;
-            g.N = m->V;
-            g.K = m->d;
-            g.R = ns;
-            g.wbf16 = m->bf16 ? 1 : 0;
-            g.epi = EPI_STORE;
-            g.out = m->logits;
-            g.ldo = m->V;
-            g.o_rows = m->lorows(m->d_headlist);
-            g.head = 1;
-            g.rms_ws = m->rms_ws;
-            g.mfma_min_rows = m->mfma_min_rows;
-            NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
-            NV_TRY(timed(m, NV_TIME_OTHER, (double)ns * m->V * 4, [&] {
-                return launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif,
-                                     m->d_tok_out, m->st);
-            }, "nv::k_sample"));
+        for (int i : stopping) exit_of[i] = sg + 1;
+        if (m->cfg.head_form == 1) {
+            // shared head: every stopping sequence of this step goes through one head pass
+            for (int i : stopping) stopped.push_back(i);
+        } else if (!stopping.empty()) {
+            NV_TRY(run_heads(m, stopping, exit_of, d_unif));
         }
     }
+    if (!stopped.empty()) NV_TRY(run_heads(m, stopped, exit_of, d_unif));
     NV_HIP(m, hipMemcpyAsync(htok_out, m->d_tok_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipMemcpyAsync(hw, m->d_w, (size_t)n * 32, hipMemcpyDeviceToHost, m->st));
     NV_TRY(sync_and_check(m));

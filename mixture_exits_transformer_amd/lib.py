@@ -31,7 +31,8 @@ class nv_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_exits", ctypes.c_int32), ("wdtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
                 ("rope_base", ctypes.c_float), ("exit_layer", ctypes.c_int32 * 4),
-                ("gate_bias", ctypes.c_float * 4)]
+                ("gate_bias", ctypes.c_float * 4), ("head_form", ctypes.c_int32), ("adapter_dim", ctypes.c_int32),
+                ("router_form", ctypes.c_int32), ("router_dim", ctypes.c_int32)]
 
 
 _lib = None

@@ -39,7 +39,7 @@ def test_mem_required(weights_dir):
     assert b > a
 
 
-@pytest.mark.parametrize("damage", ["missing", "magic", "truncated", "shape"])
+@pytest.mark.parametrize("damage", ["missing", "magic", "truncated", "shape", "form"])
 def test_bad_weights_file_is_eio(weights_dir, tmp_path, damage):
     from mixture_exits_transformer_amd import lib
     src = cached_weights(TINY, weights_dir)
@@ -51,6 +51,8 @@ def test_bad_weights_file_is_eio(weights_dir, tmp_path, damage):
         data = data[: len(data) // 2]
     elif damage == "shape":
         data[16:20] = np.int32(100).tobytes()       # d_model not n_heads * head_dim
+    elif damage == "form":
+        data[84:88] = np.int32(2).tobytes()         # no head form 2
     if damage != "missing":
         open(p, "wb").write(data)
     with pytest.raises(lib.NvError) as e:
