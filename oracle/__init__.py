@@ -19,5 +19,8 @@ Parity status per function (pins are in tests/test_oracle_*.py):
                                              forward's exit logits
   sampling and deferral, second form         pinned: chi-square against pi_mix and p_k;
                                              bit-identity with sequential decoding
+  mixture_loss (L_mix, L_compute)            pinned: closed gates / open first gate give the
+                                             textbook forward's cross-entropy and depth 1 / l_1/L;
+                                             Jensen bounds; exp(-nll) equals the sampler's pi_mix
 """
 from . import model, deferred  # noqa: F401

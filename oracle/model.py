@@ -391,6 +391,61 @@ def generate(M: OracleModel, prompt: Sequence[int], U: np.ndarray, max_ctx: int 
     return outs, st
 
 
+# --------------------------------------------------------------------------------------------
+# forward-only training objective [Arch, training part]
+# --------------------------------------------------------------------------------------------
+
+
+@dataclass
+class LossOut:
+    L_mix: float           # mean over positions of -log pi_mix(x_{t+1} | x_{1:t})
+    L_compute: float       # mean over positions of sum_k p_k * l_k / L
+    L_total: float         # L_mix + beta * L_compute
+    nll_mix: np.ndarray    # [n-1] per-position -log pi_mix
+    depth: np.ndarray      # [n-1] per-position expected normalised depth
+    logp: np.ndarray       # [n-1][N_V] log pi_k(x_{t+1})
+    w: np.ndarray          # [n-1][N_V] router outputs
+
+
+def log_softmax_at(z: np.ndarray, y: int) -> float:
+    z = np.asarray(z, dtype=np.float64)
+    mx = float(np.max(z))
+    return float(z[y] - mx - math.log(float(np.sum(np.exp(z - mx)))))
+
+
+def mixture_loss(M: OracleModel, tokens: Sequence[int], beta: float = 0.0) -> LossOut:
+    """The mixture objective on a token sequence, forward only: positions t = 0..n-2 run
+    every layer (a causal chunk), each exit k gives w_k and log pi_k(x_{t+1}); the
+    stick-breaking p_k mix them: L_mix is the cross-entropy of pi_mix and L_compute the
+    expected exit depth l_k / L, both averaged over the n-1 positions."""
+    tokens = [int(t) for t in tokens]
+    n = len(tokens)
+    r = n - 1
+    kv = KVCache(M, r)
+    X = np.asarray(M.embed[np.asarray(tokens[:r], dtype=np.int64)], dtype=np.float64)
+    pos = np.arange(r)
+    logp = np.zeros((r, M.n_exits))
+    w = np.zeros((r, M.n_exits))
+    k = 0
+    for l in range(M.L):
+        X = layer_rows(M, l, X, pos, kv)
+        if l + 1 == M.exit_layers[k]:
+            for i in range(r):
+                w[i, k] = gate(M, k, X[i])
+                logp[i, k] = log_softmax_at(head_logits(M, k, X[i]), tokens[i + 1])
+            k += 1
+    nll = np.zeros(r)
+    depth = np.zeros(r)
+    for i in range(r):
+        p = exit_probs(list(w[i]))
+        terms = [math.log(p[j]) + logp[i, j] for j in range(M.n_exits) if p[j] > 0.0]
+        mx = max(terms)
+        nll[i] = -(mx + math.log(sum(math.exp(t - mx) for t in terms)))
+        depth[i] = sum(p[j] * M.exit_layers[j] / M.L for j in range(M.n_exits))
+    L_mix, L_comp = float(np.mean(nll)), float(np.mean(depth))
+    return LossOut(L_mix, L_comp, L_mix + beta * L_comp, nll, depth, logp, w)
+
+
 def boundary_distances(o: StepOut, token: int, exit_: int) -> dict:
     """How close the draw that produced (token, exit_) sits to this step's decision
     boundaries: per walked gate |u_k - w_k|, and for the token the distance of u_4
