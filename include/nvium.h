@@ -117,6 +117,23 @@ nv_status nv_step(nv_model *m, const float *uniforms, int32_t *tokens_out, int32
 nv_status nv_step_forced(nv_model *m, const float *uniforms, const int32_t *next_inputs,
                          int32_t *tokens_out, int32_t *exits_out);
 
+/* The mixture objective on a token sequence, forward only (gist.science technical
+ * summary, section 2 "Methodik", part "Training": L_total = L_mix + beta * L_compute;
+ * L_mix is the cross-entropy of pi_mix, L_compute the expected exit depth).
+ * Sequence `seq` is prefilled with tokens[0..n-1] exactly as nv_prefill does
+ * (afterwards it can decode), and after each segment every position t = 0..n-2
+ * evaluates that exit's router w_k and log pi_k(tokens[t+1]).
+ *   out      [3] host float64: L_mix = mean_t -log sum_k p_k pi_k(tokens[t+1]),
+ *            L_compute = mean_t sum_k p_k l_k / L (l_k = exit k's last layer),
+ *            L_total = L_mix + beta * L_compute.
+ *   per_pos  NULL, or host float64 [n-1][10]: w_1..w_4 (w_4 = 1), log pi_1..4 of
+ *            the target, -log pi_mix of the target, expected depth.
+ * Errors: NV_EINVAL (seq out of range, NULL tokens or out, n < 2, token >= vocab,
+ * beta not finite), NV_ECAPACITY (n > max_ctx), NV_EDEVICE.  On error the
+ * sequence must be prefilled again before it decodes. */
+nv_status nv_mixture_loss(nv_model *m, int32_t seq, const int32_t *tokens, int32_t n, double beta,
+                          double *out, double *per_pos);
+
 /* Run every deferred segment of sequence `seq` (-1: all prefilled sequences)
  * over all consumed positions, with no gates and no heads.  Afterwards every
  * layer's KV is complete for every consumed position.  A second flush is a

@@ -94,6 +94,7 @@ hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, 
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
                                const float* part_ml, const float* part_o, float* out,
                                hipStream_t st);
+// Gates write w_out[seqs[i] * 4 + ucol]; with uniforms null they take no stop decision.
 hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d,
                        const float* gw, float bias, const float* uniforms, int ucol,
                        double* w_out, int* stop_out, hipStream_t st);
@@ -106,6 +107,18 @@ hipError_t launch_gate_mlp(const RowInfo* rows, const int* seqs, int n, const fl
                            double* hid, double* w_out, int* stop_out, hipStream_t st);
 // dst row i = Hs row rows[i].hrow (d floats each).
 hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst, hipStream_t st);
+// out[i * ostride + ocol] = log softmax(logits row i)[targets[i]] (float64).
+hipError_t launch_xent(const float* logits, int64_t ld, int n, int V, const int* targets, double* out, int ostride,
+                       int ocol, hipStream_t st);
+// Exit layers l_k and the layer count L, for the expected depth sum_k p_k l_k / L.
+struct ExitDepths {
+    int layer[4];
+    int L;
+};
+// Rows i < n of w and lp are [n][4] (router outputs, log pi_k of the target); writes
+// w[i][3] = 1, the per-row mixture NLL and expected depth, and their means to sums[0..1].
+hipError_t launch_loss_reduce(double* w, const double* lp, int n, ExitDepths dep, double* nll, double* depth,
+                              double* sums, hipStream_t st);
 hipError_t init_kernel_attributes();
 // Timing: the next launch stamps `start` at its start; every launch stamps `stop` at its
 // end, until cleared with (nullptr, nullptr).

@@ -1435,7 +1435,7 @@ __global__ __launch_bounds__(256) void k_gate(const RowInfo* rows, const int* se
         }
         const int seq = seqs[i];
         w_out[seq * 4 + ucol] = w;
-        stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+        if (uniforms) stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
     }
 }
 
@@ -1504,7 +1504,7 @@ __global__ __launch_bounds__(64) void k_router_out(const int* seqs, int n, const
         }
         const int seq = seqs[i];
         w_out[seq * 4 + ucol] = w;
-        stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+        if (uniforms) stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
     }
 }
 
@@ -1530,6 +1530,94 @@ __global__ __launch_bounds__(256) void k_copy_rows(const RowInfo* rows, int n, c
 hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     NV_LAUNCH(k_copy_rows, dim3(n), dim3(256), 0, st, rows, n, Hs, d, dst);
+    return hipGetLastError();
+}
+
+// Log-probability of the target token under softmax(z) for each row: z[y] - max z -
+// log sum exp(z - max z), exponentials in float32 summed in float64 (as the sampler).
+__global__ __launch_bounds__(1024) void k_xent(const float* logits, int64_t ld, int n, int V, const int* targets,
+                                               double* out, int ostride, int ocol) {
+    __shared__ float smax[16];
+    __shared__ double ssum[16];
+    const int i = blockIdx.x;
+    if (i >= n) return;
+    const float* z = logits + (int64_t)i * ld;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+    float mx = -INFINITY;
+    for (int k = t; k < V; k += blockDim.x) mx = fmaxf(mx, z[k]);
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    mx = smax[0];
+    for (int w = 1; w < nw; ++w) mx = fmaxf(mx, smax[w]);
+    double acc = 0.0;
+    for (int k = t; k < V; k += blockDim.x) acc += (double)expf(z[k] - mx);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) ssum[wave] = acc;
+    __syncthreads();
+    if (t == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < nw; ++w) tot += ssum[w];
+        out[(int64_t)i * ostride + ocol] = (double)z[targets[i]] - (double)mx - log(tot);
+    }
+}
+
+hipError_t launch_xent(const float* logits, int64_t ld, int n, int V, const int* targets, double* out, int ostride,
+                       int ocol, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    NV_LAUNCH(k_xent, dim3(n), dim3(1024), 0, st, logits, ld, n, V, targets, out, ostride, ocol);
+    return hipGetLastError();
+}
+
+// Mixture objective per row (one block, fixed reduction order): the last exit's router
+// output is 1; p_k = w_k prod_{j<k} (1 - w_j); nll = -log sum_k p_k pi_k(y), a log-sum-exp
+// over the exits with p_k > 0; depth = sum_k p_k l_k / L.  sums = {mean nll, mean depth}.
+__global__ __launch_bounds__(256) void k_loss_reduce(double* w, const double* lp, int n, ExitDepths dep, double* nll,
+                                                     double* depth, double* sums) {
+    __shared__ double sa[256], sb[256];
+    const int t = threadIdx.x;
+    double an = 0.0, ad = 0.0;
+    for (int i = t; i < n; i += blockDim.x) {
+        w[(int64_t)i * 4 + 3] = 1.0;
+        double p[4], rest = 1.0;
+        for (int k = 0; k < 4; ++k) {
+            p[k] = w[(int64_t)i * 4 + k] * rest;
+            rest *= 1.0 - w[(int64_t)i * 4 + k];
+        }
+        double mx = -INFINITY;
+        for (int k = 0; k < 4; ++k)
+            if (p[k] > 0.0) mx = fmax(mx, log(p[k]) + lp[(int64_t)i * 4 + k]);
+        double se = 0.0, dp = 0.0;
+        for (int k = 0; k < 4; ++k) {
+            if (p[k] > 0.0) se += exp(log(p[k]) + lp[(int64_t)i * 4 + k] - mx);
+            dp += p[k] * (double)dep.layer[k] / (double)dep.L;
+        }
+        const double v = -(mx + log(se));
+        nll[i] = v;
+        depth[i] = dp;
+        an += v;
+        ad += dp;
+    }
+    sa[t] = an;
+    sb[t] = ad;
+    __syncthreads();
+    for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+        if (t < o) {
+            sa[t] += sa[t + o];
+            sb[t] += sb[t + o];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        sums[0] = n > 0 ? sa[0] / n : 0.0;
+        sums[1] = n > 0 ? sb[0] / n : 0.0;
+    }
+}
+
+hipError_t launch_loss_reduce(double* w, const double* lp, int n, ExitDepths dep, double* nll, double* depth,
+                              double* sums, hipStream_t st) {
+    NV_LAUNCH(k_loss_reduce, dim3(1), dim3(256), 0, st, w, lp, n, dep, nll, depth, sums);
     return hipGetLastError();
 }
 

@@ -79,6 +79,8 @@ struct Plan {
     size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0;
     size_t tables = 0, small = 0, logits = 0, router_hid = 0;
     size_t seg = 0;     // persistent segment kernel: tagged exchange buffers, counters, layer table
+    int loss_ch = 0;    // mixture objective: rows per head pass
+    size_t loss = 0;    // its logits, per-row router outputs / log-probabilities / losses, row tables
     size_t total = 0;
 };
 
@@ -179,7 +181,11 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
-    p.total = p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head + p.hidden + p.kv +
+    p.loss_ch = (int)std::min<size_t>(128, rmax);
+    p.loss = align_up((size_t)p.loss_ch * V * 4) + 4 * align_up((size_t)max_ctx * 32) + align_up(64) +
+             2 * align_up((size_t)max_ctx * 4) + align_up((size_t)max_ctx * sizeof(RowInfo)) +
+             align_up((size_t)p.loss_ch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
+    p.total = p.loss + p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head + p.hidden + p.kv +
               p.rope + p.qbuf + p.attn_o +
               p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
     return p;
@@ -213,6 +219,14 @@ struct nv_model {
     float* part_o = nullptr;
     float* rms_ws = nullptr;   // [R_max] per-row inverse RMS for the matrix-core GEMM
     double* router_hid = nullptr;   // [max_batch][router_dim] router MLP hidden units
+    // mixture objective over one sequence of up to max_ctx tokens (rows = positions)
+    float* loss_logits = nullptr;   // [loss_ch][V]
+    double *loss_w = nullptr, *loss_lp = nullptr;       // [max_ctx][4]
+    double *loss_nll = nullptr, *loss_depth = nullptr;  // [max_ctx] (allocated [max_ctx][4])
+    double* loss_sums = nullptr;    // [2] means
+    int *loss_tgt = nullptr, *loss_ids = nullptr;       // [max_ctx] target tokens, row ids 0..n-1
+    RowInfo* loss_rows = nullptr;   // [max_ctx]
+    double* loss_hid = nullptr;     // [loss_ch][router_dim]
     int mfma_min_rows = 9;     // chunks of at least this many rows use the matrix cores
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
@@ -1027,6 +1041,16 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->d_tok_out = (int*)m->take((size_t)max_batch * 4);
     m->logits = (float*)m->take(P.logits);
     m->router_hid = (double*)m->take(P.router_hid);
+    m->loss_logits = (float*)m->take((size_t)P.loss_ch * m->V * 4);
+    m->loss_w = (double*)m->take((size_t)max_ctx * 32);
+    m->loss_lp = (double*)m->take((size_t)max_ctx * 32);
+    m->loss_nll = (double*)m->take((size_t)max_ctx * 32);
+    m->loss_depth = (double*)m->take((size_t)max_ctx * 32);
+    m->loss_sums = (double*)m->take(64);
+    m->loss_tgt = (int*)m->take((size_t)max_ctx * 4);
+    m->loss_ids = (int*)m->take((size_t)max_ctx * 4);
+    m->loss_rows = (RowInfo*)m->take((size_t)max_ctx * sizeof(RowInfo));
+    m->loss_hid = (double*)m->take((size_t)P.loss_ch * (m->cfg.router_dim > 0 ? m->cfg.router_dim : 1) * 8);
     m->seg_base = m->take(P.seg);
     if (m->arena_off > P.total) return fail(m, NV_ECAPACITY, "internal: arena plan too small");
 
@@ -1393,6 +1417,171 @@ nv_status nv_step_forced(nv_model* m, const float* uniforms, const int32_t* next
                          int32_t* exits_out) {
     if (!next_inputs) return m ? fail(m, NV_EINVAL, "null next_inputs") : NV_EINVAL;
     return step_impl(m, uniforms, next_inputs, tokens_out, exits_out);
+}
+
+// Mixture objective, rows o..o+k-1 of the loss pass after segment sg: the exit's router
+// output for each row, its logits (own head, or adapter + shared head) into the loss logits
+// workspace and log pi_k of each row's target token.
+static nv_status loss_exit(nv_model* m, int sg, int o, int k) {
+    const ExitPtrs& X = m->exits[sg];
+    const RowInfo* rows = m->loss_rows + o;
+    if (sg < kMaxExits - 1) {
+        if (m->cfg.router_form == 1) {
+            NV_TRY(timed(m, NV_TIME_OTHER, (double)k * m->d * 8 + (double)m->cfg.router_dim * m->d * 4, [&] {
+                return launch_gate_mlp(rows, m->loss_ids + o, k, m->Hs, m->d, X.router_w1, X.router_b1, X.router_w2,
+                                       m->cfg.router_dim, X.bias, nullptr, sg, m->loss_hid, m->loss_w, nullptr,
+                                       m->st);
+            }, "nv::k_router_hidden + nv::k_router_out"));
+        } else {
+            NV_TRY(timed(m, NV_TIME_OTHER, (double)k * m->d * 8, [&] {
+                return launch_gate(rows, m->loss_ids + o, k, m->Hs, m->d, X.gate_w, X.bias, nullptr, sg, m->loss_w,
+                                   nullptr, m->st);
+            }, "nv::k_gate"));
+        }
+    }
+    GemmArgs g{};
+    g.eps = m->cfg.norm_eps;
+    g.wbf16 = m->bf16 ? 1 : 0;
+    g.rms_ws = m->rms_ws;
+    g.mfma_min_rows = m->mfma_min_rows;
+    const int d = m->d;
+    if (m->cfg.head_form == 1) {
+        float* A = m->attn_o;   // [k][d] gathered rows, then adapter outputs
+        NV_TRY(timed(m, NV_TIME_EXIT_HEAD, (double)k * d * 8, [&] {
+            return launch_copy_rows(rows, k, m->Hs, d, A, m->st);
+        }, "nv::k_copy_rows"));
+        if (sg < kMaxExits - 1) {
+            const int r = m->cfg.adapter_dim;
+            GemmArgs a = g;
+            a.A = A;
+            a.lda = d;
+            a.W = X.adapter_down;
+            a.N = r;
+            a.K = d;
+            a.R = k;
+            a.epi = EPI_SILU;
+            a.out = m->mlp;
+            a.ldo = r;
+            NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, a), [&] { return launch_gemm(a, m->st); }));
+            GemmArgs b = g;
+            b.A = m->mlp;
+            b.lda = r;
+            b.W = X.adapter_up;
+            b.N = d;
+            b.K = r;
+            b.R = k;
+            b.epi = EPI_RESID;
+            b.out = A;
+            b.ldo = d;
+            NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, b), [&] { return launch_gemm(b, m->st); }));
+        }
+        g.A = A;
+        g.lda = d;
+    } else {
+        g.A = m->Hs;
+        g.lda = d;
+        g.a_rows = rows;
+    }
+    g.norm_w = X.norm;
+    g.W = X.head;
+    g.N = m->V;
+    g.K = d;
+    g.R = k;
+    g.epi = EPI_STORE;
+    g.out = m->loss_logits;
+    g.ldo = m->V;
+    g.head = 1;
+    NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+    NV_TRY(timed(m, NV_TIME_OTHER, (double)k * m->V * 4, [&] {
+        return launch_xent(m->loss_logits, m->V, k, m->V, m->loss_tgt + o, m->loss_lp + (int64_t)o * 4, 4, sg, m->st);
+    }, "nv::k_xent"));
+    return NV_OK;
+}
+
+nv_status nv_mixture_loss(nv_model* m, int32_t seq, const int32_t* tokens, int32_t n, double beta, double* out,
+                          double* per_pos) {
+    nv_status s = check_seq(m, seq);
+    if (s != NV_OK) return s;
+    if (!tokens || !out || n < 2) return fail(m, NV_EINVAL, "the mixture objective needs out and at least two tokens");
+    if (n > m->max_ctx) return fail(m, NV_ECAPACITY, "token sequence longer than max_ctx");
+    if (!std::isfinite(beta)) return fail(m, NV_EINVAL, "beta is not finite");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->V) return fail(m, NV_EINVAL, "token id out of range");
+    const int np = n - 1;
+    // row tables for the whole pass: rows, row ids, target tokens
+    if ((s = stage_sync(m)) != NV_OK) return s;
+    std::vector<RowInfo> hr(np);
+    std::vector<int> ids(np), tgt(np);
+    for (int i = 0; i < np; ++i) {
+        hr[i] = RowInfo{seq * m->max_ctx + i, seq, i, 0};
+        ids[i] = i;
+        tgt[i] = tokens[i + 1];
+    }
+    NV_HIP(m, hipMemcpyAsync(m->loss_rows, hr.data(), sizeof(RowInfo) * np, hipMemcpyHostToDevice, m->st));
+    NV_HIP(m, hipMemcpyAsync(m->loss_ids, ids.data(), 4 * (size_t)np, hipMemcpyHostToDevice, m->st));
+    NV_HIP(m, hipMemcpyAsync(m->loss_tgt, tgt.data(), 4 * (size_t)np, hipMemcpyHostToDevice, m->st));
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    // the prefill of the first n-1 tokens, with every exit's router and head after its segment
+    SeqHost& S = m->seqs[seq];
+    S = SeqHost();
+    S.live = true;
+    S.pending = tokens[n - 1];
+    const int cap = m->plan.R_max;
+    for (int o = 0; o < np; o += cap) {
+        const int k = std::min(cap, np - o);
+        if ((s = stage_sync(m)) != NV_OK) return s;
+        int* ht = (int*)m->h_stage;
+        for (int i = 0; i < k; ++i) ht[i] = tokens[o + i];
+        NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, 4 * (size_t)k, hipMemcpyHostToDevice, m->st));
+        m->stage_busy = true;
+        NV_TRY(timed(m, NV_TIME_OTHER, (double)k * m->d * (m->plan.es + 4), [&] {
+            return launch_embed((const int*)m->d_tables, m->loss_rows + o, k, m->embed, m->bf16, m->Hs, m->d, m->st);
+        }, "nv::k_embed"));
+    }
+    const std::vector<Chunk> ch{{seq, 0, np}};
+    for (int sg = 0; sg < kMaxExits; ++sg) {
+        if ((s = run_chunks(m, sg, ch)) != NV_OK) return s;
+        for (int o = 0; o < np; o += m->plan.loss_ch)
+            NV_TRY(loss_exit(m, sg, o, std::min(m->plan.loss_ch, np - o)));
+    }
+    ExitDepths dep{};
+    for (int k = 0; k < kMaxExits; ++k) dep.layer[k] = m->cfg.exit_layer[k];
+    dep.L = m->L;
+    NV_TRY(timed(m, NV_TIME_OTHER, (double)np * 80, [&] {
+        return launch_loss_reduce(m->loss_w, m->loss_lp, np, dep, m->loss_nll, m->loss_depth, m->loss_sums, m->st);
+    }, "nv::k_loss_reduce"));
+    double sums[2];
+    NV_HIP(m, hipMemcpyAsync(sums, m->loss_sums, 16, hipMemcpyDeviceToHost, m->st));
+    std::vector<double> pw, plp, pn, pd;
+    if (per_pos) {
+        pw.resize((size_t)np * 4);
+        plp.resize((size_t)np * 4);
+        pn.resize(np);
+        pd.resize(np);
+        NV_HIP(m, hipMemcpyAsync(pw.data(), m->loss_w, (size_t)np * 32, hipMemcpyDeviceToHost, m->st));
+        NV_HIP(m, hipMemcpyAsync(plp.data(), m->loss_lp, (size_t)np * 32, hipMemcpyDeviceToHost, m->st));
+        NV_HIP(m, hipMemcpyAsync(pn.data(), m->loss_nll, (size_t)np * 8, hipMemcpyDeviceToHost, m->st));
+        NV_HIP(m, hipMemcpyAsync(pd.data(), m->loss_depth, (size_t)np * 8, hipMemcpyDeviceToHost, m->st));
+    }
+    NV_TRY(sync_and_check(m));
+    if (m->timing) NV_TRY(resolve_timing(m));
+    S.n = np;
+    for (int k = 0; k < kMaxExits; ++k) S.f[k] = np;
+    for (int k = 0; k < 4; ++k) m->last_w[(size_t)seq * 4 + k] = NAN;
+    out[0] = sums[0];
+    out[1] = sums[1];
+    out[2] = sums[0] + beta * sums[1];
+    if (per_pos)
+        for (int i = 0; i < np; ++i) {
+            double* r = per_pos + (size_t)i * 10;
+            for (int k = 0; k < 4; ++k) {
+                r[k] = pw[(size_t)i * 4 + k];
+                r[4 + k] = plp[(size_t)i * 4 + k];
+            }
+            r[8] = pn[i];
+            r[9] = pd[i];
+        }
+    return NV_OK;
 }
 
 nv_status nv_flush(nv_model* m, int32_t seq) {

@@ -51,6 +51,7 @@ _SIGS = {
     "nv_prefill": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, ctypes.c_int32]),
     "nv_step": (ctypes.c_int, [_P, _F32P, _I32P, _I32P]),
     "nv_step_forced": (ctypes.c_int, [_P, _F32P, _I32P, _I32P, _I32P]),
+    "nv_mixture_loss": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_double, _F64P, _F64P]),
     "nv_flush": (ctypes.c_int, [_P, ctypes.c_int32]),
     "nv_debug_frontiers": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, _I32P]),
     "nv_debug_logits": (ctypes.c_int, [_P, ctypes.c_int32, _F32P]),
@@ -179,6 +180,18 @@ def nv_step_forced(h: Handle, uniforms, next_inputs) -> Tuple[np.ndarray, np.nda
     _check(h.ptr, library().nv_step_forced(h.ptr, _ptr(u, ctypes.c_float), _ptr(f, ctypes.c_int32),
                                            _ptr(tok, ctypes.c_int32), _ptr(ex, ctypes.c_int32)))
     return tok, ex
+
+
+def nv_mixture_loss(h: Handle, seq: int, tokens, beta: float = 0.0, per_pos: bool = False):
+    """(L_mix, L_compute, L_total), and with per_pos the [n-1][10] rows w_1..4,
+    log pi_1..4 of the target, -log pi_mix, expected depth.  Prefills `seq` with tokens."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = np.empty(3, np.float64)
+    pp = np.empty((max(len(t) - 1, 0), 10), np.float64) if per_pos else None
+    _check(h.ptr, library().nv_mixture_loss(h.ptr, seq, _ptr(t, ctypes.c_int32), len(t), float(beta),
+                                            _ptr(out, ctypes.c_double),
+                                            _ptr(pp, ctypes.c_double) if per_pos else None))
+    return (tuple(float(x) for x in out), pp) if per_pos else tuple(float(x) for x in out)
 
 
 def nv_flush(h: Handle, seq: int = -1) -> None:

@@ -67,3 +67,4 @@ def test_null_arguments_are_einval():
     assert L.nv_load(None, 1, 16, None, 0, None, lib.ctypes.byref(out)) == lib.NV_EINVAL
     assert L.nv_step(None, None, None, None) == lib.NV_EINVAL
     assert L.nv_flush(None, 0) == lib.NV_EINVAL
+    assert L.nv_mixture_loss(None, 0, None, 0, 0.0, None, None) == lib.NV_EINVAL
