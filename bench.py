@@ -14,6 +14,11 @@ Beside it: the same kernels with every intermediate gate closed (all tokens exit
 wall-clock stamps per block for the decode GEMMs and attention, HIP events for the
 rest; roofline of the dominant block GEMM against 8 TB/s), and the CPU oracle timed
 on a bounded sample of the same decode.
+
+Workload "L" (--workload L) times the mixture objective instead: a step is one
+nv_mixture_loss over a 2048-token sequence on the same 1.5B model (full-depth causal
+pass, every exit's router and head at every position); `value` = scored positions/s,
+roofline of the dominant block GEMM against the bf16 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("mixture_exits_transformer_amd/csrc/nv_kernels.hip",
                   "mixture_exits_transformer_amd/csrc/nv_segment.hip",
                   "mixture_exits_transformer_amd/csrc/nv_device.h",
@@ -118,12 +124,103 @@ def cpu_baseline(wl, path, prompt, U, budget_s):
                       f"{dt:.1f} s"}
 
 
+def loss_cpu_baseline(path, tokens, budget_tokens):
+    """The oracle's mixture_loss on the first `budget_tokens` tokens of the sequence."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import model as om
+    M = om.OracleModel(path)
+    t0 = time.perf_counter()
+    om.mixture_loss(M, tokens[:budget_tokens], 0.5)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": (budget_tokens - 1) / dt, "unit": "scored tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"mixture_loss over the first {budget_tokens} tokens ({budget_tokens - 1} positions, every "
+                      f"exit's router and head) of the same sequence, {dt:.1f} s"}
+
+
+def bench_loss(args, wl):
+    """Mixture objective: a step is one nv_mixture_loss over the whole sequence (the
+    full-depth causal pass over n-1 positions, each exit's router and head at every
+    position, log-softmax at the target, the mixture and the means)."""
+    import torch
+
+    from mixture_exits_transformer_amd import lib
+    from synth import cached_weights, prompts
+    tokens = prompts(wl)[0]
+    n = len(tokens)
+    steps = args.steps if args.steps is not None else 10
+    warmup = args.warmup if args.warmup is not None else 2
+    path = cached_weights(wl.model)
+    h = lib.nv_load(path, 1, n)
+    for _ in range(warmup):
+        lib.nv_mixture_loss(h, 0, tokens, 0.5)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        L = lib.nv_mixture_loss(h, 0, tokens, 0.5)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    lib.nv_timing_enable(h, True)
+    lib.nv_mixture_loss(h, 0, tokens, 0.5)
+    tim = lib.nv_timing_read(h)
+    ker = lib.nv_timing_kernels(h)
+    lib.nv_timing_enable(h, False)
+    lib.nv_free(h)
+    m = wl.model
+    d, F, Lr, V, r = m.d_model, m.ffn, m.n_layers, m.vocab, n - 1
+    # dominant kernel: of the block GEMMs of the full-depth pass, those with the RMSNorm
+    # folded in (QKV, gate/up: "k_row_rms + ...") and those without (O, down) are timed
+    # under two names; their algorithmic FLOPs are 2 r L (3d^2 + 2Fd) and 2 r L (d^2 + Fd).
+    gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
+    assert len(gemms) == 2, [k[4] for k in gemms]
+    _, nl, ms, by, kname = gemms[0]
+    normed = "k_row_rms" in kname
+    flops = 2.0 * r * Lr * ((3 * d * d + 2 * F * d) if normed else (d * d + F * d))
+    achieved = flops / (ms * 1e-3) / 1e12
+    all_flops = 2.0 * r * Lr * (4 * d * d + 3 * d * F)
+    counted = counted_traffic(kname)
+    top = sorted(ker, key=lambda k: -k[2])[:8]
+    total_flops = all_flops + 2.0 * r * 4 * V * d + 2.0 * Lr * m.n_heads * m.head_dim * r * (r + 1)
+    out = {
+        "metric": "mixture-objective scored tokens/s (forward L_mix + beta L_compute), 1.5B bf16",
+        "value": round(steps * r / dt, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(dt / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m.wdtype,
+        "data": "synthetic: uniform-random token ids (seed 1), random-init N(0,0.02) weights",
+        "config": {"workload": f"{wl.name}: {wl.note}", "batch": 1, "tokens": n, "positions": r},
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": MFMA_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_TFLOPS, 4),
+                     "traffic": counted[0] if counted else None,
+                     "traffic_source": counted[1] if counted else None,
+                     "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
+                     "flops_per_launch": round(flops / max(nl, 1))},
+        "block_gemm_all_TFLOPs": round(all_flops / (tim["block_gemm"][0] * 1e-3) / 1e12, 1),
+        "pass_TFLOPs": round(total_flops / (dt / steps) / 1e12, 1),
+        "L": [round(x, 6) for x in L],
+        "top_kernels": [{"kernel": k[4], "class": k[0], "launches": k[1],
+                         "avg_us": round(k[2] / max(k[1], 1) * 1e3, 3)} for k in top],
+        "kernel_classes_ms_per_step": {k: round(v[0], 4) for k, v in tim.items()},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = loss_cpu_baseline(path, tokens, args.cpu_loss_tokens)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="A")
+    ap.add_argument("--steps", type=int, default=None, help="decode steps (default 512); loss passes (10)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 16; loss passes 2)")
+    ap.add_argument("--workload", default="A", help="A, B, D, E (decode, batch 1) or L (mixture objective)")
+    ap.add_argument("--cpu-loss-tokens", type=int, default=40, help="oracle sample for workload L")
     ap.add_argument("--no-baseline", action="store_true", help="skip the exit-4-forced run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -145,8 +242,11 @@ def main():
 
     torch.cuda.set_device(0)
     wl = workload(args.workload)
+    if wl.name == "L":
+        return bench_loss(args, wl)
     assert wl.batch == 1, "bench.py times the batch-1 workloads"
-    steps, warmup = args.steps, args.warmup
+    steps = args.steps if args.steps is not None else 512
+    warmup = args.warmup if args.warmup is not None else 16
     prompt = prompts(wl)[0]
     U = uniforms(wl, steps=max(steps, warmup))[:, 0, :]
     max_ctx = len(prompt) + max(steps, warmup)

@@ -120,6 +120,9 @@ WORKLOADS = {
                   prompt_len=512, decode_steps=512,
                   note="1.5B bf16, shared LM head + adapters (192), router MLPs (64), batch 1, prompt 512, "
                        "decode 512, exit mass ~[.4,.25,.2,.15]"),
+    "L": Workload("L", M15B, batch=1, prompt_len=2048, decode_steps=0,
+                  note="mixture objective (L_mix + beta L_compute, forward) over one 2048-token sequence, "
+                       "1.5B bf16, every exit's router and head at every position"),
 }
 
 
