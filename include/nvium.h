@@ -117,6 +117,36 @@ nv_status nv_step(nv_model *m, const float *uniforms, int32_t *tokens_out, int32
 nv_status nv_step_forced(nv_model *m, const float *uniforms, const int32_t *next_inputs,
                          int32_t *tokens_out, int32_t *exits_out);
 
+/* Scheduling policies of nv_generate. */
+#define NV_SCHED_LOCKSTEP 0  /* rounds: every listed sequence's token runs segment 1, then the
+                                ones still going run segment 2, ...; one token per sequence per
+                                round (what repeated nv_step calls do) */
+#define NV_SCHED_GREEDY 1    /* each tick runs the segment with the highest
+                                (waiting sequences + half the longest wait there, in ticks);
+                                ties go to the deeper segment */
+
+/* Batched decoding where sequences advance through the segments independently (the
+ * gptget.net summary's limitations section names the batched-inference strategy as
+ * needing change, since tokens of one batch are sampled at different exits).  Sequences seqs[0..n_seq-1]
+ * (distinct, prefilled, in any order and any subset of the handle's slots) each
+ * generate n_tokens tokens.  A tick runs one segment for every listed sequence whose
+ * current token waits there, each with its deferred rows as one causal chunk, then
+ * that segment's gate; sequences that stop get their exit head and draw, and their
+ * next token enters segment 1 at a later tick.  `policy` chooses the tick's segment.
+ *   uniforms   [n_seq][n_tokens][4] float32 in [0,1): token t of sequence seqs[i] uses
+ *              uniforms[i][t] exactly as nv_step uses its row (gates walked with
+ *              u[0..2], inverse CDF with u[3]).
+ *   tokens_out [n_seq][n_tokens], exits_out [n_seq][n_tokens] (1..4).
+ * Each sequence's tokens and exits are those of n_tokens nv_step calls with the same
+ * uniforms (the kernels may group rows differently, so floating-point results can
+ * differ in the last bits).  The last token becomes the pending input.  nv_debug_gates
+ * reports NaN afterwards for the listed sequences.
+ * Errors: NV_EINVAL (NULL pointers, n_seq outside 1..max_batch, index out of range or
+ * repeated, n_tokens < 0, bad uniform, unknown policy), NV_ESTATE (a listed sequence is
+ * not prefilled), NV_ECAPACITY (a sequence would pass max_ctx), NV_EDEVICE. */
+nv_status nv_generate(nv_model *m, const int32_t *seqs, int32_t n_seq, int32_t n_tokens,
+                      const float *uniforms, int32_t policy, int32_t *tokens_out, int32_t *exits_out);
+
 /* The mixture objective on a token sequence, forward only (gist.science technical
  * summary, section 2 "Methodik", part "Training": L_total = L_mix + beta * L_compute;
  * L_mix is the cross-entropy of pi_mix, L_compute the expected exit depth).

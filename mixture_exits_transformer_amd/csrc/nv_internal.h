@@ -77,8 +77,9 @@ struct CombineInfo {
 
 // Launch wrappers (nv_kernels.hip).
 hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStream_t st);
+// Hs row rows[i].hrow = embedding of tokens[i] (by_seq: of tokens[rows[i].seq]).
 hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const void* E, int wbf16,
-                        float* Hs, int d, hipStream_t st);
+                        float* Hs, int d, hipStream_t st, int by_seq = 0);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // Decode-sized row blocks (<= ATTN_DEC_ROWS rows): each item is one split of one
 // (row block, head); split partials are merged by launch_attn_combine.

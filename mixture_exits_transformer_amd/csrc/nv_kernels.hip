@@ -75,10 +75,10 @@ hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStre
 // ------------------------------------------------------------------------------------------
 
 __global__ void k_embed(const int* tokens, const RowInfo* rows, int n, const void* E, int wbf16, float* Hs,
-                        int d) {
+                        int d, int by_seq) {
     int r = blockIdx.x;
     if (r >= n) return;
-    int64_t src = (int64_t)tokens[r] * d;
+    int64_t src = (int64_t)tokens[by_seq ? rows[r].seq : r] * d;
     float* dst = Hs + (int64_t)rows[r].hrow * d;
     for (int k = threadIdx.x; k < d; k += blockDim.x)
         dst[k] = wbf16 ? __uint_as_float(((uint32_t)((const uint16_t*)E)[src + k]) << 16)
@@ -86,9 +86,9 @@ __global__ void k_embed(const int* tokens, const RowInfo* rows, int n, const voi
 }
 
 hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const void* E, int wbf16, float* Hs, int d,
-                        hipStream_t st) {
+                        hipStream_t st, int by_seq) {
     if (n <= 0) return hipSuccess;
-    NV_LAUNCH(k_embed, dim3(n), dim3(256), 0, st, tokens, rows, n, E, wbf16, Hs, d);
+    NV_LAUNCH(k_embed, dim3(n), dim3(256), 0, st, tokens, rows, n, E, wbf16, Hs, d, by_seq);
     return hipGetLastError();
 }
 

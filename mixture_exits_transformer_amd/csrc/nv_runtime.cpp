@@ -67,6 +67,7 @@ struct Chunk {
 };
 
 constexpr size_t kEventPairs = 8192;
+constexpr int kRing = 4;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -253,10 +254,16 @@ struct nv_model {
     char* h_stage = nullptr;   // pinned; mirrors the device table region
     size_t h_stage_bytes = 0;
     bool stage_busy = false;   // an async copy from h_stage may still be pending
+    // h_headlist has two halves used in turn; a half is busy from its upload until the
+    // next stream synchronisation (a step can launch two head passes with no sync between)
+    bool hl_busy[2] = {false, false};
+    int hl_next = 0;
     char* h_stepblk = nullptr;
     char* h_gatelist = nullptr;
     char* h_headlist = nullptr;
     char* h_out = nullptr;     // pinned: stop flags, tokens, router outputs coming back
+    int* h_ring = nullptr;     // pinned [kRing][max_batch]: sampled tokens coming back (nv_generate)
+    bool sb_busy = false;      // an async copy from h_stepblk may still be pending
 
     size_t stepblk_bytes() const { return (size_t)max_batch * (16 + 4 + sizeof(RowInfo)); }
     size_t list_bytes() const { return (size_t)max_batch * (4 + 2 * sizeof(RowInfo)); }
@@ -420,10 +427,17 @@ double gemm_bytes(const nv_model* m, const GemmArgs& g) {
         if (s_ != NV_OK) return s_;       \
     } while (0)
 
+// The work stream was synchronised: every async copy from a pinned staging buffer is done.
+void stream_synced(nv_model* m) {
+    m->stage_busy = false;
+    m->sb_busy = false;
+    m->hl_busy[0] = m->hl_busy[1] = false;
+}
+
 nv_status stage_sync(nv_model* m) {
     if (m->stage_busy) {
         NV_HIP(m, hipStreamSynchronize(m->st));
-        m->stage_busy = false;
+        stream_synced(m);
     }
     return NV_OK;
 }
@@ -760,7 +774,7 @@ nv_status sync_and_check(nv_model* m) {
     uint32_t* h_err = (uint32_t*)(m->h_out + (size_t)m->max_batch * 48);
     if (m->seg_ran) NV_HIP(m, hipMemcpyAsync(h_err, m->seg_err, 4, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipStreamSynchronize(m->st));
-    m->stage_busy = false;
+    stream_synced(m);
     return seg_check(m, h_err);
 }
 
@@ -893,6 +907,7 @@ void nv_free(nv_model* m) {
     if (m->h_gatelist) (void)hipHostFree(m->h_gatelist);
     if (m->h_headlist) (void)hipHostFree(m->h_headlist);
     if (m->h_out) (void)hipHostFree(m->h_out);
+    if (m->h_ring) (void)hipHostFree(m->h_ring);
     delete m;
 }
 
@@ -1058,8 +1073,9 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     NV_HIP(m, hipHostMalloc((void**)&m->h_stage, m->h_stage_bytes, hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_stepblk, m->stepblk_bytes(), hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_gatelist, m->list_bytes(), hipHostMallocDefault));
-    NV_HIP(m, hipHostMalloc((void**)&m->h_headlist, m->list_bytes(), hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_headlist, 2 * m->list_bytes(), hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_out, (size_t)max_batch * 48 + 16, hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_ring, (size_t)kRing * max_batch * 4, hipHostMallocDefault));
 
     // weights: file tensors -> pinned bounce buffer -> device (repacking W_gate/W_up rows)
     int fd = ::open(path, O_RDONLY);
@@ -1221,7 +1237,13 @@ nv_status nv_prefill(nv_model* m, int32_t seq, const int32_t* tokens, int32_t n)
 //                adapter U silu(D h), then one pass of the final RMSNorm and LM head.
 static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std::vector<int>& exit_of,
                            const float* d_unif) {
-    char* hl = m->h_headlist;
+    if (m->hl_busy[m->hl_next]) {
+        NV_HIP(m, hipStreamSynchronize(m->st));
+        stream_synced(m);
+    }
+    char* hl = m->h_headlist + (size_t)m->hl_next * m->list_bytes();
+    m->hl_busy[m->hl_next] = true;
+    m->hl_next ^= 1;
     const int ns = (int)seqs.size();
     for (int j = 0; j < ns; ++j) {
         const int i = seqs[j];
@@ -1299,6 +1321,42 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
     return NV_OK;
 }
 
+// Router gate sg on the current rows of sequences `run`: the walk's decision (u_sg < w_sg)
+// comes back to the host, which then launches the next segment or the head.  The stream
+// is synchronised.  `run` splits into the sequences that stop here and the rest.
+static nv_status run_gates(nv_model* m, int sg, const std::vector<int>& run, const float* d_unif,
+                           std::vector<int>* stopping, std::vector<int>* rest) {
+    char* gl = m->h_gatelist;
+    const int na = (int)run.size();
+    int top = 0;
+    for (int j = 0; j < na; ++j) {
+        const int i = run[j];
+        nv_model::lseqs(gl)[j] = i;
+        m->lrows(gl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
+        top = std::max(top, i + 1);
+    }
+    NV_HIP(m, hipMemcpyAsync(m->d_gatelist, gl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
+    if (m->cfg.router_form == 1) {
+        const ExitPtrs& X = m->exits[sg];
+        NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8 + (double)m->cfg.router_dim * m->d * 4, [&] {
+            return launch_gate_mlp(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
+                                   X.router_w1, X.router_b1, X.router_w2, m->cfg.router_dim, X.bias, d_unif, sg,
+                                   m->router_hid, m->d_w, m->d_stop, m->st);
+        }, "nv::k_router_hidden + nv::k_router_out"));
+    } else {
+        NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
+            return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
+                               m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
+        }, "nv::k_gate"));
+    }
+    int* hstop = (int*)m->h_out;
+    NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)top * 4, hipMemcpyDeviceToHost, m->st));
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    stream_synced(m);
+    for (int i : run) (hstop[i] ? *stopping : *rest).push_back(i);
+    return NV_OK;
+}
+
 static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, int32_t* tok_out, int32_t* exit_out) {
     if (!m) return NV_EINVAL;
     if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
@@ -1335,7 +1393,6 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
     std::vector<int> active(n), exit_of(n, kMaxExits);
     for (int i = 0; i < n; ++i) active[i] = i;
     for (int i = 0; i < n * 4; ++i) m->last_w[i] = NAN;
-    int* hstop = (int*)m->h_out;
     int* htok_out = (int*)(m->h_out + (size_t)m->max_batch * 4);
     double* hw = (double*)(m->h_out + (size_t)m->max_batch * 8);
     std::vector<int> stopped;   // shared head: the step's stopping sequences, in exit order
@@ -1348,34 +1405,8 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
         if ((s = run_chunks(m, sg, ch)) != NV_OK) return s;
         std::vector<int> stopping;
         if (sg < kMaxExits - 1) {
-            // router gate on the current rows of the active sequences; the walk's decision
-            // comes back to the host, which launches the next segment or the head
-            char* gl = m->h_gatelist;
-            const int na = (int)active.size();
-            for (int j = 0; j < na; ++j) {
-                const int i = active[j];
-                nv_model::lseqs(gl)[j] = i;
-                m->lrows(gl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
-            }
-            NV_HIP(m, hipMemcpyAsync(m->d_gatelist, gl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
-            if (m->cfg.router_form == 1) {
-                const ExitPtrs& X = m->exits[sg];
-                NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8 + (double)m->cfg.router_dim * m->d * 4, [&] {
-                    return launch_gate_mlp(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
-                                           X.router_w1, X.router_b1, X.router_w2, m->cfg.router_dim, X.bias, d_unif,
-                                           sg, m->router_hid, m->d_w, m->d_stop, m->st);
-                }, "nv::k_router_hidden + nv::k_router_out"));
-            } else {
-                NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
-                    return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
-                                       m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
-                }, "nv::k_gate"));
-            }
-            NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
-            NV_HIP(m, hipStreamSynchronize(m->st));
-            m->stage_busy = false;
             std::vector<int> rest;
-            for (int i : active) (hstop[i] ? stopping : rest).push_back(i);
+            NV_TRY(run_gates(m, sg, active, d_unif, &stopping, &rest));
             active.swap(rest);
         } else {
             stopping = active;
@@ -1417,6 +1448,185 @@ nv_status nv_step_forced(nv_model* m, const float* uniforms, const int32_t* next
                          int32_t* exits_out) {
     if (!next_inputs) return m ? fail(m, NV_EINVAL, "null next_inputs") : NV_EINVAL;
     return step_impl(m, uniforms, next_inputs, tokens_out, exits_out);
+}
+
+// Decoding with sequences advancing through the segments independently.  Each tick runs
+// one segment over the sequences whose current token waits there (with their deferred
+// rows), then that segment's gate; the sequences that stop get their head and draw, and
+// their next token enters segment 1.  The policy picks the tick's segment.  Each
+// sequence's computation is the one nv_step performs for it, so its tokens and exits
+// depend only on its own uniforms.
+nv_status nv_generate(nv_model* m, const int32_t* seqs, int32_t n_seq, int32_t n_tokens, const float* uniforms,
+                      int32_t policy, int32_t* tokens_out, int32_t* exits_out) {
+    if (!m) return NV_EINVAL;
+    if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
+    if (!seqs || !uniforms || !tokens_out || !exits_out) return fail(m, NV_EINVAL, "null pointer");
+    if (n_seq < 1 || n_seq > m->max_batch) return fail(m, NV_EINVAL, "n_seq outside 1..max_batch");
+    if (n_tokens < 0) return fail(m, NV_EINVAL, "negative n_tokens");
+    if (policy != NV_SCHED_LOCKSTEP && policy != NV_SCHED_GREEDY) return fail(m, NV_EINVAL, "unknown policy");
+    std::vector<int> idx_of(m->max_batch, -1);
+    for (int i = 0; i < n_seq; ++i) {
+        const int q = seqs[i];
+        if (q < 0 || q >= m->max_batch) return fail(m, NV_EINVAL, "sequence index out of range");
+        if (idx_of[q] >= 0) return fail(m, NV_EINVAL, "sequence listed twice");
+        idx_of[q] = i;
+        if (!m->seqs[q].live) return fail(m, NV_ESTATE, "sequence not prefilled");
+        if (m->seqs[q].n + (int64_t)n_tokens > m->max_ctx) return fail(m, NV_ECAPACITY, "sequence would pass max_ctx");
+    }
+    const int T = n_tokens;
+    for (size_t i = 0; i < (size_t)n_seq * T * 4; ++i)
+        if (!(uniforms[i] >= 0.0f && uniforms[i] < 1.0f)) return fail(m, NV_EINVAL, "uniform outside [0,1) or NaN");
+    if (T == 0) return NV_OK;
+    NV_HIP(m, hipStreamSynchronize(m->st));
+    stream_synced(m);
+
+    struct Gen {
+        int slot, t, q, age;   // token index, segment its current token waits at, ticks waited
+        bool fresh;            // current token not embedded yet
+    };
+    std::vector<Gen> g(n_seq);
+    char* hb = m->h_stepblk;
+    for (int i = 0; i < n_seq; ++i) {
+        g[i] = Gen{seqs[i], 0, 0, 0, true};
+        m->tok_in(hb)[seqs[i]] = m->seqs[seqs[i]].pending;
+    }
+    // the embedding reads sequence s's input token at d_tok_out[s], where its draws land
+    NV_HIP(m, hipMemcpyAsync(m->d_tok_out, m->tok_in(hb), (size_t)m->max_batch * 4, hipMemcpyHostToDevice, m->st));
+    m->sb_busy = true;
+    const float* d_unif = nv_model::unif(m->d_stepblk);
+
+    // drawn tokens come back through a ring of pinned buffers; an entry is read after
+    // the next stream synchronisation
+    struct RingEntry {
+        std::vector<std::pair<int, int>> items;   // (slot, token index)
+        bool pending = false;
+    };
+    RingEntry ring[kRing];
+    int ring_next = 0;
+    auto drain = [&]() {
+        for (int e = 0; e < kRing; ++e) {
+            if (!ring[e].pending) continue;
+            const int* hv = m->h_ring + (size_t)e * m->max_batch;
+            for (const auto& it : ring[e].items) tokens_out[(size_t)idx_of[it.first] * T + it.second] = hv[it.first];
+            ring[e].items.clear();
+            ring[e].pending = false;
+        }
+    };
+    auto full_sync = [&]() -> nv_status {
+        NV_HIP(m, hipStreamSynchronize(m->st));
+        stream_synced(m);
+        drain();
+        return NV_OK;
+    };
+
+    std::vector<int> exit_of(m->max_batch, kMaxExits);
+    int remaining = n_seq;
+    while (remaining > 0) {
+        int cnt[kMaxExits] = {0, 0, 0, 0}, oldest[kMaxExits] = {0, 0, 0, 0};
+        for (const Gen& x : g)
+            if (x.t < T) {
+                ++cnt[x.q];
+                oldest[x.q] = std::max(oldest[x.q], x.age);
+            }
+        int sg = 0;
+        if (policy == NV_SCHED_LOCKSTEP) {
+            // finish the round's deeper segments before the next tokens start
+            for (int k = 1; k < kMaxExits; ++k)
+                if (cnt[k]) {
+                    sg = k;
+                    break;
+                }
+        } else {
+            // the segment with the most waiting sequences, plus half the longest wait
+            // there in ticks; ties go to the deeper segment
+            double best = -1.0;
+            for (int k = 0; k < kMaxExits; ++k)
+                if (cnt[k]) {
+                    const double sc = cnt[k] + 0.5 * oldest[k];
+                    if (sc >= best) {
+                        best = sc;
+                        sg = k;
+                    }
+                }
+        }
+        std::vector<int> run;
+        for (const Gen& x : g)
+            if (x.t < T && x.q == sg) run.push_back(x.slot);
+        if (sg == 0) {
+            // new tokens: their uniforms and embeddings
+            int nf = 0;
+            for (const Gen& x : g)
+                if (x.t < T && x.q == 0 && x.fresh) ++nf;
+            if (nf > 0) {
+                if (m->sb_busy) NV_TRY(full_sync());
+                int j = 0;
+                for (Gen& x : g) {
+                    if (!(x.t < T && x.q == 0 && x.fresh)) continue;
+                    const SeqHost& S = m->seqs[x.slot];
+                    const float* u = uniforms + ((size_t)idx_of[x.slot] * T + x.t) * 4;
+                    for (int c = 0; c < 4; ++c) nv_model::unif(hb)[x.slot * 4 + c] = u[c];
+                    m->cur_rows(hb)[j++] = RowInfo{x.slot * m->max_ctx + S.n, x.slot, S.n, 0};
+                    x.fresh = false;
+                }
+                NV_HIP(m, hipMemcpyAsync(m->d_stepblk, hb, m->stepblk_bytes(), hipMemcpyHostToDevice, m->st));
+                m->sb_busy = true;
+                NV_TRY(timed(m, NV_TIME_OTHER, (double)nf * m->d * (m->plan.es + 4), [&] {
+                    return launch_embed(m->d_tok_out, m->cur_rows(m->d_stepblk), nf, m->embed, m->bf16, m->Hs, m->d,
+                                        m->st, 1);
+                }, "nv::k_embed"));
+            }
+        }
+        std::vector<Chunk> ch;
+        for (int slot : run) {
+            const SeqHost& S = m->seqs[slot];
+            ch.push_back({slot, S.f[sg], S.n - S.f[sg] + 1});
+        }
+        nv_status s = run_chunks(m, sg, ch);
+        if (s != NV_OK) return s;
+        std::vector<int> stopping, rest;
+        if (sg < kMaxExits - 1) {
+            NV_TRY(run_gates(m, sg, run, d_unif, &stopping, &rest));
+            drain();
+        } else {
+            stopping = run;
+        }
+        for (Gen& x : g)
+            if (x.t < T) ++x.age;
+        for (int slot : rest) g[idx_of[slot]].q = sg + 1;
+        if (stopping.empty()) continue;
+        for (int slot : stopping) exit_of[slot] = sg + 1;
+        NV_TRY(run_heads(m, stopping, exit_of, d_unif));
+        if (ring[ring_next].pending) NV_TRY(full_sync());
+        NV_HIP(m, hipMemcpyAsync(m->h_ring + (size_t)ring_next * m->max_batch, m->d_tok_out,
+                                 (size_t)m->max_batch * 4, hipMemcpyDeviceToHost, m->st));
+        RingEntry& E = ring[ring_next];
+        E.pending = true;
+        ring_next = (ring_next + 1) % kRing;
+        for (int slot : stopping) {
+            Gen& x = g[idx_of[slot]];
+            SeqHost& S = m->seqs[slot];
+            const int e = sg + 1;
+            E.items.push_back({slot, x.t});
+            exits_out[(size_t)idx_of[slot] * T + x.t] = e;
+            for (int k = 0; k < e; ++k) S.f[k] = S.n + 1;
+            S.n += 1;
+            S.last_exit = e;
+            x.t += 1;
+            x.q = 0;
+            x.age = 0;
+            x.fresh = true;
+            if (x.t == T) --remaining;
+        }
+    }
+    NV_TRY(sync_and_check(m));
+    drain();
+    if (m->timing) NV_TRY(resolve_timing(m));
+    for (int i = 0; i < n_seq; ++i) {
+        SeqHost& S = m->seqs[seqs[i]];
+        S.pending = tokens_out[(size_t)i * T + T - 1];
+        for (int k = 0; k < 4; ++k) m->last_w[(size_t)seqs[i] * 4 + k] = NAN;
+    }
+    return NV_OK;
 }
 
 // Mixture objective, rows o..o+k-1 of the loss pass after segment sg: the exit's router
@@ -1521,6 +1731,7 @@ nv_status nv_mixture_loss(nv_model* m, int32_t seq, const int32_t* tokens, int32
     NV_HIP(m, hipMemcpyAsync(m->loss_ids, ids.data(), 4 * (size_t)np, hipMemcpyHostToDevice, m->st));
     NV_HIP(m, hipMemcpyAsync(m->loss_tgt, tgt.data(), 4 * (size_t)np, hipMemcpyHostToDevice, m->st));
     NV_HIP(m, hipStreamSynchronize(m->st));
+    stream_synced(m);
     // the prefill of the first n-1 tokens, with every exit's router and head after its segment
     SeqHost& S = m->seqs[seq];
     S = SeqHost();

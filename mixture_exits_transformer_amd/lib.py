@@ -51,6 +51,8 @@ _SIGS = {
     "nv_prefill": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, ctypes.c_int32]),
     "nv_step": (ctypes.c_int, [_P, _F32P, _I32P, _I32P]),
     "nv_step_forced": (ctypes.c_int, [_P, _F32P, _I32P, _I32P, _I32P]),
+    "nv_generate": (ctypes.c_int, [_P, _I32P, ctypes.c_int32, ctypes.c_int32, _F32P, ctypes.c_int32, _I32P,
+                                   _I32P]),
     "nv_mixture_loss": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_double, _F64P, _F64P]),
     "nv_flush": (ctypes.c_int, [_P, ctypes.c_int32]),
     "nv_debug_frontiers": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, _I32P]),
@@ -179,6 +181,21 @@ def nv_step_forced(h: Handle, uniforms, next_inputs) -> Tuple[np.ndarray, np.nda
     ex = np.empty(n, np.int32)
     _check(h.ptr, library().nv_step_forced(h.ptr, _ptr(u, ctypes.c_float), _ptr(f, ctypes.c_int32),
                                            _ptr(tok, ctypes.c_int32), _ptr(ex, ctypes.c_int32)))
+    return tok, ex
+
+
+SCHED_LOCKSTEP, SCHED_GREEDY = 0, 1
+
+
+def nv_generate(h: Handle, seqs, uniforms, policy: int = SCHED_GREEDY) -> Tuple[np.ndarray, np.ndarray]:
+    """uniforms [n_seq][n_tokens][4] -> (tokens, exits), each [n_seq][n_tokens]."""
+    q = np.ascontiguousarray(seqs, dtype=np.int32).reshape(-1)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    assert u.ndim == 3 and u.shape[0] == len(q) and u.shape[2] == 4, u.shape
+    tok = np.zeros(u.shape[:2], np.int32)
+    ex = np.zeros(u.shape[:2], np.int32)
+    _check(h.ptr, library().nv_generate(h.ptr, _ptr(q, ctypes.c_int32), len(q), u.shape[1], _ptr(u, ctypes.c_float),
+                                        policy, _ptr(tok, ctypes.c_int32), _ptr(ex, ctypes.c_int32)))
     return tok, ex
 
 
