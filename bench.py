@@ -15,6 +15,8 @@ wall-clock stamps per block for the decode GEMMs and attention, HIP events for t
 rest; roofline of the dominant block GEMM against 8 TB/s), and the CPU oracle timed
 on a bounded sample of the same decode.
 
+Workload "C" (--workload C) decodes 16 sequences with nv_generate's greedy segment
+scheduling; lock-step scheduling, nv_step and exit-4-forced decoding are timed beside it.
 Workload "L" (--workload L) times the mixture objective instead: a step is one
 nv_mixture_loss over a 2048-token sequence on the same 1.5B model (full-depth causal
 pass, every exit's router and head at every position); `value` = scored positions/s,
@@ -214,12 +216,123 @@ def bench_loss(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def bench_batch(args, wl):
+    """Batched decode (workload C: 16 independent sequences): a step is one token for
+    every sequence.  `value` uses nv_generate with the greedy tick policy (sequences
+    advance through the segments independently); beside it the lock-step policy, a
+    loop of nv_step calls, and exit-4-forced decoding."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+
+    from mixture_exits_transformer_amd import lib
+    from synth import cached_weights, prompts, uniforms
+    from synth.configs import BIAS_ALL_LAST
+    ps = prompts(wl)
+    B = wl.batch
+    steps = args.steps if args.steps is not None else wl.decode_steps
+    warmup = args.warmup if args.warmup is not None else 8
+    U = np.ascontiguousarray(uniforms(wl, steps=steps + warmup).transpose(1, 0, 2))   # [B][steps+warmup][4]
+    Uw, Ut = np.ascontiguousarray(U[:, steps:]), np.ascontiguousarray(U[:, :steps])
+    max_ctx = max(len(p) for p in ps) + max(steps, warmup)
+    slots = list(range(B))
+    path = cached_weights(wl.model)
+
+    def prefill_all(h):
+        for i, p in enumerate(ps):
+            lib.nv_prefill(h, i, p)
+
+    def timed_generate(h, policy):
+        prefill_all(h)
+        if warmup:
+            lib.nv_generate(h, slots, Uw, policy)
+        prefill_all(h)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, exs = lib.nv_generate(h, slots, Ut, policy)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, exs
+
+    h = lib.nv_load(path, B, max_ctx)
+    dt_g, ex_g = timed_generate(h, lib.SCHED_GREEDY)
+    dt_l, ex_l = timed_generate(h, lib.SCHED_LOCKSTEP)
+    prefill_all(h)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(steps):
+        lib.nv_step(h, Ut[:, t, :])
+    torch.cuda.synchronize()
+    dt_s = time.perf_counter() - t0
+    prefill_all(h)
+    lib.nv_timing_enable(h, True)
+    lib.nv_generate(h, slots, Ut, lib.SCHED_GREEDY)
+    tim = lib.nv_timing_read(h)
+    ker = lib.nv_timing_kernels(h)
+    lib.nv_timing_enable(h, False)
+    lib.nv_free(h)
+    base = None
+    if not args.no_baseline:
+        h4 = lib.nv_load(cached_weights(replace(wl.model, gate_bias=BIAS_ALL_LAST)), B, max_ctx)
+        dt4, ex4 = timed_generate(h4, lib.SCHED_LOCKSTEP)
+        lib.nv_free(h4)
+        assert set(ex4.ravel().tolist()) == {4}
+        base = B * steps / dt4
+    tok_s = B * steps / dt_g
+    gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
+    _, nl, ms, by, kname = gemms[0]
+    achieved = by / (ms * 1e-3) / 1e9
+    counted = counted_traffic(kname)
+    top = sorted(ker, key=lambda k: -k[2])[:8]
+    out = {
+        "metric": "generated tokens/s over 16 sequences, 1.5B, greedy segment scheduling vs lock-step; "
+                  "achieved HBM GB/s",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(dt_g / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.model.wdtype,
+        "data": "synthetic: uniform-random token ids, seeded uniforms, random-init N(0,0.02) weights",
+        "config": {"workload": f"{wl.name}: {wl.note}", "batch": B, "prompts": [len(p) for p in ps],
+                   "decode_steps": steps},
+        "roofline": {"bound": "hbm", "kernel": kname,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counted[0] if counted else None,
+                     "traffic_source": counted[1] if counted else None,
+                     "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
+                     "bytes_per_launch": round(by / max(nl, 1))},
+        "lockstep_policy_tokens_per_s": round(B * steps / dt_l, 2),
+        "nv_step_loop_tokens_per_s": round(B * steps / dt_s, 2),
+        "greedy_vs_lockstep": round(dt_l / dt_g - 1.0, 4),
+        "exit4_forced_tokens_per_s": round(base, 2) if base else None,
+        "speedup_vs_exit4": round(tok_s / base - 1.0, 4) if base else None,
+        "exit_histogram": [int(x) for x in np.bincount(ex_g.ravel(), minlength=5)[1:]],
+        "lockstep_exit_histogram": [int(x) for x in np.bincount(ex_l.ravel(), minlength=5)[1:]],
+        "top_kernels": [{"kernel": k[4], "class": k[0], "launches": k[1],
+                         "avg_us": round(k[2] / max(k[1], 1) * 1e3, 3),
+                         "GBps": round(k[3] / (k[2] * 1e-3) / 1e9, 1) if k[2] > 0 else None} for k in top],
+        "kernel_classes_ms_per_step": {k: round(v[0] / steps, 4) for k, v in tim.items()},
+    }
+    if not args.no_cpu:
+        j = int(np.argmin([len(p) for p in ps]))
+        cb = cpu_baseline(wl, path, ps[j], Ut[j], args.cpu_budget)
+        cb["sample"] = f"sequence {j} alone: " + cb["sample"]
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="decode steps (default 512); loss passes (10)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 16; loss passes 2)")
-    ap.add_argument("--workload", default="A", help="A, B, D, E (decode, batch 1) or L (mixture objective)")
+    ap.add_argument("--workload", default="A",
+                    help="A, B, D, E (decode, batch 1), C (16 sequences) or L (mixture objective)")
     ap.add_argument("--cpu-loss-tokens", type=int, default=40, help="oracle sample for workload L")
     ap.add_argument("--no-baseline", action="store_true", help="skip the exit-4-forced run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -244,7 +357,8 @@ def main():
     wl = workload(args.workload)
     if wl.name == "L":
         return bench_loss(args, wl)
-    assert wl.batch == 1, "bench.py times the batch-1 workloads"
+    if wl.batch > 1:
+        return bench_batch(args, wl)
     steps = args.steps if args.steps is not None else 512
     warmup = args.warmup if args.warmup is not None else 16
     prompt = prompts(wl)[0]

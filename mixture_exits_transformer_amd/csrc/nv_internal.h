@@ -89,6 +89,11 @@ constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combin
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
                            float* out, hipStream_t st);
+// Matrix-core variant of launch_attn for a bf16 KV cache and head_dim 32, 64 or 128:
+// items of up to 64 rows, key ranges starting at multiples of 64.
+bool attn_mfma_ok(const LayerDims& D);
+hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
+                            int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st);
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
                        const void* kv, int layer, const LayerDims& D, float* part_ml,
                        float* part_o, float* out, hipStream_t st);

@@ -1132,6 +1132,201 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Chunked causal attention on the matrix cores (bf16 KV cache), for launch groups of many
+// rows.  An item is up to 64 consecutive rows of one sequence, one head and one key range;
+// wave w takes rows 16w..16w+15.  Per 64-key tile (double-buffered in LDS, keys as rows,
+// values transposed) the wave forms the transposed scores S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16: lane l then holds the scores of query l%16 for keys
+// 16t + 4(l/16) + i (t = 0..3, i = 0..3).  That is, with keys permuted inside each
+// 32-key step, the B operand of O^T = V^T P^T, so the probabilities go from the
+// accumulators to the second product without leaving the registers; V^T is read with the
+// same key permutation.  Every value a lane holds belongs to its one query, so the online
+// softmax rescales a lane's accumulators by one factor; the row max crosses the four lane
+// groups of a query once per tile, the row sum only at the end.
+// Outputs: the normalised row (single split) or the (max, sum, unnormalised output)
+// partials that k_attn_combine merges, as k_attn writes them.
+// ------------------------------------------------------------------------------------------
+
+constexpr int AM_ROWS = 64;   // rows per item
+constexpr int AM_KT = 64;     // keys per tile
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_mfma(const AttnItem* items, const RowInfo* rows, const float* q,
+                                                   const uint16_t* kv, int layer, LayerDims D, float* part_ml,
+                                                   float* part_o, float* out) {
+    constexpr int KLD = HD + 8;         // K tile row stride (bf16)
+    constexpr int VLD = AM_KT + 8;      // transposed V tile row stride (bf16)
+    constexpr int NKS = HD / 32;        // k-steps of the score product
+    constexpr int NHT = HD / 16;        // 16-wide output tiles
+    constexpr int CPR = HD / 8;         // 16-byte chunks per key row
+    constexpr int CPT = AM_KT * CPR / 256;   // chunks per thread per tile, for K and for V
+    __shared__ __align__(16) uint16_t Ks[2][AM_KT * KLD];
+    __shared__ __align__(16) uint16_t Vt[2][HD * VLD];
+    const AttnItem it = items[blockIdx.x];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qn = lane & 15, g = lane >> 4;
+    const int r = wave * 16 + qn;                  // this lane's query row within the item
+    const bool rv = r < it.nrows;
+    const int qpos = rv ? rows[it.row0 + r].pos : -1;
+    const int seq = rows[it.row0].seq;
+    const uint16_t* Kg = kv + kv_base(D, seq, layer, 0, it.head);
+    const uint16_t* Vg = kv + kv_base(D, seq, layer, 1, it.head);
+
+    // queries (B operand of the score product), pre-scaled by 1/sqrt(hd)
+    bf16x8_t qf[NKS];
+    {
+        const float scale = 1.0f / sqrtf((float)HD);
+        const float* qr = q + (int64_t)(it.row0 + (rv ? r : 0)) * D.d + it.head * HD;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            uint32_t p[4] = {0u, 0u, 0u, 0u};
+            if (rv) {
+                const float4 a = *(const float4*)(qr + 32 * ks + 8 * g);
+                const float4 b = *(const float4*)(qr + 32 * ks + 8 * g + 4);
+                p[0] = pack_bf2(a.x * scale, a.y * scale);
+                p[1] = pack_bf2(a.z * scale, a.w * scale);
+                p[2] = pack_bf2(b.x * scale, b.y * scale);
+                p[3] = pack_bf2(b.z * scale, b.w * scale);
+            }
+            qf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+        }
+    }
+
+    uint4 kr[CPT], vr[CPT];
+    auto gload = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = tid + 256 * j;
+            const int key = min(t0 + c / CPR, it.hi - 1);   // rows past the range are masked
+            const int col = (c % CPR) * 8;
+            kr[j] = *(const uint4*)(Kg + (int64_t)key * HD + col);
+            vr[j] = *(const uint4*)(Vg + (int64_t)key * HD + col);
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = tid + 256 * j;
+            const int key = c / CPR, col = (c % CPR) * 8;
+            *(uint4*)&Ks[buf][key * KLD + col] = kr[j];
+            const uint16_t* v = (const uint16_t*)&vr[j];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Vt[buf][(col + e) * VLD + key] = v[e];
+        }
+    };
+
+    f32x4_t o[NHT];
+#pragma unroll
+    for (int t = 0; t < NHT; ++t) o[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    const int ntile = (it.hi - it.lo + AM_KT - 1) / AM_KT;
+    gload(it.lo);
+    lstore(0);
+    __syncthreads();
+    for (int tt = 0; tt < ntile; ++tt) {
+        const int buf = tt & 1, t0 = it.lo + tt * AM_KT;
+        if (tt + 1 < ntile) gload(t0 + AM_KT);
+        // S^T for this tile: 4 key tiles of 16
+        f32x4_t sc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            sc[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint4 a = *(const uint4*)&Ks[buf][(16 * mt + qn) * KLD + 32 * ks + 8 * g];
+                sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qf[ks], sc[mt],
+                                                                 0, 0, 0);
+            }
+        }
+        // mask (causal and the item's key range) and the running max of this lane's query
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = t0 + 16 * mt + 4 * g + i;
+                const bool ok = key < it.hi && key <= qpos;
+                sc[mt][i] = ok ? sc[mt][i] : -INFINITY;
+                tmax = fmaxf(tmax, sc[mt][i]);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m, tmax);
+        const float alpha = (mn == -INFINITY) ? 1.0f : __expf(m - mn);
+        float ps = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = (sc[mt][i] == -INFINITY) ? 0.f : __expf(sc[mt][i] - mn);
+                sc[mt][i] = pv;
+                ps += pv;
+            }
+        lsum = lsum * alpha + ps;
+        m = mn;
+#pragma unroll
+        for (int t = 0; t < NHT; ++t) o[t] *= alpha;
+        // O^T += V^T P^T over the tile's two 32-key steps
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 pb = make_uint4(pack_bf2(sc[2 * ks][0], sc[2 * ks][1]), pack_bf2(sc[2 * ks][2], sc[2 * ks][3]),
+                                        pack_bf2(sc[2 * ks + 1][0], sc[2 * ks + 1][1]),
+                                        pack_bf2(sc[2 * ks + 1][2], sc[2 * ks + 1][3]));
+            const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+#pragma unroll
+            for (int t = 0; t < NHT; ++t) {
+                const uint16_t* vrow = &Vt[buf][(16 * t + qn) * VLD + 32 * ks + 4 * g];
+                const uint2 lo = *(const uint2*)vrow;
+                const uint2 hi = *(const uint2*)(vrow + 16);
+                const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pf, o[t], 0, 0, 0);
+            }
+        }
+        if (tt + 1 < ntile) lstore(buf ^ 1);
+        __syncthreads();
+    }
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (!rv) return;
+    if (it.nsplit == 1) {
+        const float inv = 1.0f / lsum;
+        float* orow = out + (int64_t)(it.row0 + r) * D.d + it.head * HD;
+#pragma unroll
+        for (int t = 0; t < NHT; ++t)
+            *(float4*)(orow + 16 * t + 4 * g) = make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+        return;
+    }
+    const int64_t slot = it.part + r;
+    if (g == 0) {
+        part_ml[2 * slot] = m;
+        part_ml[2 * slot + 1] = lsum;
+    }
+    float* po = part_o + slot * HD;
+#pragma unroll
+    for (int t = 0; t < NHT; ++t) *(float4*)(po + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+}
+
+bool attn_mfma_ok(const LayerDims& D) { return D.kv_bf16 && (D.hd == 32 || D.hd == 64 || D.hd == 128); }
+
+hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
+                            int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st) {
+    if (n_items <= 0) return hipSuccess;
+    if (!attn_mfma_ok(D)) return hipErrorInvalidValue;
+    const uint16_t* k16 = (const uint16_t*)kv;
+    if (D.hd == 128)
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
+                  part_ml, part_o, out);
+    else if (D.hd == 64)
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
+                  part_ml, part_o, out);
+    else
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
+                  part_ml, part_o, out);
+    return hipGetLastError();
+}
+
 // Merge the split partials of one (row, head): the (max, sum) pairs of its splits are
 // staged in LDS, turned into weights exp(max - M), and each thread forms the weighted sum
 // of one output dim with independent loads.  Rows whose key range was not split were

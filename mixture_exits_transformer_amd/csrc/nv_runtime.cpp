@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kMaxExits = 4;
 constexpr int kAttnRowsPerItem = 32;
+constexpr int AM_ROWS_PER_ITEM = 64;   // rows per item of the matrix-core chunk attention
 constexpr int kDecodeRows = 64;          // launch groups up to this many rows use decode attention
 constexpr int kAttnBlocksTarget = 512;   // decode attention: aim for about this many blocks
 constexpr size_t kAlign = 256;
@@ -530,15 +531,16 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         if (slot > P.part_cap || n_items > P.items_cap)
             return fail(m, NV_ECAPACITY, "internal: attention partials exceed the workspace");
     } else {
-        // long chunks: row blocks of 32 rows sharing LDS key tiles; the key range is split
-        // into pieces of split_len keys (doubling until the partial slots fit), combined by
-        // a separate pass
+        // long chunks: row blocks of 32 rows (64 on the matrix cores) sharing LDS key tiles;
+        // the key range is split into pieces of split_len keys (doubling until the partial
+        // slots fit), combined by a separate pass
+        const int rpi = attn_mfma_ok(m->dims()) ? AM_ROWS_PER_ITEM : kAttnRowsPerItem;
         int split_len = 512;
         for (;;) {
             long slots = 0, items = 0;
             for (const Chunk& c : chunks)
-                for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
-                    int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
+                for (int rb = 0; rb < c.nrows; rb += rpi) {
+                    int nr = std::min(rpi, c.nrows - rb);
                     int ctx = c.pos0 + rb + nr;
                     int ns = (ctx + split_len - 1) / split_len;
                     slots += (long)m->H * ns * nr;
@@ -551,8 +553,8 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         }
         int slot = 0, row0 = 0;
         for (const Chunk& c : chunks) {
-            for (int rb = 0; rb < c.nrows; rb += kAttnRowsPerItem) {
-                int nr = std::min(kAttnRowsPerItem, c.nrows - rb);
+            for (int rb = 0; rb < c.nrows; rb += rpi) {
+                int nr = std::min(rpi, c.nrows - rb);
                 int ctx = c.pos0 + rb + nr;
                 int ns = (ctx + split_len - 1) / split_len;
                 for (int h = 0; h < m->H; ++h)
@@ -645,6 +647,14 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
                 NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
                     return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
                 }, "nv::k_attn_combine"));
+        } else if (attn_mfma_ok(D)) {
+            NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
+                return launch_attn_mfma(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o,
+                                        m->attn_o, m->st);
+            }, "nv::k_attn_mfma"));
+            NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
+                return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
+            }, "nv::k_attn_combine"));
         } else {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
                 return launch_attn(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o, m->attn_o,
