@@ -171,14 +171,15 @@ def bench_loss(args, wl):
     lib.nv_free(h)
     m = wl.model
     d, F, Lr, V, r = m.d_model, m.ffn, m.n_layers, m.vocab, n - 1
-    # dominant kernel: of the block GEMMs of the full-depth pass, those with the RMSNorm
-    # folded in (QKV, gate/up: "k_row_rms + ...") and those without (O, down) are timed
-    # under two names; their algorithmic FLOPs are 2 r L (3d^2 + 2Fd) and 2 r L (d^2 + Fd).
+    # dominant kernel: the block-GEMM symbol with the most device time.  The long-chunk
+    # GEMM is instantiated per epilogue (template argument EPI: 1 residual = O and down,
+    # 2 SwiGLU = gate/up, 3 QKV), so each symbol's algorithmic FLOPs follow from it.
+    per_epi = {1: 2.0 * r * Lr * (d * d + F * d), 2: 2.0 * r * Lr * 2 * F * d, 3: 2.0 * r * Lr * 3 * d * d}
     gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
-    assert len(gemms) == 2, [k[4] for k in gemms]
     _, nl, ms, by, kname = gemms[0]
-    normed = "k_row_rms" in kname
-    flops = 2.0 * r * Lr * ((3 * d * d + 2 * F * d) if normed else (d * d + F * d))
+    epi = int(kname.split("k_gemm_bf16<")[1].split(">")[0].split(",")[2]) if "k_gemm_bf16<" in kname else None
+    assert epi in per_epi, f"dominant block GEMM {kname} is not the long-chunk kernel"
+    flops = per_epi[epi]
     achieved = flops / (ms * 1e-3) / 1e12
     all_flops = 2.0 * r * Lr * (4 * d * d + 3 * d * F)
     counted = counted_traffic(kname)

@@ -35,6 +35,8 @@ struct GemmArgs {
     const struct RowInfo* o_rows;  // row i of out is out + o_rows[i].hrow * ldo (identity if null)
     int head;             // 1: an exit head (separate kernel symbol, so profiles tell them apart)
     float* rms_ws;        // [R] scratch for per-row inverse RMS (matrix-core path with norm_w)
+    uint16_t* abf;        // [R][K] bf16 scratch: the rows, normalised and rounded once (long chunks), or null
+    int abf_ready;        // abf already holds this product's rows (launch_rows_bf16 ran)
     int mfma_min_rows;    // use the matrix-core path when R >= this (0: never)
     // EPI_QKV only.  Weight row 2p + i (i = 0, 1) of the fused QKV matrix is original
     // row part*d + h*hd + j + i*hd/2, where p = part*(d/2) + h*(hd/2) + j, part 0/1/2 = q/k/v.
@@ -81,6 +83,11 @@ hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStre
 hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const void* E, int wbf16,
                         float* Hs, int d, hipStream_t st, int by_seq = 0);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// Long chunks on bf16 weights take the bf16-row path: k_rows_bf16 writes the rows of A
+// (normalised when norm_w is set) to abf, then k_gemm_bf16 runs on them.  With
+// launch_rows_bf16 first and abf_ready set, launch_gemm runs only the product.
+bool gemm_uses_bf16_rows(const GemmArgs& a);
+hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st);
 // Decode-sized row blocks (<= ATTN_DEC_ROWS rows): each item is one split of one
 // (row block, head); split partials are merged by launch_attn_combine.
 constexpr int ATTN_DEC_ROWS = 8;

@@ -97,13 +97,14 @@ hipError_t launch_embed(const int* tokens, const RowInfo* rows, int n, const voi
 // Epilogue for a pair of adjacent output columns (n, n+1), n even, of row `row`.
 // ------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, float v0, float v1) {
-    if (a.epi == EPI_SWIGLU) {
+template <int EPI>
+__device__ __forceinline__ void epi_pair_t(const GemmArgs& a, int row, int n, float v0, float v1) {
+    if constexpr (EPI == EPI_SWIGLU) {
         const int orow = a.o_rows ? a.o_rows[row].hrow : row;
         a.out[(int64_t)orow * a.ldo + (n >> 1)] = v0 / (1.0f + expf(-v0)) * v1;
         return;
     }
-    if (a.epi == EPI_QKV) {
+    if constexpr (EPI == EPI_QKV) {
         // columns n, n+1 hold rotation partners j and j + hd/2 of one head of q, k or v
         const RowInfo ri = a.a_rows[row];
         const LayerDims& D = a.D;
@@ -132,17 +133,29 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, floa
         }
         return;
     }
-    const int orow = a.o_rows ? a.o_rows[row].hrow : row;
-    float* o = a.out + (int64_t)orow * a.ldo + n;
-    if (a.epi == EPI_STORE) {
-        o[0] = v0;
-        o[1] = v1;
-    } else if (a.epi == EPI_SILU) {
-        o[0] = v0 / (1.0f + expf(-v0));
-        o[1] = v1 / (1.0f + expf(-v1));
-    } else {
-        o[0] += v0;
-        o[1] += v1;
+    if constexpr (EPI == EPI_STORE || EPI == EPI_SILU || EPI == EPI_RESID) {
+        const int orow = a.o_rows ? a.o_rows[row].hrow : row;
+        float* o = a.out + (int64_t)orow * a.ldo + n;
+        if constexpr (EPI == EPI_STORE) {
+            o[0] = v0;
+            o[1] = v1;
+        } else if constexpr (EPI == EPI_SILU) {
+            o[0] = v0 / (1.0f + expf(-v0));
+            o[1] = v1 / (1.0f + expf(-v1));
+        } else {
+            o[0] += v0;
+            o[1] += v1;
+        }
+    }
+}
+
+__device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, float v0, float v1) {
+    switch (a.epi) {
+        case EPI_SWIGLU: epi_pair_t<EPI_SWIGLU>(a, row, n, v0, v1); break;
+        case EPI_QKV: epi_pair_t<EPI_QKV>(a, row, n, v0, v1); break;
+        case EPI_STORE: epi_pair_t<EPI_STORE>(a, row, n, v0, v1); break;
+        case EPI_SILU: epi_pair_t<EPI_SILU>(a, row, n, v0, v1); break;
+        default: epi_pair_t<EPI_RESID>(a, row, n, v0, v1); break;
     }
 }
 
@@ -477,6 +490,9 @@ __global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+// Staging registers use the compiler's own vector type: arrays of HIP's uint4 (a struct)
+// are not promoted to registers, which parks every prefetched tile in scratch.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MF_BM = 64, MF_BK = 64, MF_LDK = MF_BK + 8;
 
@@ -513,25 +529,24 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
     const bool w_on = lr < BN;
     const uint16_t* Wrow = (const uint16_t*)a.W + (int64_t)(n0 + (w_on ? lr : 0)) * K;
 
-    float4 ar[4];
-    uint4 wr[2];
-    auto gload = [&](int k0) {
+    f32x4_t ar[4];
+    u32x4 wr[2];
+    auto gload = [&](int k0) __attribute__((always_inline)) {
         if (a_ok) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ar[j] = *(const float4*)(Arow + k0 + lk + 4 * j);
+            for (int j = 0; j < 4; ++j) ar[j] = *(const f32x4_t*)(Arow + k0 + lk + 4 * j);
         }
         if (w_on) {
-            wr[0] = *(const uint4*)(Wrow + k0 + lk);
-            wr[1] = *(const uint4*)(Wrow + k0 + lk + 8);
+            wr[0] = *(const u32x4*)(Wrow + k0 + lk);
+            wr[1] = *(const u32x4*)(Wrow + k0 + lk + 8);
         }
     };
-    auto lstore = [&](int buf, int k0) {
+    auto lstore = [&](int buf, int k0) __attribute__((always_inline)) {
         uint32_t p[8];
         if (a_ok) {
-            const float* v = (const float*)ar;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float x0 = v[2 * j] * rs, x1 = v[2 * j + 1] * rs;
+                float x0 = ar[j >> 1][(2 * j) & 3] * rs, x1 = ar[j >> 1][(2 * j + 1) & 3] * rs;
                 if (a.norm_w) {
                     x0 *= a.norm_w[k0 + lk + 2 * j];
                     x1 *= a.norm_w[k0 + lk + 2 * j + 1];
@@ -546,7 +561,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
         dst[0] = make_uint4(p[0], p[1], p[2], p[3]);
         dst[1] = make_uint4(p[4], p[5], p[6], p[7]);
         if (w_on) {
-            uint4* wd = (uint4*)&Ws[buf][lr * MF_LDK + lk];
+            u32x4* wd = (u32x4*)&Ws[buf][lr * MF_LDK + lk];
             wd[0] = wr[0];
             wd[1] = wr[1];
         }
@@ -591,6 +606,165 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
     }
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Long-chunk products on bf16 activations.  k_rows_bf16 writes each row of A once as bf16
+// (RMSNormed and scaled by the norm weight when norm_w is set) into a contiguous [R][K]
+// scratch; k_gemm_bf16 then computes 128-row x BN-column tiles with four waves in a 2x2
+// layout (64 x BN/2 each), K staged through LDS in double-buffered 64-wide steps, on
+// v_mfma_f32_16x16x32_bf16 (lane layout as in k_gemm_mfma).  Epilogues as for the other
+// products (row i of the chunk keeps its a_rows / o_rows entries).
+// ------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_rows_bf16(const float* A, int64_t lda, const RowInfo* rows, int R, int K,
+                                                   const float* norm_w, float eps, uint16_t* out) {
+    const int r = blockIdx.x;
+    if (r >= R) return;
+    const float* src = A + (int64_t)(rows ? rows[r].hrow : r) * lda;
+    __shared__ float red[4];
+    float inv = 1.0f;
+    if (norm_w) {
+        float ss = 0.f;
+        for (int k = threadIdx.x * 4; k < K; k += 1024) {
+            const float4 v = *(const float4*)(src + k);
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)K + eps);
+    }
+    uint16_t* dst = out + (int64_t)r * K;
+    for (int k = threadIdx.x * 4; k < K; k += 1024) {
+        float4 v = *(const float4*)(src + k);
+        if (norm_w) {
+            const float4 g = *(const float4*)(norm_w + k);
+            v = make_float4(v.x * inv * g.x, v.y * inv * g.y, v.z * inv * g.z, v.w * inv * g.w);
+        }
+        *(uint2*)(dst + k) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+    }
+}
+
+constexpr int GB_BM = 128, GB_BK = 64, GB_LDK = GB_BK + 8;
+constexpr int GB_MIN_ROWS = 33;    // chunks of at least this many rows use k_gemm_bf16
+
+template <int BN, int HEAD, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
+    constexpr int WN = BN / 2;                        // columns per wave
+    constexpr int NT = WN / 16;
+    constexpr int MT = 4;                             // 64 rows per wave
+    constexpr int ACH = GB_BM * GB_BK / 8 / 256;      // 16-byte chunks per thread per tile
+    constexpr int WCH = BN * GB_BK / 8 / 256;
+    constexpr int A_EL = GB_BM * GB_LDK, W_EL = BN * GB_LDK;
+    constexpr int CLD = BN + 4;                       // fp32 output tile row stride
+    constexpr int OPER_B = 2 * (A_EL + W_EL) * 2, OUT_B = GB_BM * CLD * 4;
+    __shared__ __align__(16) unsigned char smem[OPER_B > OUT_B ? OPER_B : OUT_B];
+    uint16_t* const As = (uint16_t*)smem;             // [2][GB_BM][GB_LDK]
+    uint16_t* const Ws = As + 2 * A_EL;               // [2][BN][GB_LDK]
+    float* const Cs = (float*)smem;                   // [GB_BM][CLD] after the last product
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * GB_BM;
+    const int K = a.K;
+    const uint16_t* Ab = a.abf;
+    const uint16_t* Wb = (const uint16_t*)a.W;
+    u32x4 ar[ACH], wr[WCH];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < ACH; ++j) {
+            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
+            const int grow = min(m0 + row, a.R - 1);   // rows past R are computed and dropped
+            ar[j] = *(const u32x4*)(Ab + (int64_t)grow * K + k0 + kc);
+        }
+#pragma unroll
+        for (int j = 0; j < WCH; ++j) {
+            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
+            wr[j] = *(const u32x4*)(Wb + (int64_t)(n0 + row) * K + k0 + kc);
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < ACH; ++j) {
+            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
+            *(u32x4*)&As[buf * A_EL + row * GB_LDK + kc] = ar[j];
+        }
+#pragma unroll
+        for (int j = 0; j < WCH; ++j) {
+            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
+            *(u32x4*)&Ws[buf * W_EL + row * GB_LDK + kc] = wr[j];
+        }
+    };
+    f32x4_t acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[i][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    const int nk = K / GB_BK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * GB_BK);
+        const uint16_t* Ab_l = As + buf * A_EL;
+        const uint16_t* Wb_l = Ws + buf * W_EL;
+#pragma unroll
+        for (int ks = 0; ks < GB_BK; ks += 32) {
+            bf16x8_t af[MT], bfr[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                af[i] = __builtin_bit_cast(
+                    bf16x8_t, *(const u32x4*)&Ab_l[(wm * 64 + i * 16 + (lane & 15)) * GB_LDK + ks + 8 * (lane >> 4)]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                bfr[t] = __builtin_bit_cast(
+                    bf16x8_t, *(const u32x4*)&Wb_l[(wn * WN + t * 16 + (lane & 15)) * GB_LDK + ks + 8 * (lane >> 4)]);
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
+        }
+        if (kt + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+    // the output tile goes through LDS (the operand buffers are free now), so that the
+    // epilogue runs as one compact loop with coalesced stores
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Cs[(wm * 64 + i * 16 + 4 * (lane >> 4) + e) * CLD + wn * WN + t * 16 + (lane & 15)] = acc[i][t][e];
+    __syncthreads();
+    const int rows = min(GB_BM, a.R - m0);
+    for (int idx = tid; idx < rows * (BN / 2); idx += 256) {
+        const int r = idx / (BN / 2), c = 2 * (idx - r * (BN / 2));
+        const float2 v = *(const float2*)&Cs[r * CLD + c];
+        epi_pair_t<EPI>(a, m0 + r, n0 + c, v.x, v.y);
+    }
+}
+
+template <int BN>
+static void launch_gemm_bf16_bn(const GemmArgs& a, dim3 grid, hipStream_t st) {
+    if (a.head) {
+        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE>), grid, dim3(256), 0, st, a);
+        return;
+    }
+    switch (a.epi) {
+        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE>), grid, dim3(256), 0, st, a); break;
+        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID>), grid, dim3(256), 0, st, a); break;
+        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU>), grid, dim3(256), 0, st, a); break;
+        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV>), grid, dim3(256), 0, st, a); break;
+        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU>), grid, dim3(256), 0, st, a); break;
+    }
+}
+
+bool gemm_uses_bf16_rows(const GemmArgs& a) {
+    return a.wbf16 && a.abf && a.mfma_min_rows > 0 && a.R >= GB_MIN_ROWS && a.N % 64 == 0 && a.K % GB_BK == 0 &&
+           !a.comb;
+}
 
 // ------------------------------------------------------------------------------------------
 // Decode-sized products, K split across the waves of a block.
@@ -814,10 +988,10 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
             gn[s2][4] = g1.x; gn[s2][5] = g1.y; gn[s2][6] = g1.z; gn[s2][7] = g1.w;
         }
     }
-    uint4 wv[S];
+    u32x4 wv[S];
     const uint16_t* wp = (const uint16_t*)a.W + (int64_t)(n0 + (lane & 15)) * K + kb;
 #pragma unroll
-    for (int s2 = 0; s2 < S; ++s2) wv[s2] = *(const uint4*)(wp + 32 * s2);
+    for (int s2 = 0; s2 < S; ++s2) wv[s2] = *(const u32x4*)(wp + 32 * s2);
 
     float ss[MT];
     bf16x8_t af[MT][S];
@@ -890,6 +1064,12 @@ static bool use_mfma(const GemmArgs& a) {
            (a.norm_w == nullptr || a.rms_ws != nullptr);
 }
 
+hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st) {
+    if (!gemm_uses_bf16_rows(a)) return hipErrorInvalidValue;
+    NV_LAUNCH(k_rows_bf16, dim3(a.R), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.norm_w, a.eps, a.abf);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.R <= 0) return hipSuccess;
     const int epc = a.wbf16 ? 8 : 4;
@@ -957,6 +1137,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
                 return hipGetLastError();
             }
         }
+    }
+    if (gemm_uses_bf16_rows(a)) {
+        if (!a.abf_ready) {
+            NV_LAUNCH(k_rows_bf16, dim3(a.R), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.norm_w, a.eps,
+                      a.abf);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const unsigned mt = (unsigned)((a.R + GB_BM - 1) / GB_BM);
+        const bool wide = a.N % 128 == 0 && (a.N / 128) * (long)mt >= 512;
+        if (t_ev_stop)
+            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d>(nv::GemmArgs)",
+                     a.abf_ready ? "" : "nv::k_rows_bf16 + ", wide ? 128 : 64, a.head ? 1 : 0,
+                     a.head ? (int)EPI_STORE : a.epi);
+        if (wide) launch_gemm_bf16_bn<128>(a, dim3(a.N / 128, mt), st);
+        else launch_gemm_bf16_bn<64>(a, dim3(a.N / 64, mt), st);
+        return hipGetLastError();
     }
     if (use_mfma(a)) {
         if (a.norm_w) {
@@ -1152,7 +1349,7 @@ constexpr int AM_ROWS = 64;   // rows per item
 constexpr int AM_KT = 64;     // keys per tile
 
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_mfma(const AttnItem* items, const RowInfo* rows, const float* q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(const AttnItem* items, const RowInfo* rows, const float* q,
                                                    const uint16_t* kv, int layer, LayerDims D, float* part_ml,
                                                    float* part_o, float* out) {
     constexpr int KLD = HD + 8;         // K tile row stride (bf16)
@@ -1193,26 +1390,27 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const AttnItem* items, const 
         }
     }
 
-    uint4 kr[CPT], vr[CPT];
-    auto gload = [&](int t0) {
+    u32x4 kr[CPT], vr[CPT];
+    auto gload = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = tid + 256 * j;
             const int key = min(t0 + c / CPR, it.hi - 1);   // rows past the range are masked
             const int col = (c % CPR) * 8;
-            kr[j] = *(const uint4*)(Kg + (int64_t)key * HD + col);
-            vr[j] = *(const uint4*)(Vg + (int64_t)key * HD + col);
+            kr[j] = *(const u32x4*)(Kg + (int64_t)key * HD + col);
+            vr[j] = *(const u32x4*)(Vg + (int64_t)key * HD + col);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = tid + 256 * j;
             const int key = c / CPR, col = (c % CPR) * 8;
-            *(uint4*)&Ks[buf][key * KLD + col] = kr[j];
-            const uint16_t* v = (const uint16_t*)&vr[j];
+            *(u32x4*)&Ks[buf][key * KLD + col] = kr[j];
+            const uint32_t w4[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Vt[buf][(col + e) * VLD + key] = v[e];
+            for (int e = 0; e < 8; ++e)
+                Vt[buf][(col + e) * VLD + key] = (uint16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
         }
     };
 

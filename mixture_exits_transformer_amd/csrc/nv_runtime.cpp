@@ -78,7 +78,7 @@ struct Plan {
     size_t embed = 0, layer_w = 0, exit_w = 0, shared_head = 0;
     size_t hidden = 0, kv = 0, rope = 0;
     int R_max = 0, part_cap = 0, items_cap = 0;
-    size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0;
+    size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0, abf = 0;
     size_t tables = 0, small = 0, logits = 0, router_hid = 0;
     size_t seg = 0;     // persistent segment kernel: tagged exchange buffers, counters, layer table
     int loss_ch = 0;    // mixture objective: rows per head pass
@@ -173,6 +173,7 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.part_ml = align_up((size_t)p.part_cap * 2 * 4);
     p.part_o = align_up((size_t)p.part_cap * hd * 4);
     p.rms = align_up(rmax * 4);
+    p.abf = align_up(rmax * std::max(d, F) * 2);
     p.tables = align_up(rmax * sizeof(RowInfo) * 2 + rmax * sizeof(CombineInfo) +
                         (size_t)p.items_cap * sizeof(AttnItem) + rmax * 4);
     // uniforms, router outputs, stop flags, tokens in/out, head lists
@@ -187,8 +188,8 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.loss = align_up((size_t)p.loss_ch * V * 4) + 4 * align_up((size_t)max_ctx * 32) + align_up(64) +
              2 * align_up((size_t)max_ctx * 4) + align_up((size_t)max_ctx * sizeof(RowInfo)) +
              align_up((size_t)p.loss_ch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
-    p.total = p.loss + p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head + p.hidden + p.kv +
-              p.rope + p.qbuf + p.attn_o +
+    p.total = p.abf + p.loss + p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head +
+              p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
               p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
     return p;
 }
@@ -220,6 +221,7 @@ struct nv_model {
     float* part_ml = nullptr;
     float* part_o = nullptr;
     float* rms_ws = nullptr;   // [R_max] per-row inverse RMS for the matrix-core GEMM
+    uint16_t* abf = nullptr;   // [R_max][max(d, F)] bf16 rows for the long-chunk GEMM
     double* router_hid = nullptr;   // [max_batch][router_dim] router MLP hidden units
     // mixture objective over one sequence of up to max_ctx tokens (rows = positions)
     float* loss_logits = nullptr;   // [loss_ch][V]
@@ -428,6 +430,15 @@ double gemm_bytes(const nv_model* m, const GemmArgs& g) {
         if (s_ != NV_OK) return s_;       \
     } while (0)
 
+// One product, timed; on the long-chunk path the bf16 row pass is timed as its own launch.
+nv_status run_gemm(nv_model* m, int kind, GemmArgs g) {
+    if (gemm_uses_bf16_rows(g)) {
+        NV_TRY(timed(m, kind, (double)g.R * g.K * 6, [&] { return launch_rows_bf16(g, m->st); }, "nv::k_rows_bf16"));
+        g.abf_ready = 1;
+    }
+    return timed(m, kind, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); });
+}
+
 // The work stream was synchronised: every async copy from a pinned staging buffer is done.
 void stream_synced(nv_model* m) {
     m->stage_busy = false;
@@ -618,6 +629,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.wbf16 = m->bf16 ? 1 : 0;
         g.R = t.R;
         g.rms_ws = m->rms_ws;
+        g.abf = m->abf;
         g.mfma_min_rows = m->mfma_min_rows;
         // q, k, v = RMSNorm(x) W_qkv^T
         g.A = m->Hs;
@@ -636,7 +648,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.rope = m->rope;
         g.layer = l;
         g.D = D;
-        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+        NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
         if (t.dec) {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                 return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
@@ -683,7 +695,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->Hs;
         g.ldo = d;
         g.o_rows = t.rows;
-        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+        NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
         g.comb = nullptr;
         // u = silu(RMSNorm(x) W_g^T) * (RMSNorm(x) W_u^T)
         g.A = m->Hs;
@@ -697,7 +709,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->mlp;
         g.ldo = m->F;
         g.o_rows = nullptr;
-        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+        NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
         // x += u W_d^T
         g.A = m->mlp;
         g.lda = m->F;
@@ -710,7 +722,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->Hs;
         g.ldo = d;
         g.o_rows = t.rows;
-        NV_TRY(timed(m, NV_TIME_BLOCK_GEMM, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+        NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
     }
     return NV_OK;
 }
@@ -1056,6 +1068,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->part_ml = (float*)m->take(P.part_ml);
     m->part_o = (float*)m->take(P.part_o);
     m->rms_ws = (float*)m->take(P.rms);
+    m->abf = (uint16_t*)m->take(P.abf);
     if (const char* e = std::getenv("NVIUM_MFMA_MIN_ROWS")) m->mfma_min_rows = std::atoi(e);
     m->d_tables = m->take(P.tables);
     m->d_stepblk = m->take(m->stepblk_bytes());
@@ -1267,6 +1280,7 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
     g.eps = m->cfg.norm_eps;
     g.wbf16 = m->bf16 ? 1 : 0;
     g.rms_ws = m->rms_ws;
+    g.abf = m->abf;
     g.mfma_min_rows = m->mfma_min_rows;
     if (m->cfg.head_form == 1) {
         float* X = m->attn_o;   // [ns][d] gathered rows, then adapter outputs
@@ -1290,7 +1304,7 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
                 a.epi = EPI_SILU;
                 a.out = S + (int64_t)j0 * r;
                 a.ldo = r;
-                NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, a), [&] { return launch_gemm(a, m->st); }));
+                NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, a));
                 GemmArgs b = g;
                 b.A = S + (int64_t)j0 * r;
                 b.lda = r;
@@ -1301,7 +1315,7 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
                 b.epi = EPI_RESID;
                 b.out = X + (int64_t)j0 * d;
                 b.ldo = d;
-                NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, b), [&] { return launch_gemm(b, m->st); }));
+                NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, b));
             }
             j0 = j1;
         }
@@ -1323,7 +1337,7 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
     g.ldo = m->V;
     g.o_rows = m->lorows(m->d_headlist);
     g.head = 1;
-    NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+    NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, g));
     NV_TRY(timed(m, NV_TIME_OTHER, (double)ns * m->V * 4, [&] {
         return launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif, m->d_tok_out,
                              m->st);
@@ -1663,6 +1677,7 @@ static nv_status loss_exit(nv_model* m, int sg, int o, int k) {
     g.eps = m->cfg.norm_eps;
     g.wbf16 = m->bf16 ? 1 : 0;
     g.rms_ws = m->rms_ws;
+    g.abf = m->abf;
     g.mfma_min_rows = m->mfma_min_rows;
     const int d = m->d;
     if (m->cfg.head_form == 1) {
@@ -1682,7 +1697,7 @@ static nv_status loss_exit(nv_model* m, int sg, int o, int k) {
             a.epi = EPI_SILU;
             a.out = m->mlp;
             a.ldo = r;
-            NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, a), [&] { return launch_gemm(a, m->st); }));
+            NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, a));
             GemmArgs b = g;
             b.A = m->mlp;
             b.lda = r;
@@ -1693,7 +1708,7 @@ static nv_status loss_exit(nv_model* m, int sg, int o, int k) {
             b.epi = EPI_RESID;
             b.out = A;
             b.ldo = d;
-            NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, b), [&] { return launch_gemm(b, m->st); }));
+            NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, b));
         }
         g.A = A;
         g.lda = d;
@@ -1711,7 +1726,7 @@ static nv_status loss_exit(nv_model* m, int sg, int o, int k) {
     g.out = m->loss_logits;
     g.ldo = m->V;
     g.head = 1;
-    NV_TRY(timed(m, NV_TIME_EXIT_HEAD, gemm_bytes(m, g), [&] { return launch_gemm(g, m->st); }));
+    NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, g));
     NV_TRY(timed(m, NV_TIME_OTHER, (double)k * m->V * 4, [&] {
         return launch_xent(m->loss_logits, m->V, k, m->V, m->loss_tgt + o, m->loss_lp + (int64_t)o * 4, 4, sg, m->st);
     }, "nv::k_xent"));

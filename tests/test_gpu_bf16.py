@@ -90,3 +90,26 @@ def test_mfma_and_valu_paths_agree(lib, weights_dir, monkeypatch):
             lib.nv_free(h)
     for (k1, v1), (k2, v2) in zip(*kvs):
         assert rel(k1, k2) < 1e-2 and rel(v1, v2) < 1e-2
+
+
+def test_long_chunk_gemm_paths_agree(lib, weights_dir, monkeypatch):
+    """A 300-row prefill through the long-chunk bf16 GEMM (rows normalised and rounded
+    once, 128-row tiles; 3 row tiles with a ragged 44-row tail) and through the
+    vector-ALU GEMM gives the same KV and hidden states to bf16 rounding."""
+    path = cached_weights(BF16_TINY, weights_dir)
+    rng = np.random.default_rng(6)
+    prompt = rng.integers(0, BF16_TINY.vocab, size=301)
+    outs = []
+    for thr in ("16", "0"):
+        monkeypatch.setenv("NVIUM_MFMA_MIN_ROWS", thr)
+        h = lib.nv_load(path, 1, 320)
+        try:
+            lib.nv_prefill(h, 0, prompt)
+            kv = [lib.nv_debug_kv(h, 0, l, 0, 300) for l in range(BF16_TINY.n_layers)]
+            outs.append((kv, lib.nv_debug_hidden(h, 0, 0, 300)))
+        finally:
+            lib.nv_free(h)
+    (kv1, h1), (kv2, h2) = outs
+    for (k1, v1), (k2, v2) in zip(kv1, kv2):
+        assert rel(k1, k2) < 1e-2 and rel(v1, v2) < 1e-2
+    assert rel(h1, h2) < 1e-2
