@@ -69,6 +69,18 @@ def counted_traffic(kname):
     return None
 
 
+def calibration_copy(out):
+    """One 1 GiB device-to-device copy after the timed work: the reference that scales the
+    HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a profiled run."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    out["calibration_copy_bytes"] = 1 << 30
+
+
 def run_decode(lib, h, prompt, U, steps, warmup):
     """Warm up, restart the sequence, then time `steps` decode steps."""
     import torch
@@ -171,15 +183,21 @@ def bench_loss(args, wl):
     lib.nv_free(h)
     m = wl.model
     d, F, Lr, V, r = m.d_model, m.ffn, m.n_layers, m.vocab, n - 1
-    # dominant kernel: the block-GEMM symbol with the most device time.  The long-chunk
+    # dominant kernel: the block-GEMM product symbol with the most device time.  The long-chunk
     # GEMM is instantiated per epilogue (template argument EPI: 1 residual = O and down,
     # 2 SwiGLU = gate/up, 3 QKV), so each symbol's algorithmic FLOPs follow from it.
     per_epi = {1: 2.0 * r * Lr * (d * d + F * d), 2: 2.0 * r * Lr * 2 * F * d, 3: 2.0 * r * Lr * 3 * d * d}
-    gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
+    gemms = sorted([k for k in ker if k[0] == "block_gemm" and "k_gemm_bf16<" in k[4]], key=lambda k: -k[2])
     _, nl, ms, by, kname = gemms[0]
     epi = int(kname.split("k_gemm_bf16<")[1].split(">")[0].split(",")[2]) if "k_gemm_bf16<" in kname else None
     assert epi in per_epi, f"dominant block GEMM {kname} is not the long-chunk kernel"
     flops = per_epi[epi]
+    # algorithmic bytes: weights once, the bf16 rows, the outputs (fp32; read and written
+    # for a residual; q in fp32 and K, V in bf16 for QKV)
+    per_epi_bytes = {1: Lr * (2 * d * d + 2 * d * F + r * d * 2 + r * F * 2 + 2 * r * d * 8),
+                     2: Lr * (2 * F * d * 2 + r * d * 2 + r * F * 4),
+                     3: Lr * (3 * d * d * 2 + r * d * 2 + r * d * 4 + r * 2 * d * 2)}
+    bytes_per_launch = per_epi_bytes[epi] / nl
     achieved = flops / (ms * 1e-3) / 1e12
     all_flops = 2.0 * r * Lr * (4 * d * d + 3 * d * F)
     counted = counted_traffic(kname)
@@ -204,7 +222,7 @@ def bench_loss(args, wl):
                      "traffic": counted[0] if counted else None,
                      "traffic_source": counted[1] if counted else None,
                      "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
-                     "flops_per_launch": round(flops / max(nl, 1))},
+                     "flops_per_launch": round(flops / max(nl, 1)), "bytes_per_launch": round(bytes_per_launch)},
         "block_gemm_all_TFLOPs": round(all_flops / (tim["block_gemm"][0] * 1e-3) / 1e12, 1),
         "pass_TFLOPs": round(total_flops / (dt / steps) / 1e12, 1),
         "L": [round(x, 6) for x in L],
@@ -214,6 +232,8 @@ def bench_loss(args, wl):
     }
     if not args.no_cpu:
         out["cpu_baseline"] = loss_cpu_baseline(path, tokens, args.cpu_loss_tokens)
+    if args.calibrate_copy:
+        calibration_copy(out)
     print(json.dumps(out), flush=True)
 
 
@@ -324,6 +344,8 @@ def bench_batch(args, wl):
         cb = cpu_baseline(wl, path, ps[j], Ut[j], args.cpu_budget)
         cb["sample"] = f"sequence {j} alone: " + cb["sample"]
         out["cpu_baseline"] = cb
+    if args.calibrate_copy:
+        calibration_copy(out)
     print(json.dumps(out), flush=True)
 
 
@@ -426,12 +448,7 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, path, prompt, U[:steps], args.cpu_budget)
     if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["calibration_copy_bytes"] = 1 << 30
+        calibration_copy(out)
     print(json.dumps(out), flush=True)
 
 

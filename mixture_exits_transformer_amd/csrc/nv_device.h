@@ -83,6 +83,19 @@ __device__ __forceinline__ void stamp_end(unsigned long long* stamp, unsigned lo
     }
 }
 
+// As stamp_end for a grid of any shape: block (x, y) stores at its linear index, if that
+// index is below `cap`.
+__device__ __forceinline__ void stamp_end_lin(unsigned long long* stamp, unsigned long long t0, int cap) {
+    if (stamp) {
+        __syncthreads();
+        const int b = blockIdx.y * gridDim.x + blockIdx.x;
+        if (threadIdx.x == 0 && b < cap) {
+            stamp[2 * b] = t0;
+            stamp[2 * b + 1] = (unsigned long long)wall_clock64();
+        }
+    }
+}
+
 // Sum N values per lane over the 64 lanes of a wave.  Transposed reduction: each step
 // halves the values a lane keeps (exchanging the other half with the partner lane), so
 // after log2(N) steps lane L holds one value and a final butterfly finishes the sum.

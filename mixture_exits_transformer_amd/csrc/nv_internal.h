@@ -139,7 +139,7 @@ void set_launch_events(hipEvent_t start, hipEvent_t stop);
 const char* last_launch_name();   // symbol of the last kernel issued while timing
 // Timing: block-stamp buffer the next stamped kernels write (nullptr: none).
 void set_launch_stamp(unsigned long long* stamps);
-constexpr int STAMP_BLOCKS = 8192;  // largest grid the timing stamps cover
+constexpr int STAMP_BLOCKS = 65536;  // largest grid the timing stamps cover
 unsigned long long* current_launch_stamp();
 void current_launch_events(hipEvent_t* start, hipEvent_t* stop);
 

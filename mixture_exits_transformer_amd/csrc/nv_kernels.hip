@@ -662,6 +662,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     uint16_t* const As = (uint16_t*)smem;             // [2][GB_BM][GB_LDK]
     uint16_t* const Ws = As + 2 * A_EL;               // [2][BN][GB_LDK]
     float* const Cs = (float*)smem;                   // [GB_BM][CLD] after the last product
+    const unsigned long long t_begin = stamp_begin(a.stamp);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * GB_BM;
@@ -744,6 +745,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         const float2 v = *(const float2*)&Cs[r * CLD + c];
         epi_pair_t<EPI>(a, m0 + r, n0 + c, v.x, v.y);
     }
+    stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
 }
 
 template <int BN>
@@ -1151,8 +1153,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
             snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d>(nv::GemmArgs)",
                      a.abf_ready ? "" : "nv::k_rows_bf16 + ", wide ? 128 : 64, a.head ? 1 : 0,
                      a.head ? (int)EPI_STORE : a.epi);
-        if (wide) launch_gemm_bf16_bn<128>(a, dim3(a.N / 128, mt), st);
-        else launch_gemm_bf16_bn<64>(a, dim3(a.N / 64, mt), st);
+        if (wide) launch_gemm_bf16_bn<128>(b, dim3(a.N / 128, mt), st);
+        else launch_gemm_bf16_bn<64>(b, dim3(a.N / 64, mt), st);
         return hipGetLastError();
     }
     if (use_mfma(a)) {
@@ -1349,9 +1351,10 @@ constexpr int AM_ROWS = 64;   // rows per item
 constexpr int AM_KT = 64;     // keys per tile
 
 template <int HD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(const AttnItem* items, const RowInfo* rows, const float* q,
-                                                   const uint16_t* kv, int layer, LayerDims D, float* part_ml,
-                                                   float* part_o, float* out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(
+    const AttnItem* items, const RowInfo* rows, const float* q, const uint16_t* kv, int layer, LayerDims D,
+    float* part_ml, float* part_o, float* out, unsigned long long* stamp) {
+    const unsigned long long t_begin = stamp_begin(stamp);
     constexpr int KLD = HD + 8;         // K tile row stride (bf16)
     constexpr int VLD = AM_KT + 8;      // transposed V tile row stride (bf16)
     constexpr int NKS = HD / 32;        // k-steps of the score product
@@ -1487,23 +1490,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    if (!rv) return;
-    if (it.nsplit == 1) {
+    if (rv && it.nsplit == 1) {
         const float inv = 1.0f / lsum;
         float* orow = out + (int64_t)(it.row0 + r) * D.d + it.head * HD;
 #pragma unroll
         for (int t = 0; t < NHT; ++t)
             *(float4*)(orow + 16 * t + 4 * g) = make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
-        return;
-    }
-    const int64_t slot = it.part + r;
-    if (g == 0) {
-        part_ml[2 * slot] = m;
-        part_ml[2 * slot + 1] = lsum;
-    }
-    float* po = part_o + slot * HD;
+    } else if (rv) {
+        const int64_t slot = it.part + r;
+        if (g == 0) {
+            part_ml[2 * slot] = m;
+            part_ml[2 * slot + 1] = lsum;
+        }
+        float* po = part_o + slot * HD;
 #pragma unroll
-    for (int t = 0; t < NHT; ++t) *(float4*)(po + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+        for (int t = 0; t < NHT; ++t) *(float4*)(po + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+    }
+    stamp_end_lin(stamp, t_begin, STAMP_BLOCKS);
 }
 
 bool attn_mfma_ok(const LayerDims& D) { return D.kv_bf16 && (D.hd == 32 || D.hd == 64 || D.hd == 128); }
@@ -1515,13 +1518,13 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
     const uint16_t* k16 = (const uint16_t*)kv;
     if (D.hd == 128)
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out);
+                  part_ml, part_o, out, t_stamp);
     else if (D.hd == 64)
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out);
+                  part_ml, part_o, out, t_stamp);
     else
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out);
+                  part_ml, part_o, out, t_stamp);
     return hipGetLastError();
 }
 
