@@ -945,24 +945,26 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 // Activation fragments (rows l%16 of each tile, k 8*(l/16)..) are loaded first, scaled by
 // g, rounded to bf16; weight fragments W[n0 + l%16][k ...] follow.  Partial tiles of the
 // waves are summed through LDS.
-template <int S, int MT, bool NORM, int HEAD>
+template <int S, int MT, int NT, bool NORM, int HEAD>
 __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
-    __shared__ float red[16][MT][64][4];
+    __shared__ float red[16][MT][NT][64][4];
     __shared__ float ssr[16][MT * 16];
     const unsigned long long t_begin = stamp_begin(a.stamp);
     const int K = a.K, R = a.R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * NT;
     const int kq = 8 * (lane >> 4);
     const int kb = wave * (32 * S) + kq;   // host: K == nw * 32 * S
 
-    // epilogue context for the rows this lane finishes (waves < MT own one tile each)
+    // epilogue context for the rows this lane finishes (waves < MT * NT own one
+    // (row tile, column tile) each)
     EpiCtx ectx[4];
-    const int ecol = n0 + (lane & 15);
-    if (wave < MT && (ecol & 1) == 0) {
+    const int emt = wave / NT, ent = wave - (wave / NT) * NT;
+    const int ecol = n0 + ent * 16 + (lane & 15);
+    if (wave < MT * NT && (ecol & 1) == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = wave * 16 + 4 * (lane >> 4) + i;
+            const int row = emt * 16 + 4 * (lane >> 4) + i;
             if (row < R) ectx[i] = epi_prepare(a, row, ecol);
         }
     }
@@ -990,10 +992,13 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
             gn[s2][4] = g1.x; gn[s2][5] = g1.y; gn[s2][6] = g1.z; gn[s2][7] = g1.w;
         }
     }
-    u32x4 wv[S];
-    const uint16_t* wp = (const uint16_t*)a.W + (int64_t)(n0 + (lane & 15)) * K + kb;
+    u32x4 wv[NT][S];
 #pragma unroll
-    for (int s2 = 0; s2 < S; ++s2) wv[s2] = *(const u32x4*)(wp + 32 * s2);
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint16_t* wp = (const uint16_t*)a.W + (int64_t)(n0 + nt * 16 + (lane & 15)) * K + kb;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) wv[nt][s2] = *(const u32x4*)(wp + 32 * s2);
+    }
 
     float ss[MT];
     bf16x8_t af[MT][S];
@@ -1019,32 +1024,39 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
             af[mt][s2] = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
         }
     }
-    f32x4_t acc[MT];
+    f32x4_t acc[MT][NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
-        const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, wv[s2]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt][s2], bf, acc[mt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, wv[nt][s2]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt][s2], bf, acc[mt][nt], 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][mt][lane][i] = acc[mt][i];
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][mt][nt][lane][i] = acc[mt][nt][i];
         float t = ss[mt];
         t += __shfl_xor(t, 16, 64);
         t += __shfl_xor(t, 32, 64);
         if (lane < 16) ssr[wave][mt * 16 + lane] = t;
     }
     __syncthreads();
-    if (wave < MT) {
-        const int mt = wave;
+    if (wave < MT * NT) {
+        const int mt = emt;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         for (int ww = 0; ww < nw; ++ww)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] += red[ww][mt][lane][i];
+            for (int i = 0; i < 4; ++i) v[i] += red[ww][mt][ent][lane][i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mt * 16 + 4 * (lane >> 4) + i;
@@ -1115,11 +1127,18 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
             }
         if (S > 0) {
             const int nw = a.K / (32 * S);
-            const dim3 grid(a.N / 16), block(64 * nw);
+            // two column tiles per block when one tile per block would take more than one
+            // round of blocks (a block of 16 waves fills a CU)
+            const int ntv = (a.N % 32 == 0 && a.N / 16 > 256) ? 2 : 1;
+            const dim3 grid(a.N / (16 * ntv)), block(64 * nw);
+#define NV_MKS3(SV, MTV, NTV, NV_)                                                                             \
+    do {                                                                                                      \
+        if (a.head) NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NTV, NV_, 1>), grid, block, 0, st, b); \
+        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NTV, NV_, 0>), grid, block, 0, st, b);        \
+    } while (0)
 #define NV_MKS2(SV, MTV, NV_)                                                                                  \
     do {                                                                                                      \
-        if (a.head) NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 1>), grid, block, 0, st, b); \
-        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_mfma_ks<SV, MTV, NV_, 0>), grid, block, 0, st, b);        \
+        if (ntv == 2) NV_MKS3(SV, MTV, 2, NV_); else NV_MKS3(SV, MTV, 1, NV_);                              \
     } while (0)
 #define NV_MKS(SV, MTV)                                                                                        \
     do {                                                                                                      \
@@ -1127,8 +1146,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     } while (0)
             if (nw >= 2 || a.R <= 16) {
                 if (t_ev_stop)
-                    snprintf(t_name, sizeof(t_name), "void nv::k_gemm_mfma_ks<%d, %d, %s, %d>(nv::GemmArgs)", S,
-                             a.R <= 16 ? 1 : 2, a.norm_w ? "true" : "false", a.head ? 1 : 0);
+                    snprintf(t_name, sizeof(t_name), "void nv::k_gemm_mfma_ks<%d, %d, %d, %s, %d>(nv::GemmArgs)", S,
+                             a.R <= 16 ? 1 : 2, ntv, a.norm_w ? "true" : "false", a.head ? 1 : 0);
                 if (a.R <= 16) {
                     if (S == 3) NV_MKS(3, 1); else if (S == 8) NV_MKS2(8, 1, false); else NV_MKS(1, 1);
                 } else {
@@ -1136,6 +1155,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
                 }
 #undef NV_MKS
 #undef NV_MKS2
+#undef NV_MKS3
                 return hipGetLastError();
             }
         }
