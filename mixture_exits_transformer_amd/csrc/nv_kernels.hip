@@ -1548,13 +1548,13 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
     return hipGetLastError();
 }
 
-// Merge the split partials of one (row, head): the (max, sum) pairs of its splits are
-// staged in LDS, turned into weights exp(max - M), and each thread forms the weighted sum
-// of one output dim with independent loads.  Rows whose key range was not split were
-// written by the attention kernel and are skipped.
+// Decode-sized groups (few (row, head) pairs, possibly many splits): one block per pair;
+// the (max, sum) pairs of its splits are staged in LDS and turned into weights by one
+// thread, then each thread forms one output dim with independent loads.
 constexpr int COMB_MAX = 4096;   // splits of one (row, head) held in LDS
+constexpr int COMB_WAVE_MIN_PAIRS = 2048;   // (row, head) pairs from which one wave per pair is used
 
-__global__ __launch_bounds__(128) void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
+__global__ __launch_bounds__(128) void k_attn_combine_blk(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
                                                       const float* part_o, float* out, unsigned long long* stamp) {
     const unsigned long long t_begin = stamp_begin(stamp);
     __shared__ float w[COMB_MAX];
@@ -1595,6 +1595,43 @@ __global__ __launch_bounds__(128) void k_attn_combine(const CombineInfo* ci, int
     stamp_end(stamp, t_begin);
 }
 
+
+// Merge the split partials of one (row, head), one wave each (four per block): every lane
+// folds the (max, sum) pairs of all splits (the max first, then the weights exp(max - M)),
+// then forms two output dims as the weighted sum of the splits' partial outputs.  Rows
+// whose key range was not split were written by the attention kernel and are skipped.
+__global__ __launch_bounds__(256) void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
+                                                      const float* part_o, float* out, unsigned long long* stamp) {
+    const unsigned long long t_begin = stamp_begin(stamp);
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p < R * D.H) {
+        const int i = p / D.H, h = p - i * D.H;
+        const CombineInfo c = ci[i];
+        if (c.nsplit > 1) {
+            const int ns = c.nsplit, hd = D.hd;
+            const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
+            float M = -INFINITY;
+            for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
+            float L = 0.f, o0 = 0.f, o1 = 0.f;
+            const int e = 2 * lane;
+            for (int sp = 0; sp < ns; ++sp) {
+                const int64_t slot = base + (int64_t)sp * c.nrows;
+                const float2 ml = *(const float2*)(part_ml + 2 * slot);
+                const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
+                L += w * ml.y;
+                if (e < hd) {
+                    const float2 v = *(const float2*)(part_o + slot * hd + e);
+                    o0 += w * v.x;
+                    o1 += w * v.y;
+                }
+            }
+            if (e < hd) *(float2*)(out + (int64_t)i * D.d + h * hd + e) = make_float2(o0 / L, o1 / L);
+        }
+    }
+    stamp_end(stamp, t_begin);
+}
+
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
                        int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st) {
     if (n_items <= 0) return hipSuccess;
@@ -1607,7 +1644,13 @@ hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, 
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,
                                const float* part_o, float* out, hipStream_t st) {
     if (R <= 0) return hipSuccess;
-    NV_LAUNCH(k_attn_combine, dim3(R * D.H), dim3(128), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
+    if (R * D.H >= COMB_WAVE_MIN_PAIRS) {
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_attn_combine");
+        NV_LAUNCH(k_attn_combine, dim3((R * D.H + 3) / 4), dim3(256), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
+    } else {
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_attn_combine_blk");
+        NV_LAUNCH(k_attn_combine_blk, dim3(R * D.H), dim3(128), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
+    }
     return hipGetLastError();
 }
 

@@ -184,7 +184,7 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
-    p.loss_ch = (int)std::min<size_t>(128, rmax);
+    p.loss_ch = (int)std::min<size_t>(256, rmax);
     p.loss = align_up((size_t)p.loss_ch * V * 4) + 4 * align_up((size_t)max_ctx * 32) + align_up(64) +
              2 * align_up((size_t)max_ctx * 4) + align_up((size_t)max_ctx * sizeof(RowInfo)) +
              align_up((size_t)p.loss_ch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
@@ -658,7 +658,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             if (t.any_split && !fuse_merge(m, t))
                 NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
                     return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-                }, "nv::k_attn_combine"));
+                }));
         } else if (attn_mfma_ok(D)) {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
                 return launch_attn_mfma(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o,
@@ -666,7 +666,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             }, "nv::k_attn_mfma"));
             NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
                 return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-            }, "nv::k_attn_combine"));
+            }));
         } else {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
                 return launch_attn(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o, m->attn_o,
@@ -674,7 +674,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             }, "nv::k_attn"));
             NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
                 return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-            }, "nv::k_attn_combine"));
+            }));
         }
         // x += o W_o^T
         g.epi = EPI_RESID;

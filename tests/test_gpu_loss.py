@@ -3,7 +3,7 @@ mixture_loss: L_mix, L_compute, L_total and every position's router outputs,
 log pi_k of the target, -log pi_mix and expected depth.
 
 - Tiny fp32 model, both exit forms (own heads + linear gate; shared head with adapters +
-  router MLP): 299 positions, i.e. head passes of 128, 128 and a ragged 43 rows.  Router
+  router MLP): 299 positions, i.e. head passes of 256 and a ragged 43 rows.  Router
   outputs within 1e-6, log-probabilities within 1e-4 absolute, the means within 1e-6
   relative.
 - The shortest sequence (two tokens, one position) and the argument errors.
