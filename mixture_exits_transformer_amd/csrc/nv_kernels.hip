@@ -1370,6 +1370,12 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
 constexpr int AM_ROWS = 64;   // rows per item
 constexpr int AM_KT = 64;     // keys per tile
 
+// Column swizzle of the transposed V tile: row r (one value dim) holds key k at column
+// k ^ vt_swz(r).  The mask is a multiple of 4, so aligned groups of four keys stay
+// contiguous for the 8-byte operand reads, and the 16 lanes that store one key into rows
+// 8 apart hit 16 different banks instead of 2.
+__device__ __forceinline__ int vt_swz(int r) { return ((r >> 3) & 15) * 4; }
+
 template <int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(
     const AttnItem* items, const RowInfo* rows, const float* q, const uint16_t* kv, int layer, LayerDims D,
@@ -1433,7 +1439,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             const uint32_t w4[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                Vt[buf][(col + e) * VLD + key] = (uint16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
+                Vt[buf][(col + e) * VLD + (key ^ vt_swz(col + e))] =
+                    (uint16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
         }
     };
 
@@ -1498,9 +1505,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
 #pragma unroll
             for (int t = 0; t < NHT; ++t) {
-                const uint16_t* vrow = &Vt[buf][(16 * t + qn) * VLD + 32 * ks + 4 * g];
-                const uint2 lo = *(const uint2*)vrow;
-                const uint2 hi = *(const uint2*)(vrow + 16);
+                const int vr_ = 16 * t + qn;
+                const uint16_t* vrow = &Vt[buf][vr_ * VLD];
+                const uint2 lo = *(const uint2*)(vrow + ((32 * ks + 4 * g) ^ vt_swz(vr_)));
+                const uint2 hi = *(const uint2*)(vrow + ((32 * ks + 16 + 4 * g) ^ vt_swz(vr_)));
                 const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pf, o[t], 0, 0, 0);
             }
