@@ -645,7 +645,10 @@ __global__ __launch_bounds__(256) void k_rows_bf16(const float* A, int64_t lda, 
     }
 }
 
-constexpr int GB_BM = 128, GB_BK = 64, GB_LDK = GB_BK + 8;
+constexpr int GB_BM = 128, GB_BK = 64, GB_LDK = GB_BK;
+// 16-byte chunk j of tile row r is stored at chunk j ^ gb_swz(r): the 8 lanes storing one
+// row and the 16 lanes reading one k-chunk of 16 rows then cover every LDS bank once.
+__device__ __forceinline__ int gb_swz(int r) { return (r >> 1) & 7; }
 constexpr int GB_MIN_ROWS = 33;    // chunks of at least this many rows use k_gemm_bf16
 
 template <int BN, int HEAD, int EPI>
@@ -686,13 +689,13 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < ACH; ++j) {
-            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
-            *(u32x4*)&As[buf * A_EL + row * GB_LDK + kc] = ar[j];
+            const int c = tid + 256 * j, row = c >> 3;
+            *(u32x4*)&As[buf * A_EL + row * GB_LDK + (((c & 7) ^ gb_swz(row)) << 3)] = ar[j];
         }
 #pragma unroll
         for (int j = 0; j < WCH; ++j) {
-            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
-            *(u32x4*)&Ws[buf * W_EL + row * GB_LDK + kc] = wr[j];
+            const int c = tid + 256 * j, row = c >> 3;
+            *(u32x4*)&Ws[buf * W_EL + row * GB_LDK + (((c & 7) ^ gb_swz(row)) << 3)] = wr[j];
         }
     };
     f32x4_t acc[MT][NT];
@@ -712,14 +715,19 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
         for (int ks = 0; ks < GB_BK; ks += 32) {
             bf16x8_t af[MT], bfr[NT];
+            const int kch = (ks >> 3) + (lane >> 4);     // 16-byte k-chunk of this lane
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-                af[i] = __builtin_bit_cast(
-                    bf16x8_t, *(const u32x4*)&Ab_l[(wm * 64 + i * 16 + (lane & 15)) * GB_LDK + ks + 8 * (lane >> 4)]);
+            for (int i = 0; i < MT; ++i) {
+                const int row = wm * 64 + i * 16 + (lane & 15);
+                af[i] = __builtin_bit_cast(bf16x8_t,
+                                           *(const u32x4*)&Ab_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
+            }
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                bfr[t] = __builtin_bit_cast(
-                    bf16x8_t, *(const u32x4*)&Wb_l[(wn * WN + t * 16 + (lane & 15)) * GB_LDK + ks + 8 * (lane >> 4)]);
+            for (int t = 0; t < NT; ++t) {
+                const int row = wn * WN + t * 16 + (lane & 15);
+                bfr[t] = __builtin_bit_cast(bf16x8_t,
+                                            *(const u32x4*)&Wb_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
+            }
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
