@@ -1564,53 +1564,63 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
     return hipGetLastError();
 }
 
-// Decode-sized groups (few (row, head) pairs, possibly many splits): one block per pair;
-// the (max, sum) pairs of its splits are staged in LDS and turned into weights by one
-// thread, then each thread forms one output dim with independent loads.
-constexpr int COMB_MAX = 4096;   // splits of one (row, head) held in LDS
+// Decode-sized groups (few (row, head) pairs, possibly many splits): one block of 512
+// threads per pair.  The split maxima and the weights exp(m_s - M) are formed by all
+// threads together (block reductions, weights kept in LDS); each value dim's weighted sum
+// is then spread over 512 / hd thread subsets that take every (512 / hd)-th split, and the
+// subsets are added in LDS.
+constexpr int COMB_MAX = 4096;   // splits of one (row, head) whose weights LDS holds
 constexpr int COMB_WAVE_MIN_PAIRS = 2048;   // (row, head) pairs from which one wave per pair is used
 
-__global__ __launch_bounds__(128) void k_attn_combine_blk(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
-                                                      const float* part_o, float* out, unsigned long long* stamp) {
+__global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci, int R, LayerDims D,
+                                                          const float* part_ml, const float* part_o, float* out,
+                                                          unsigned long long* stamp) {
     const unsigned long long t_begin = stamp_begin(stamp);
-    __shared__ float w[COMB_MAX];
-    __shared__ float ls[COMB_MAX];
-    __shared__ float lsum;
+    __shared__ float wsh[COMB_MAX];
+    __shared__ float red[512];
+    __shared__ float wred[8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = blockIdx.x / D.H, h = blockIdx.x - i * D.H;
     const CombineInfo c = ci[i];
-    if (c.nsplit == 1) {
-        stamp_end(stamp, t_begin);
-        return;
-    }
-    const int ns = c.nsplit, hd = D.hd;
-    const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // slot of split 0; split s adds s * nrows
-    for (int sp = threadIdx.x; sp < ns; sp += blockDim.x) {
-        const float2 ml = *(const float2*)(part_ml + 2 * (base + (int64_t)sp * c.nrows));
-        w[sp] = ml.x;
-        ls[sp] = ml.y;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, w[sp]);
-        float L = 0.f;
-        for (int sp = 0; sp < ns; ++sp) {
-            const float wt = w[sp] == -INFINITY ? 0.f : expf(w[sp] - M);
-            w[sp] = wt;
-            L += wt * ls[sp];
+    if (c.nsplit > 1) {
+        const int ns = c.nsplit, hd = D.hd;
+        const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
+        float mx = -INFINITY;
+        for (int sp = tid; sp < ns; sp += 512) mx = fmaxf(mx, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
+        mx = wave_max(mx);
+        if (lane == 0) wred[wave] = mx;
+        __syncthreads();
+        float M = wred[0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) M = fmaxf(M, wred[w]);
+        __syncthreads();
+        float ls = 0.f;
+        for (int sp = tid; sp < ns; sp += 512) {
+            const float2 ml = *(const float2*)(part_ml + 2 * (base + (int64_t)sp * c.nrows));
+            const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
+            wsh[sp] = w;
+            ls += w * ml.y;
         }
-        lsum = L;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < hd; e += blockDim.x) {
-        float O = 0.f;
-#pragma unroll 8
-        for (int sp = 0; sp < ns; ++sp) O += w[sp] * part_o[(base + (int64_t)sp * c.nrows) * hd + e];
-        out[(int64_t)i * D.d + h * hd + e] = O / lsum;
+        ls = wave_sum(ls);
+        if (lane == 0) wred[wave] = ls;
+        __syncthreads();
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) L += wred[w];
+        const int Q = 512 / hd, e = tid % hd, q = tid / hd;
+        float o = 0.f;
+#pragma unroll 4
+        for (int sp = q; sp < ns; sp += Q) o += wsh[sp] * part_o[(base + (int64_t)sp * c.nrows) * hd + e];
+        red[tid] = o;
+        __syncthreads();
+        if (tid < hd) {
+            float v = 0.f;
+            for (int qq = 0; qq < Q; ++qq) v += red[qq * hd + tid];
+            out[(int64_t)i * D.d + h * hd + tid] = v / L;
+        }
     }
     stamp_end(stamp, t_begin);
 }
-
 
 // Merge the split partials of one (row, head), one wave each (four per block): every lane
 // folds the (max, sum) pairs of all splits (the max first, then the weights exp(max - M)),
@@ -1665,7 +1675,7 @@ hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
         NV_LAUNCH(k_attn_combine, dim3((R * D.H + 3) / 4), dim3(256), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
     } else {
         if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_attn_combine_blk");
-        NV_LAUNCH(k_attn_combine_blk, dim3(R * D.H), dim3(128), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
+        NV_LAUNCH(k_attn_combine_blk, dim3(R * D.H), dim3(512), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
     }
     return hipGetLastError();
 }
