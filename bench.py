@@ -192,10 +192,11 @@ def bench_loss(args, wl):
     epi = int(kname.split("k_gemm_bf16<")[1].split(">")[0].split(",")[2]) if "k_gemm_bf16<" in kname else None
     assert epi in per_epi, f"dominant block GEMM {kname} is not the long-chunk kernel"
     flops = per_epi[epi]
-    # algorithmic bytes: weights once, the bf16 rows, the outputs (fp32; read and written
-    # for a residual; q in fp32 and K, V in bf16 for QKV)
+    # algorithmic bytes: weights once, the bf16 rows, the outputs (fp32, read and written
+    # for a residual; SwiGLU written as the down product's bf16 rows; q in fp32 and K, V in
+    # bf16 for QKV)
     per_epi_bytes = {1: Lr * (2 * d * d + 2 * d * F + r * d * 2 + r * F * 2 + 2 * r * d * 8),
-                     2: Lr * (2 * F * d * 2 + r * d * 2 + r * F * 4),
+                     2: Lr * (2 * F * d * 2 + r * d * 2 + r * F * 2),
                      3: Lr * (3 * d * d * 2 + r * d * 2 + r * d * 4 + r * 2 * d * 2)}
     bytes_per_launch = per_epi_bytes[epi] / nl
     achieved = flops / (ms * 1e-3) / 1e12

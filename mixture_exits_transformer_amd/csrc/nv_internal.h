@@ -36,7 +36,10 @@ struct GemmArgs {
     int head;             // 1: an exit head (separate kernel symbol, so profiles tell them apart)
     float* rms_ws;        // [R] scratch for per-row inverse RMS (matrix-core path with norm_w)
     uint16_t* abf;        // [R][K] bf16 scratch: the rows, normalised and rounded once (long chunks), or null
-    int abf_ready;        // abf already holds this product's rows (launch_rows_bf16 ran)
+    int abf_ready;        // abf already holds this product's rows (launch_rows_bf16 ran, or the
+                          // producing epilogue wrote them)
+    uint16_t* out_bf16;   // EPI_SWIGLU only, or null: silu(g) * u goes here as bf16 [R][ldo],
+                          // rounded as launch_rows_bf16 would round it, instead of to out
     int mfma_min_rows;    // use the matrix-core path when R >= this (0: never)
     // EPI_QKV only.  Weight row 2p + i (i = 0, 1) of the fused QKV matrix is original
     // row part*d + h*hd + j + i*hd/2, where p = part*(d/2) + h*(hd/2) + j, part 0/1/2 = q/k/v.

@@ -101,7 +101,9 @@ template <int EPI>
 __device__ __forceinline__ void epi_pair_t(const GemmArgs& a, int row, int n, float v0, float v1) {
     if constexpr (EPI == EPI_SWIGLU) {
         const int orow = a.o_rows ? a.o_rows[row].hrow : row;
-        a.out[(int64_t)orow * a.ldo + (n >> 1)] = v0 / (1.0f + expf(-v0)) * v1;
+        const float y = v0 / (1.0f + expf(-v0)) * v1;
+        if (a.out_bf16) a.out_bf16[(int64_t)orow * a.ldo + (n >> 1)] = f2bf(y);
+        else a.out[(int64_t)orow * a.ldo + (n >> 1)] = y;
         return;
     }
     if constexpr (EPI == EPI_QKV) {
@@ -651,19 +653,38 @@ constexpr int GB_BM = 128, GB_BK = 64, GB_LDK = GB_BK;
 __device__ __forceinline__ int gb_swz(int r) { return (r >> 1) & 7; }
 constexpr int GB_MIN_ROWS = 33;    // chunks of at least this many rows use k_gemm_bf16
 
-template <int BN, int HEAD, int EPI>
+// Direct global -> LDS loads (global_load_lds_dwordx4): lane l of a wave writes its 16
+// bytes at ldsbase + 16 l, so a tile is laid out by choosing which global chunk each lane
+// fetches.  The loads count on vmcnt; the K loop waits for them with explicit counts and
+// meets at a bare s_barrier, because a fenced barrier would wait for every load in flight.
+#define NV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");      // keeps the compiler from moving LDS accesses across
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BN, int HEAD, int EPI, int ST>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     constexpr int WN = BN / 2;                        // columns per wave
     constexpr int NT = WN / 16;
     constexpr int MT = 4;                             // 64 rows per wave
     constexpr int ACH = GB_BM * GB_BK / 8 / 256;      // 16-byte chunks per thread per tile
     constexpr int WCH = BN * GB_BK / 8 / 256;
+    constexpr int NL = ACH + WCH;                     // loads per thread per tile
     constexpr int A_EL = GB_BM * GB_LDK, W_EL = BN * GB_LDK;
     constexpr int CLD = BN + 4;                       // fp32 output tile row stride
-    constexpr int OPER_B = 2 * (A_EL + W_EL) * 2, OUT_B = GB_BM * CLD * 4;
+    constexpr int OPER_B = ST * (A_EL + W_EL) * 2, OUT_B = GB_BM * CLD * 4;
+    static_assert(ST == 2 || ST == 3, "two or three operand stages");
     __shared__ __align__(16) unsigned char smem[OPER_B > OUT_B ? OPER_B : OUT_B];
-    uint16_t* const As = (uint16_t*)smem;             // [2][GB_BM][GB_LDK]
-    uint16_t* const Ws = As + 2 * A_EL;               // [2][BN][GB_LDK]
+    uint16_t* const As = (uint16_t*)smem;             // [ST][GB_BM][GB_LDK]
+    uint16_t* const Ws = As + ST * A_EL;              // [ST][BN][GB_LDK]
     float* const Cs = (float*)smem;                   // [GB_BM][CLD] after the last product
     const unsigned long long t_begin = stamp_begin(a.stamp);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -672,30 +693,27 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     const int K = a.K;
     const uint16_t* Ab = a.abf;
     const uint16_t* Wb = (const uint16_t*)a.W;
-    u32x4 ar[ACH], wr[WCH];
-    auto gload = [&](int k0) {
+    // tile kt into stage s: load j of a wave fills chunk slots p0 .. p0 + 63 of the stage
+    // (p0 = 256 j + 64 wave); slot p is row p / 8, position p % 8, which holds the row's
+    // k-chunk (p % 8) ^ gb_swz(row)
+    auto issue = [&](int kt, int s) __attribute__((always_inline)) {
+        const int k0 = kt * GB_BK;
+        uint16_t* const Ad = As + s * A_EL;
+        uint16_t* const Wd = Ws + s * W_EL;
 #pragma unroll
         for (int j = 0; j < ACH; ++j) {
-            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
+            const int p0 = 256 * j + 64 * wave, p = p0 + lane, row = p >> 3;
             const int grow = min(m0 + row, a.R - 1);   // rows past R are computed and dropped
-            ar[j] = *(const u32x4*)(Ab + (int64_t)grow * K + k0 + kc);
+            const int g = (p & 7) ^ gb_swz(row);
+            __builtin_amdgcn_global_load_lds((const void*)(Ab + (int64_t)grow * K + k0 + 8 * g), NV_LDS(Ad + 8 * p0),
+                                             16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < WCH; ++j) {
-            const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
-            wr[j] = *(const u32x4*)(Wb + (int64_t)(n0 + row) * K + k0 + kc);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < ACH; ++j) {
-            const int c = tid + 256 * j, row = c >> 3;
-            *(u32x4*)&As[buf * A_EL + row * GB_LDK + (((c & 7) ^ gb_swz(row)) << 3)] = ar[j];
-        }
-#pragma unroll
-        for (int j = 0; j < WCH; ++j) {
-            const int c = tid + 256 * j, row = c >> 3;
-            *(u32x4*)&Ws[buf * W_EL + row * GB_LDK + (((c & 7) ^ gb_swz(row)) << 3)] = wr[j];
+            const int p0 = 256 * j + 64 * wave, p = p0 + lane, row = p >> 3;
+            const int g = (p & 7) ^ gb_swz(row);
+            __builtin_amdgcn_global_load_lds((const void*)(Wb + (int64_t)(n0 + row) * K + k0 + 8 * g),
+                                             NV_LDS(Wd + 8 * p0), 16, 0, 0);
         }
     };
     f32x4_t acc[MT][NT];
@@ -704,14 +722,23 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[i][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     const int nk = K / GB_BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < ST - 1; ++s)
+        if (s < nk) issue(s, s);
+    int cs = 0;                                        // stage holding tile kt
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * GB_BK);
-        const uint16_t* Ab_l = As + buf * A_EL;
-        const uint16_t* Wb_l = Ws + buf * W_EL;
+        // this wave's loads of tile kt are done once at most the later tiles' are in flight
+        if constexpr (ST == 3) {
+            if (kt + 1 < nk) wait_vmcnt<NL>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        wait_lgkmcnt0();                               // and its reads of tile kt - 1 have returned
+        barrier_nofence();                             // every wave's part of tile kt is in LDS
+        if (kt + ST - 1 < nk) issue(kt + ST - 1, cs == 0 ? ST - 1 : cs - 1);   // the stage of tile kt - 1
+        const uint16_t* Ab_l = As + cs * A_EL;
+        const uint16_t* Wb_l = Ws + cs * W_EL;
 #pragma unroll
         for (int ks = 0; ks < GB_BK; ks += 32) {
             bf16x8_t af[MT], bfr[NT];
@@ -734,9 +761,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
                 for (int t = 0; t < NT; ++t)
                     acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
+        cs = cs + 1 == ST ? 0 : cs + 1;
     }
+    __syncthreads();                                   // all reads of the last stage are done
     // the output tile goes through LDS (the operand buffers are free now), so that the
     // epilogue runs as one compact loop with coalesced stores
 #pragma unroll
@@ -756,18 +783,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
 }
 
-template <int BN>
+template <int BN, int ST>
 static void launch_gemm_bf16_bn(const GemmArgs& a, dim3 grid, hipStream_t st) {
     if (a.head) {
-        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE>), grid, dim3(256), 0, st, a);
+        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE, ST>), grid, dim3(256), 0, st, a);
         return;
     }
     switch (a.epi) {
-        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE>), grid, dim3(256), 0, st, a); break;
-        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID>), grid, dim3(256), 0, st, a); break;
-        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU>), grid, dim3(256), 0, st, a); break;
-        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV>), grid, dim3(256), 0, st, a); break;
-        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU>), grid, dim3(256), 0, st, a); break;
+        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE, ST>), grid, dim3(256), 0, st, a); break;
+        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID, ST>), grid, dim3(256), 0, st, a); break;
+        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU, ST>), grid, dim3(256), 0, st, a); break;
+        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV, ST>), grid, dim3(256), 0, st, a); break;
+        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU, ST>), grid, dim3(256), 0, st, a); break;
     }
 }
 
@@ -1176,13 +1203,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
             if (e != hipSuccess) return e;
         }
         const unsigned mt = (unsigned)((a.R + GB_BM - 1) / GB_BM);
-        const bool wide = a.N % 128 == 0 && (a.N / 128) * (long)mt >= 512;
+        // 128-column tiles (two stages, two blocks per CU) when their blocks fill at least 3/4
+        // of the rounds of 512 slots they take; else 64-column tiles, with three stages
+        // while at most one round of 512 is launched (the deeper prefetch pays when few
+        // blocks share a CU) and two stages (three blocks per CU) above that
+        const long b128 = (a.N / 128) * (long)mt, b64 = (a.N / 64) * (long)mt;
+        const bool wide = a.N % 128 == 0 && 4 * b128 >= 3 * 512 * ((b128 + 511) / 512);
+        const int stg = wide ? 2 : b64 <= 512 ? 3 : 2;
         if (t_ev_stop)
-            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d>(nv::GemmArgs)",
+            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d, %d>(nv::GemmArgs)",
                      a.abf_ready ? "" : "nv::k_rows_bf16 + ", wide ? 128 : 64, a.head ? 1 : 0,
-                     a.head ? (int)EPI_STORE : a.epi);
-        if (wide) launch_gemm_bf16_bn<128>(b, dim3(a.N / 128, mt), st);
-        else launch_gemm_bf16_bn<64>(b, dim3(a.N / 64, mt), st);
+                     a.head ? (int)EPI_STORE : a.epi, stg);
+        if (wide) launch_gemm_bf16_bn<128, 2>(b, dim3(a.N / 128, mt), st);
+        else if (stg == 3) launch_gemm_bf16_bn<64, 3>(b, dim3(a.N / 64, mt), st);
+        else launch_gemm_bf16_bn<64, 2>(b, dim3(a.N / 64, mt), st);
         return hipGetLastError();
     }
     if (use_mfma(a)) {

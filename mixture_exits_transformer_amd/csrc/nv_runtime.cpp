@@ -421,7 +421,9 @@ double gemm_bytes(const nv_model* m, const GemmArgs& g) {
     const double es = m->plan.es;
     const double nout = g.epi == EPI_SWIGLU ? g.N / 2 : g.N;
     const double out_rw = g.epi == EPI_RESID ? 2.0 : 1.0;
-    return (double)g.N * g.K * es + (double)g.R * g.K * 4.0 + (double)g.R * nout * 4.0 * out_rw;
+    const double in_es = gemm_uses_bf16_rows(g) ? 2.0 : 4.0;   // the product reads bf16 rows
+    const double out_es = g.out_bf16 ? 2.0 : 4.0;
+    return (double)g.N * g.K * es + (double)g.R * g.K * in_es + (double)g.R * nout * out_es * out_rw;
 }
 
 #define NV_TRY(expr)                      \
@@ -432,7 +434,7 @@ double gemm_bytes(const nv_model* m, const GemmArgs& g) {
 
 // One product, timed; on the long-chunk path the bf16 row pass is timed as its own launch.
 nv_status run_gemm(nv_model* m, int kind, GemmArgs g) {
-    if (gemm_uses_bf16_rows(g)) {
+    if (gemm_uses_bf16_rows(g) && !g.abf_ready) {
         NV_TRY(timed(m, kind, (double)g.R * g.K * 6, [&] { return launch_rows_bf16(g, m->st); }, "nv::k_rows_bf16"));
         g.abf_ready = 1;
     }
@@ -709,20 +711,28 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->mlp;
         g.ldo = m->F;
         g.o_rows = nullptr;
-        NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
         // x += u W_d^T
-        g.A = m->mlp;
-        g.lda = m->F;
-        g.a_rows = nullptr;
-        g.norm_w = nullptr;
-        g.W = W.wd;
-        g.N = d;
-        g.K = m->F;
-        g.epi = EPI_RESID;
-        g.out = m->Hs;
-        g.ldo = d;
-        g.o_rows = t.rows;
+        GemmArgs gd = g;
+        gd.A = m->mlp;
+        gd.lda = m->F;
+        gd.a_rows = nullptr;
+        gd.norm_w = nullptr;
+        gd.W = W.wd;
+        gd.N = d;
+        gd.K = m->F;
+        gd.epi = EPI_RESID;
+        gd.out = m->Hs;
+        gd.ldo = d;
+        gd.o_rows = t.rows;
+        if (gemm_uses_bf16_rows(g) && gemm_uses_bf16_rows(gd)) {
+            // both products on bf16 rows: the SwiGLU epilogue writes u as the down
+            // product's bf16 rows (in the mlp buffer, which holds [R][F] fp32)
+            g.out_bf16 = (uint16_t*)m->mlp;
+            gd.abf = (uint16_t*)m->mlp;
+            gd.abf_ready = 1;
+        }
         NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
+        NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, gd));
     }
     return NV_OK;
 }
