@@ -111,16 +111,20 @@ hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
                                const float* part_ml, const float* part_o, float* out,
                                hipStream_t st);
 // Gates write w_out[seqs[i] * 4 + ucol]; with uniforms null they take no stop decision.
+// With host_flags set (device address of mapped, coherent host memory), each decision is
+// also stored there as host_flags[seq] = tag * 2 + stop, so the host can wait for it
+// without a copy or a stream synchronisation.
 hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d,
                        const float* gw, float bias, const float* uniforms, int ucol,
-                       double* w_out, int* stop_out, hipStream_t st);
+                       double* w_out, int* stop_out, hipStream_t st, int* host_flags = nullptr, int tag = 0);
 hipError_t launch_sample(const float* logits, int64_t ld, const int* seqs, int n, int V,
                          const float* uniforms, int* tok_out, hipStream_t st);
 // Router MLP gate: w = sigmoid(w2 . silu(W1 h + b1) + bias) in float64 (W1 [rr][d]);
 // hid: [n][rr] float64 scratch for the hidden units.
 hipError_t launch_gate_mlp(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d, const float* w1,
                            const float* b1, const float* w2, int rr, float bias, const float* uniforms, int ucol,
-                           double* hid, double* w_out, int* stop_out, hipStream_t st);
+                           double* hid, double* w_out, int* stop_out, hipStream_t st, int* host_flags = nullptr,
+                           int tag = 0);
 // dst row i = Hs row rows[i].hrow (d floats each).
 hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst, hipStream_t st);
 // out[i * ostride + ocol] = log softmax(logits row i)[targets[i]] (float64).

@@ -865,36 +865,44 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
             gv[4 * e] = t.x; gv[4 * e + 1] = t.y; gv[4 * e + 2] = t.z; gv[4 * e + 3] = t.w;
         }
     }
+    // COMB: this lane's 8 dims (e0..e0+7 of head h) of the attention output are the online
+    // merge of the split partials (max m_s, sum l_s, unnormalised output o_s), 8 splits per
+    // batch.  The first batch is loaded before the weights, so that its latency overlaps
+    // theirs (vector loads retire in order: loaded after, it would wait for the weights).
+    const bool merge = COMB && cmb.nsplit > 1;
+    const int c_hd = a.D.hd, c_h = COMB ? k0 / max(c_hd, 1) : 0, c_e0 = k0 - c_h * c_hd;
+    const int64_t c_base = COMB ? cmb.base + (int64_t)c_h * cmb.nsplit * cmb.nrows + cmb.off : 0;
+    auto load_parts = [&](int s0, float2 (&ml)[8], float (&ob)[8][EPC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int sp = s0 + j < cmb.nsplit ? s0 + j : cmb.nsplit - 1;
+            const int64_t slot = c_base + (int64_t)sp * cmb.nrows;
+            ml[j] = *(const float2*)(a.part_ml + 2 * slot);
+            const float4* op = (const float4*)(a.part_o + slot * c_hd + c_e0);
+#pragma unroll
+            for (int q4 = 0; q4 < EPC / 4; ++q4) {
+                const float4 t = op[q4];
+                ob[j][4 * q4] = t.x; ob[j][4 * q4 + 1] = t.y; ob[j][4 * q4 + 2] = t.z; ob[j][4 * q4 + 3] = t.w;
+            }
+        }
+    };
+    float2 ml0[8];
+    float ob0[8][EPC];
+    if constexpr (COMB) {
+        if (merge) load_parts(0, ml0, ob0);
+    }
+
     uint4 w[KS_CPB];
 #pragma unroll
     for (int c = 0; c < KS_CPB; ++c) w[c] = *(const uint4*)((const char*)a.W + ((size_t)(n0 + c) * K + k0) * ESZ);
 
     if constexpr (COMB) {
-        if (cmb.nsplit > 1) {
-            // this lane's 8 dims (e0..e0+7 of head h) of the attention output: online merge of
-            // the split partials (max m_s, sum l_s, unnormalised output o_s), 8 splits per batch
-            const int hd = a.D.hd;
-            const int h = k0 / hd, e0 = k0 - h * hd;
+        if (merge) {
             const int ns = cmb.nsplit;
-            const int64_t base = cmb.base + (int64_t)h * ns * cmb.nrows + cmb.off;
             float M = -INFINITY, L = 0.f, O[EPC];
 #pragma unroll
             for (int e = 0; e < EPC; ++e) O[e] = 0.f;
-            for (int s0 = 0; s0 < ns; s0 += 8) {
-                float2 ml[8];
-                float ob[8][EPC];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int sp = s0 + j < ns ? s0 + j : ns - 1;
-                    const int64_t slot = base + (int64_t)sp * cmb.nrows;
-                    ml[j] = *(const float2*)(a.part_ml + 2 * slot);
-                    const float4* op = (const float4*)(a.part_o + slot * hd + e0);
-#pragma unroll
-                    for (int q4 = 0; q4 < EPC / 4; ++q4) {
-                        const float4 t = op[q4];
-                        ob[j][4 * q4] = t.x; ob[j][4 * q4 + 1] = t.y; ob[j][4 * q4 + 2] = t.z; ob[j][4 * q4 + 3] = t.w;
-                    }
-                }
+            auto merge_parts = [&](int s0, const float2 (&ml)[8], const float (&ob)[8][EPC]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if (s0 + j < ns && ml[j].x != -INFINITY) {
@@ -906,6 +914,13 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
                         M = Mn;
                     }
                 }
+            };
+            merge_parts(0, ml0, ob0);
+            for (int s0 = 8; s0 < ns; s0 += 8) {
+                float2 ml[8];
+                float ob[8][EPC];
+                load_parts(s0, ml, ob);
+                merge_parts(s0, ml, ob);
             }
 #pragma unroll
             for (int e = 0; e < EPC; ++e) av[0][e] = O[e] / L;
@@ -1928,9 +1943,15 @@ hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, con
 // Router gate at the end of a segment: w = sigmoid(g . h + b) in float64, stop iff u < w.
 // ------------------------------------------------------------------------------------------
 
+// The stop decision also goes to mapped host memory when host_flags is set: a plain
+// vector store at system scope (fine-grained memory; nothing else needs ordering with it).
+__device__ __forceinline__ void publish_stop(int* host_flags, int seq, int tag, int stop) {
+    if (host_flags) __hip_atomic_store(host_flags + seq, tag * 2 + stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __global__ __launch_bounds__(256) void k_gate(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d,
                                               const float* gw, float bias, const float* uniforms, int ucol,
-                                              double* w_out, int* stop_out) {
+                                              double* w_out, int* stop_out, int* host_flags, int tag) {
     __shared__ double red[256];
     const int i = blockIdx.x;
     if (i >= n) return;
@@ -1954,15 +1975,20 @@ __global__ __launch_bounds__(256) void k_gate(const RowInfo* rows, const int* se
         }
         const int seq = seqs[i];
         w_out[seq * 4 + ucol] = w;
-        if (uniforms) stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+        if (uniforms) {
+            const int stop = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+            stop_out[seq] = stop;
+            publish_stop(host_flags, seq, tag, stop);
+        }
     }
 }
 
 hipError_t launch_gate(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d, const float* gw, float bias,
-                       const float* uniforms, int ucol, double* w_out, int* stop_out, hipStream_t st) {
+                       const float* uniforms, int ucol, double* w_out, int* stop_out, hipStream_t st, int* host_flags,
+                       int tag) {
     if (n <= 0) return hipSuccess;
     NV_LAUNCH(k_gate, dim3(n), dim3(256), 0, st, rows, seqs, n, Hs, d, gw, bias, uniforms, ucol, w_out,
-                       stop_out);
+                       stop_out, host_flags, tag);
     return hipGetLastError();
 }
 
@@ -2004,7 +2030,7 @@ __global__ __launch_bounds__(256) void k_router_hidden(const RowInfo* rows, int 
 
 __global__ __launch_bounds__(64) void k_router_out(const int* seqs, int n, const double* hid, const float* w2, int rr,
                                                    float bias, const float* uniforms, int ucol, double* w_out,
-                                                   int* stop_out) {
+                                                   int* stop_out, int* host_flags, int tag) {
     const int i = blockIdx.x;
     if (i >= n) return;
     const int lane = threadIdx.x;
@@ -2023,19 +2049,24 @@ __global__ __launch_bounds__(64) void k_router_out(const int* seqs, int n, const
         }
         const int seq = seqs[i];
         w_out[seq * 4 + ucol] = w;
-        if (uniforms) stop_out[seq] = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+        if (uniforms) {
+            const int stop = ((double)uniforms[seq * 4 + ucol] < w) ? 1 : 0;
+            stop_out[seq] = stop;
+            publish_stop(host_flags, seq, tag, stop);
+        }
     }
 }
 
 hipError_t launch_gate_mlp(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d, const float* w1,
                            const float* b1, const float* w2, int rr, float bias, const float* uniforms, int ucol,
-                           double* hid, double* w_out, int* stop_out, hipStream_t st) {
+                           double* hid, double* w_out, int* stop_out, hipStream_t st, int* host_flags, int tag) {
     if (n <= 0) return hipSuccess;
     if (rr < 1 || rr > GATE_MLP_MAX || d % 4 != 0 || d > 256 * GATE_MLP_KD) return hipErrorInvalidValue;
     NV_LAUNCH(k_router_hidden, dim3(n, (rr + 3) / 4), dim3(256), 0, st, rows, n, Hs, d, w1, b1, rr, hid);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    NV_LAUNCH(k_router_out, dim3(n), dim3(64), 0, st, seqs, n, hid, w2, rr, bias, uniforms, ucol, w_out, stop_out);
+    NV_LAUNCH(k_router_out, dim3(n), dim3(64), 0, st, seqs, n, hid, w2, rr, bias, uniforms, ucol, w_out, stop_out,
+              host_flags, tag);
     return hipGetLastError();
 }
 

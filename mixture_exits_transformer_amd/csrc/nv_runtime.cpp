@@ -266,6 +266,10 @@ struct nv_model {
     char* h_headlist = nullptr;
     char* h_out = nullptr;     // pinned: stop flags, tokens, router outputs coming back
     int* h_ring = nullptr;     // pinned [kRing][max_batch]: sampled tokens coming back (nv_generate)
+    // mapped, coherent [max_batch]: gate decisions stored by the gate kernels as tag * 2 + stop
+    int* h_flags = nullptr;
+    int* d_flags = nullptr;    // device address of h_flags
+    int gate_tag = 0;          // tag of the last gate launch
     bool sb_busy = false;      // an async copy from h_stepblk may still be pending
 
     size_t stepblk_bytes() const { return (size_t)max_batch * (16 + 4 + sizeof(RowInfo)); }
@@ -458,7 +462,7 @@ nv_status stage_sync(nv_model* m) {
 
 // Build and upload the tables for one launch group of causal chunks at one segment:
 // compact rows, attention items and combine info.  Layout in the device table region:
-// [rows R][headless: reserved R][comb R][items n_items].
+// [rows R][comb R][items n_items], R being this group's rows.
 struct Tables {
     RowInfo* rows;
     CombineInfo* comb;
@@ -484,9 +488,12 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
     int R = 0;
     for (const Chunk& c : chunks) R += c.nrows;
     if (R > P.R_max) return fail(m, NV_ECAPACITY, "internal: launch group exceeds workspace rows");
+    // compact layout for this group: [rows R][comb R][items], so a decode step copies a
+    // few KB rather than the worst case
+    const size_t comb_off = sizeof(RowInfo) * (size_t)R, items_off = comb_off + sizeof(CombineInfo) * (size_t)R;
     RowInfo* hrows = (RowInfo*)m->h_stage;
-    CombineInfo* hcomb = (CombineInfo*)(m->h_stage + sizeof(RowInfo) * P.R_max);
-    AttnItem* hitems = (AttnItem*)(m->h_stage + (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max);
+    CombineInfo* hcomb = (CombineInfo*)(m->h_stage + comb_off);
+    AttnItem* hitems = (AttnItem*)(m->h_stage + items_off);
     // rows
     int r = 0;
     for (const Chunk& c : chunks)
@@ -602,12 +609,12 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         t->any_split |= hitems[i].nsplit > 1;
         t->max_split = std::max(t->max_split, hitems[i].nsplit);
     }
-    size_t bytes = (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max + sizeof(AttnItem) * (size_t)n_items;
+    const size_t bytes = items_off + sizeof(AttnItem) * (size_t)n_items;
     NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, bytes, hipMemcpyHostToDevice, m->st));
     m->stage_busy = true;
     t->rows = (RowInfo*)m->d_tables;
-    t->comb = (CombineInfo*)(m->d_tables + sizeof(RowInfo) * P.R_max);
-    t->items = (AttnItem*)(m->d_tables + (sizeof(RowInfo) + sizeof(CombineInfo)) * P.R_max);
+    t->comb = (CombineInfo*)(m->d_tables + comb_off);
+    t->items = (AttnItem*)(m->d_tables + items_off);
     t->R = R;
     t->n_items = n_items;
     double kvb = 0;
@@ -940,6 +947,7 @@ void nv_free(nv_model* m) {
     if (m->h_headlist) (void)hipHostFree(m->h_headlist);
     if (m->h_out) (void)hipHostFree(m->h_out);
     if (m->h_ring) (void)hipHostFree(m->h_ring);
+    if (m->h_flags) (void)hipHostFree(m->h_flags);
     delete m;
 }
 
@@ -1109,6 +1117,9 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     NV_HIP(m, hipHostMalloc((void**)&m->h_headlist, 2 * m->list_bytes(), hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_out, (size_t)max_batch * 48 + 16, hipHostMallocDefault));
     NV_HIP(m, hipHostMalloc((void**)&m->h_ring, (size_t)kRing * max_batch * 4, hipHostMallocDefault));
+    NV_HIP(m, hipHostMalloc((void**)&m->h_flags, (size_t)max_batch * 4, hipHostMallocMapped | hipHostMallocCoherent));
+    for (int i = 0; i < max_batch; ++i) m->h_flags[i] = -1;
+    NV_HIP(m, hipHostGetDevicePointer((void**)&m->d_flags, m->h_flags, 0));
 
     // weights: file tensors -> pinned bounce buffer -> device (repacking W_gate/W_up rows)
     int fd = ::open(path, O_RDONLY);
@@ -1355,39 +1366,64 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
     return NV_OK;
 }
 
+// Wait until the gate kernels have published the decisions of `run` with this tag in
+// mapped host memory.  The stream is polled now and then, so that a failed launch or a
+// device fault is reported instead of waited on.
+static nv_status wait_gate_flags(nv_model* m, const std::vector<int>& run, int tag) {
+    const volatile int* f = m->h_flags;
+    auto all_in = [&] {
+        for (int i : run)
+            if ((f[i] >> 1) != tag) return false;
+        return true;
+    };
+    for (unsigned it = 1;; ++it) {
+        if (all_in()) return NV_OK;
+        if ((it & 255) == 0) {
+            const hipError_t e = hipStreamQuery(m->st);
+            if (e == hipSuccess) {
+                if (all_in()) return NV_OK;
+                m->dead = true;
+                return fail(m, NV_EDEVICE, "gate decision missing after the stream drained");
+            }
+            if (e != hipErrorNotReady) NV_HIP(m, e);
+        }
+    }
+}
+
 // Router gate sg on the current rows of sequences `run`: the walk's decision (u_sg < w_sg)
-// comes back to the host, which then launches the next segment or the head.  The stream
-// is synchronised.  `run` splits into the sequences that stop here and the rest.
+// comes back to the host, which then launches the next segment or the head.  Every
+// launch before the gate has completed when the decisions arrive (stream order), so the
+// pinned staging buffers are free again.  `run` splits into the sequences that stop here
+// and the rest.
 static nv_status run_gates(nv_model* m, int sg, const std::vector<int>& run, const float* d_unif,
                            std::vector<int>* stopping, std::vector<int>* rest) {
     char* gl = m->h_gatelist;
     const int na = (int)run.size();
-    int top = 0;
     for (int j = 0; j < na; ++j) {
         const int i = run[j];
         nv_model::lseqs(gl)[j] = i;
         m->lrows(gl)[j] = RowInfo{i * m->max_ctx + m->seqs[i].n, i, m->seqs[i].n, 0};
-        top = std::max(top, i + 1);
     }
     NV_HIP(m, hipMemcpyAsync(m->d_gatelist, gl, m->list_bytes(), hipMemcpyHostToDevice, m->st));
+    m->gate_tag = m->gate_tag >= (1 << 29) ? 1 : m->gate_tag + 1;
+    const int tag = m->gate_tag;
     if (m->cfg.router_form == 1) {
         const ExitPtrs& X = m->exits[sg];
         NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8 + (double)m->cfg.router_dim * m->d * 4, [&] {
             return launch_gate_mlp(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
                                    X.router_w1, X.router_b1, X.router_w2, m->cfg.router_dim, X.bias, d_unif, sg,
-                                   m->router_hid, m->d_w, m->d_stop, m->st);
+                                   m->router_hid, m->d_w, m->d_stop, m->st, m->d_flags, tag);
         }, "nv::k_router_hidden + nv::k_router_out"));
     } else {
         NV_TRY(timed(m, NV_TIME_OTHER, (double)na * m->d * 8, [&] {
             return launch_gate(m->lrows(m->d_gatelist), nv_model::lseqs(m->d_gatelist), na, m->Hs, m->d,
-                               m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st);
+                               m->exits[sg].gate_w, m->exits[sg].bias, d_unif, sg, m->d_w, m->d_stop, m->st,
+                               m->d_flags, tag);
         }, "nv::k_gate"));
     }
-    int* hstop = (int*)m->h_out;
-    NV_HIP(m, hipMemcpyAsync(hstop, m->d_stop, (size_t)top * 4, hipMemcpyDeviceToHost, m->st));
-    NV_HIP(m, hipStreamSynchronize(m->st));
+    NV_TRY(wait_gate_flags(m, run, tag));
     stream_synced(m);
-    for (int i : run) (hstop[i] ? *stopping : *rest).push_back(i);
+    for (int i : run) ((m->h_flags[i] & 1) ? *stopping : *rest).push_back(i);
     return NV_OK;
 }
 
