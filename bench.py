@@ -444,6 +444,10 @@ def main():
         "speedup_vs_exit4": round(tok_s / base - 1.0, 4) if base else None,
         "exit_histogram": [int(x) for x in hist],
         "mean_segments_per_token": round(float(np.mean(exits)), 4),
+        # the step's cost per segment a token runs: tokens/s moves with the realised exit mix
+        # (which last-bit rounding changes on random-init weights), this figure does not
+        "ms_per_segment_token": round(1e3 / tok_s / float(np.mean(exits)), 4),
+        "exit4_ms_per_segment_token": round(1e3 / base / 4.0, 4) if base else None,
         "pages_reference": "57.9% wall-clock speedup at 1.5B on unspecified hardware (context only)",
     }
     if not args.no_cpu:

@@ -110,6 +110,10 @@ hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, 
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
                                const float* part_ml, const float* part_o, float* out,
                                hipStream_t st);
+// The combine for a product on bf16 rows: every (row, head) of the attention output goes
+// to out_bf16 [R][d] as bf16 (split rows merged, the others converted from out).
+hipError_t launch_attn_combine_bf16(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,
+                                    const float* part_o, const float* attn_o, uint16_t* out_bf16, hipStream_t st);
 // Gates write w_out[seqs[i] * 4 + ucol]; with uniforms null they take no stop decision.
 // With host_flags set (device address of mapped, coherent host memory), each decision is
 // also stored there as host_flags[seq] = tag * 2 + stop, so the host can wait for it

@@ -647,6 +647,73 @@ __global__ __launch_bounds__(256) void k_rows_bf16(const float* A, int64_t lda, 
     }
 }
 
+// The same pass with one wave per row and the whole row in registers (K = 256 NPL): one
+// load per element, the sum of squares reduced inside the wave, no block barrier.
+template <int NPL>
+__global__ __launch_bounds__(256) void k_rows_bf16_w(const float* A, int64_t lda, const RowInfo* rows, int R, int K,
+                                                     const float* norm_w, float eps, uint16_t* out) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R) return;
+    // the norm weights do not depend on the row: they are loaded first, beside the row
+    // table lookup, so that only the row's own load follows it
+    float4 g[NPL];
+    if (norm_w) {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) g[j] = *(const float4*)(norm_w + 4 * (lane + 64 * j));
+    }
+    const float* src = A + (int64_t)(rows ? rows[r].hrow : r) * lda;
+    float4 v[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) v[j] = *(const float4*)(src + 4 * (lane + 64 * j));
+    float inv = 1.0f;
+    if (norm_w) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+        ss = wave_sum(ss);
+        inv = 1.0f / sqrtf(ss / (float)K + eps);
+    }
+    uint16_t* dst = out + (int64_t)r * K;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int k = 4 * (lane + 64 * j);
+        float4 x = v[j];
+        if (norm_w) x = make_float4(x.x * inv * g[j].x, x.y * inv * g[j].y, x.z * inv * g[j].z, x.w * inv * g[j].w);
+        *(uint2*)(dst + k) = make_uint2(pack_bf2(x.x, x.y), pack_bf2(x.z, x.w));
+    }
+}
+
+static void launch_rows_bf16_any(const GemmArgs& a, hipStream_t st) {
+    const int npl = a.K / 256;
+    if (a.K % 256 != 0 || npl < 1 || npl > 16) {
+        NV_LAUNCH(k_rows_bf16, dim3(a.R), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.norm_w, a.eps, a.abf);
+        return;
+    }
+    const dim3 grid((a.R + 3) / 4), block(256);
+#define NV_RW(NPLV) NV_LAUNCH(HIP_KERNEL_NAME(k_rows_bf16_w<NPLV>), grid, block, 0, st, a.A, a.lda, a.a_rows, a.R, \
+                              a.K, a.norm_w, a.eps, a.abf)
+    switch (npl) {
+        case 1: NV_RW(1); break;
+        case 2: NV_RW(2); break;
+        case 3: NV_RW(3); break;
+        case 4: NV_RW(4); break;
+        case 5: NV_RW(5); break;
+        case 6: NV_RW(6); break;
+        case 7: NV_RW(7); break;
+        case 8: NV_RW(8); break;
+        case 9: NV_RW(9); break;
+        case 10: NV_RW(10); break;
+        case 11: NV_RW(11); break;
+        case 12: NV_RW(12); break;
+        case 13: NV_RW(13); break;
+        case 14: NV_RW(14); break;
+        case 15: NV_RW(15); break;
+        default: NV_RW(16); break;
+    }
+#undef NV_RW
+}
+
 constexpr int GB_BM = 128, GB_BK = 64, GB_LDK = GB_BK;
 // 16-byte chunk j of tile row r is stored at chunk j ^ gb_swz(r): the 8 lanes storing one
 // row and the 16 lanes reading one k-chunk of 16 rows then cover every LDS bank once.
@@ -739,28 +806,40 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         if (kt + ST - 1 < nk) issue(kt + ST - 1, cs == 0 ? ST - 1 : cs - 1);   // the stage of tile kt - 1
         const uint16_t* Ab_l = As + cs * A_EL;
         const uint16_t* Wb_l = Ws + cs * W_EL;
+        // every operand fragment of the 64-wide step is read in one burst (one LDS latency
+        // per step instead of one per 32-wide half and per re-read), then the products
+        bf16x8_t af[2][MT], bfr[2][NT];
 #pragma unroll
-        for (int ks = 0; ks < GB_BK; ks += 32) {
-            bf16x8_t af[MT], bfr[NT];
-            const int kch = (ks >> 3) + (lane >> 4);     // 16-byte k-chunk of this lane
+        for (int h = 0; h < 2; ++h) {
+            const int kch = 4 * h + (lane >> 4);          // 16-byte k-chunk of this lane
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const int row = wm * 64 + i * 16 + (lane & 15);
-                af[i] = __builtin_bit_cast(bf16x8_t,
-                                           *(const u32x4*)&Ab_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
+                af[h][i] = __builtin_bit_cast(bf16x8_t,
+                                              *(const u32x4*)&Ab_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int row = wn * WN + t * 16 + (lane & 15);
-                bfr[t] = __builtin_bit_cast(bf16x8_t,
-                                            *(const u32x4*)&Wb_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
+                bfr[h][t] = __builtin_bit_cast(bf16x8_t,
+                                               *(const u32x4*)&Wb_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
             }
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);             // keep the scheduler from sinking the reads
+        // the first half's products need only its own reads (the compiler may still wait
+        // for all of them while direct-to-LDS loads are in flight)
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | ((MT + NT) << 8));
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][i], bfr[0][t], acc[i][t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][i], bfr[1][t], acc[i][t], 0, 0, 0);
         cs = cs + 1 == ST ? 0 : cs + 1;
     }
     __syncthreads();                                   // all reads of the last stage are done
@@ -1130,7 +1209,7 @@ static bool use_mfma(const GemmArgs& a) {
 
 hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st) {
     if (!gemm_uses_bf16_rows(a)) return hipErrorInvalidValue;
-    NV_LAUNCH(k_rows_bf16, dim3(a.R), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.norm_w, a.eps, a.abf);
+    launch_rows_bf16_any(a, st);
     return hipGetLastError();
 }
 
@@ -1212,8 +1291,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
     if (gemm_uses_bf16_rows(a)) {
         if (!a.abf_ready) {
-            NV_LAUNCH(k_rows_bf16, dim3(a.R), dim3(256), 0, st, a.A, a.lda, a.a_rows, a.R, a.K, a.norm_w, a.eps,
-                      a.abf);
+            launch_rows_bf16_any(a, st);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1707,6 +1785,56 @@ __global__ __launch_bounds__(256) void k_attn_combine(const CombineInfo* ci, int
     stamp_end(stamp, t_begin);
 }
 
+// As k_attn_combine, but every (row, head) is written as bf16 into the O product's rows
+// (out_bf16 [R][d], rounded as k_rows_bf16 rounds): merged partials for split rows, the
+// attention kernel's normalised fp32 output for the others.  The O product then needs no
+// row pass of its own.
+__global__ __launch_bounds__(256) void k_attn_combine_bf16(const CombineInfo* ci, int R, LayerDims D,
+                                                           const float* part_ml, const float* part_o,
+                                                           const float* attn_o, uint16_t* out_bf16) {
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= R * D.H) return;
+    const int i = p / D.H, h = p - i * D.H;
+    const CombineInfo c = ci[i];
+    const int hd = D.hd, e = 2 * lane;
+    if (e >= hd) return;
+    const int64_t o = (int64_t)i * D.d + h * hd + e;
+    float o0, o1;
+    if (c.nsplit > 1) {
+        const int ns = c.nsplit;
+        const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
+        float M = -INFINITY;
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
+        float L = 0.f, a0 = 0.f, a1 = 0.f;
+        for (int sp = 0; sp < ns; ++sp) {
+            const int64_t slot = base + (int64_t)sp * c.nrows;
+            const float2 ml = *(const float2*)(part_ml + 2 * slot);
+            const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
+            L += w * ml.y;
+            const float2 v = *(const float2*)(part_o + slot * hd + e);
+            a0 += w * v.x;
+            a1 += w * v.y;
+        }
+        o0 = a0 / L;
+        o1 = a1 / L;
+    } else {
+        const float2 v = *(const float2*)(attn_o + o);
+        o0 = v.x;
+        o1 = v.y;
+    }
+    *(uint32_t*)(out_bf16 + o) = pack_bf2(o0, o1);
+}
+
+hipError_t launch_attn_combine_bf16(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,
+                                    const float* part_o, const float* attn_o, uint16_t* out_bf16, hipStream_t st) {
+    if (R <= 0) return hipSuccess;
+    if (D.hd % 2 || D.hd > 128) return hipErrorInvalidValue;
+    NV_LAUNCH(k_attn_combine_bf16, dim3((R * D.H + 3) / 4), dim3(256), 0, st, ci, R, D, part_ml, part_o, attn_o,
+              out_bf16);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
                        int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st) {
     if (n_items <= 0) return hipSuccess;
@@ -2085,6 +2213,10 @@ hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, 
 
 // Log-probability of the target token under softmax(z) for each row: z[y] - max z -
 // log sum exp(z - max z), exponentials in float32 summed in float64 (as the sampler).
+// One row per block.  Each thread keeps its logits (k = t, t + 1024, ...) in registers
+// when V <= 32768, so the row is read from memory once; the exponentials are summed in
+// float64 in that fixed order either way.
+constexpr int XE_PER = 32;
 __global__ __launch_bounds__(1024) void k_xent(const float* logits, int64_t ld, int n, int V, const int* targets,
                                                double* out, int ostride, int ocol) {
     __shared__ float smax[16];
@@ -2093,15 +2225,34 @@ __global__ __launch_bounds__(1024) void k_xent(const float* logits, int64_t ld, 
     if (i >= n) return;
     const float* z = logits + (int64_t)i * ld;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+    const bool regs = V <= XE_PER * (int)blockDim.x;
+    const float zt = z[targets[i]];
+    float zv[XE_PER];
     float mx = -INFINITY;
-    for (int k = t; k < V; k += blockDim.x) mx = fmaxf(mx, z[k]);
+    if (regs) {
+#pragma unroll
+        for (int j = 0; j < XE_PER; ++j) {
+            const int k = t + j * (int)blockDim.x;
+            zv[j] = k < V ? z[k] : -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < XE_PER; ++j) mx = fmaxf(mx, zv[j]);
+    } else {
+        for (int k = t; k < V; k += blockDim.x) mx = fmaxf(mx, z[k]);
+    }
     mx = wave_max(mx);
     if (lane == 0) smax[wave] = mx;
     __syncthreads();
     mx = smax[0];
     for (int w = 1; w < nw; ++w) mx = fmaxf(mx, smax[w]);
     double acc = 0.0;
-    for (int k = t; k < V; k += blockDim.x) acc += (double)expf(z[k] - mx);
+    if (regs) {
+#pragma unroll
+        for (int j = 0; j < XE_PER; ++j)
+            if (t + j * (int)blockDim.x < V) acc += (double)expf(zv[j] - mx);
+    } else {
+        for (int k = t; k < V; k += blockDim.x) acc += (double)expf(z[k] - mx);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) ssum[wave] = acc;
@@ -2109,7 +2260,7 @@ __global__ __launch_bounds__(1024) void k_xent(const float* logits, int64_t ld, 
     if (t == 0) {
         double tot = 0.0;
         for (int w = 0; w < nw; ++w) tot += ssum[w];
-        out[(int64_t)i * ostride + ocol] = (double)z[targets[i]] - (double)mx - log(tot);
+        out[(int64_t)i * ostride + ocol] = (double)zt - (double)mx - log(tot);
     }
 }
 

@@ -658,6 +658,26 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.layer = l;
         g.D = D;
         NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
+        // long chunks whose O product runs on bf16 rows: the combine pass writes those rows
+        GemmArgs go = g;
+        go.A = m->attn_o;
+        go.lda = d;
+        go.a_rows = nullptr;
+        go.norm_w = nullptr;
+        go.W = W.wo;
+        go.N = d;
+        go.K = d;
+        go.epi = EPI_RESID;
+        const bool o_bf16 = !t.dec && gemm_uses_bf16_rows(go);
+        auto combine = [&] {
+            if (o_bf16)
+                return timed(m, NV_TIME_ATTENTION, (double)t.R * d * 6, [&] {
+                    return launch_attn_combine_bf16(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->abf, m->st);
+                }, "nv::k_attn_combine_bf16");
+            return timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
+                return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
+            });
+        };
         if (t.dec) {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                 return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
@@ -673,17 +693,13 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
                 return launch_attn_mfma(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o,
                                         m->attn_o, m->st);
             }, "nv::k_attn_mfma"));
-            NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
-                return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-            }));
+            NV_TRY(combine());
         } else {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
                 return launch_attn(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml, m->part_o, m->attn_o,
                                    m->st);
             }, "nv::k_attn"));
-            NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
-                return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
-            }));
+            NV_TRY(combine());
         }
         // x += o W_o^T
         g.epi = EPI_RESID;
@@ -704,7 +720,9 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.out = m->Hs;
         g.ldo = d;
         g.o_rows = t.rows;
+        g.abf_ready = o_bf16 ? 1 : 0;
         NV_TRY(run_gemm(m, NV_TIME_BLOCK_GEMM, g));
+        g.abf_ready = 0;
         g.comb = nullptr;
         // u = silu(RMSNorm(x) W_g^T) * (RMSNorm(x) W_u^T)
         g.A = m->Hs;
