@@ -231,7 +231,10 @@ struct nv_model {
     int *loss_tgt = nullptr, *loss_ids = nullptr;       // [max_ctx] target tokens, row ids 0..n-1
     RowInfo* loss_rows = nullptr;   // [max_ctx]
     double* loss_hid = nullptr;     // [loss_ch][router_dim]
-    int mfma_min_rows = 9;     // chunks of at least this many rows use the matrix cores
+    // chunks of at least this many rows use the matrix cores: at 5-8 rows the vector-ALU
+    // GEMV holds 5-8 rows of activations per lane and moves about 1 TB/s, the matrix-core
+    // path 1.5-1.7 TB/s (batch-16 decode +7 %)
+    int mfma_min_rows = 5;
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
     // goes up in one copy.  step: [uniforms MB*4 f32][pending tokens MB i32][current rows MB]
