@@ -6,7 +6,12 @@
 namespace nv {
 
 struct RowInfo;
-struct CombineInfo;
+
+// Where the split partials of compact row i live: slot(h, s) =
+// base + (h * nsplit + s) * nrows + off.
+struct CombineInfo {
+    int base, off, nsplit, nrows;
+};
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SILU = 4 };
 
@@ -41,6 +46,9 @@ struct GemmArgs {
     uint16_t* out_bf16;   // EPI_SWIGLU only, or null: silu(g) * u goes here as bf16 [R][ldo],
                           // rounded as launch_rows_bf16 would round it, instead of to out
     int mfma_min_rows;    // use the matrix-core path when R >= this (0: never)
+    // R == 1 only: when set, the one row of A is A + a_row0 * lda (the vector-ALU kernel
+    // then issues its loads without waiting for a_rows[0])
+    int a_row0_set, a_row0;
     // EPI_QKV only.  Weight row 2p + i (i = 0, 1) of the fused QKV matrix is original
     // row part*d + h*hd + j + i*hd/2, where p = part*(d/2) + h*(hd/2) + j, part 0/1/2 = q/k/v.
     float* q_out;         // [R][d]
@@ -71,14 +79,10 @@ struct RowInfo {
 struct AttnItem {
     int row0, nrows, head, lo, hi, part;
     int split, nsplit;    // split index and count over the key range of (row block, head)
-    int pad[4];
+    int seq;              // the rows' sequence (spares the kernels a dependent row-table load)
+    int pad[3];
 };
 
-// Where the split partials of compact row i live: slot(h, s) =
-// base + (h * nsplit + s) * nrows + off.
-struct CombineInfo {
-    int base, off, nsplit, nrows;
-};
 
 // Launch wrappers (nv_kernels.hip).
 hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStream_t st);

@@ -926,7 +926,7 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
             const int rr = r < R ? r : R - 1;
-            const int ar = a.a_rows ? a.a_rows[rr].hrow : rr;
+            const int ar = a.a_row0_set ? a.a_row0 : a.a_rows ? a.a_rows[rr].hrow : rr;
             const float4* ap = (const float4*)(a.A + (int64_t)ar * a.lda + k0);
 #pragma unroll
             for (int e = 0; e < EPC / 4; ++e) {
@@ -1413,7 +1413,7 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
         const int r = idx / hd, e = idx - r * hd;
         Qs[idx] = q[(int64_t)(it.row0 + r) * D.d + it.head * hd + e] * scale;
     }
-    const int seq = rows[it.row0].seq;
+    const int seq = it.seq;
     const int64_t kb = kv_base(D, seq, layer, 0, it.head);
     const int64_t vb = kv_base(D, seq, layer, 1, it.head);
 
@@ -1530,7 +1530,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int r = wave * 16 + qn;                  // this lane's query row within the item
     const bool rv = r < it.nrows;
     const int qpos = rv ? rows[it.row0 + r].pos : -1;
-    const int seq = rows[it.row0].seq;
+    const int seq = it.seq;
     const uint16_t* Kg = kv + kv_base(D, seq, layer, 0, it.head);
     const uint16_t* Vg = kv + kv_base(D, seq, layer, 1, it.head);
 
@@ -1893,7 +1893,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / LPK, dl = lane - g * LPK;
     const int nr = it.nrows;
-    const int seq = rows[it.row0].seq;
+    const int seq = it.seq;
     const int64_t kb = kv_base(D, seq, layer, 0, it.head) + dl * DPL;
     const int64_t vb = kv_base(D, seq, layer, 1, it.head) + dl * DPL;
 

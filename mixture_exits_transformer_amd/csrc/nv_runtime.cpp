@@ -471,6 +471,7 @@ struct Tables {
     CombineInfo* comb;
     AttnItem* items;
     int R, n_items;
+    int hrow0;         // hidden-state row of the first row (passed by value for one-row groups)
     bool dec;          // decode-sized group: attention combines its splits in-kernel
     int max_rows;      // most rows in one decode-attention row block
     bool any_split;    // some row's key range was split (the combine pass is needed)
@@ -538,7 +539,8 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
                         it.part = slot + (h * ns + s2) * nr;
                         it.split = s2;
                         it.nsplit = ns;
-                        it.pad[0] = it.pad[1] = it.pad[2] = it.pad[3] = 0;
+                        it.seq = c.seq;
+                        it.pad[0] = it.pad[1] = it.pad[2] = 0;
                     }
                 for (int i = 0; i < nr; ++i) {
                     CombineInfo& ci = hcomb[row0 + rb + i];
@@ -591,7 +593,8 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
                         it.part = slot + (h * ns + s2) * nr;
                         it.split = s2;
                         it.nsplit = ns;
-                        it.pad[0] = it.pad[1] = it.pad[2] = it.pad[3] = 0;
+                        it.seq = c.seq;
+                        it.pad[0] = it.pad[1] = it.pad[2] = 0;
                     }
                 for (int i = 0; i < nr; ++i) {
                     CombineInfo& ci = hcomb[row0 + rb + i];
@@ -606,6 +609,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         }
     }
     t->dec = dec;
+    t->hrow0 = R > 0 ? hrows[0].hrow : 0;
     t->any_split = false;
     t->max_split = 1;
     for (int i = 0; i < n_items; ++i) {
@@ -647,6 +651,8 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.A = m->Hs;
         g.lda = d;
         g.a_rows = t.rows;
+        g.a_row0_set = t.R == 1 ? 1 : 0;
+        g.a_row0 = t.hrow0;
         g.norm_w = W.attn_norm;
         g.W = W.wqkv;
         g.N = 3 * d;
@@ -666,6 +672,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         go.A = m->attn_o;
         go.lda = d;
         go.a_rows = nullptr;
+        go.a_row0_set = 0;
         go.norm_w = nullptr;
         go.W = W.wo;
         go.N = d;
@@ -709,6 +716,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.A = m->attn_o;
         g.lda = d;
         g.a_rows = nullptr;
+        g.a_row0_set = 0;
         g.norm_w = nullptr;
         g.W = W.wo;
         if (fuse_merge(m, t)) {
@@ -731,6 +739,8 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.A = m->Hs;
         g.lda = d;
         g.a_rows = t.rows;
+        g.a_row0_set = t.R == 1 ? 1 : 0;
+        g.a_row0 = t.hrow0;
         g.norm_w = W.mlp_norm;
         g.W = W.wgu;
         g.N = 2 * m->F;
@@ -744,6 +754,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         gd.A = m->mlp;
         gd.lda = m->F;
         gd.a_rows = nullptr;
+        gd.a_row0_set = 0;
         gd.norm_w = nullptr;
         gd.W = W.wd;
         gd.N = d;
@@ -1368,6 +1379,10 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
         g.A = m->Hs;
         g.lda = m->d;
         g.a_rows = m->lrows(m->d_headlist);
+        if (ns == 1) {
+            g.a_row0_set = 1;
+            g.a_row0 = m->lrows(hl)[0].hrow;
+        }
     }
     g.norm_w = m->exits[ex0].norm;
     g.W = m->exits[ex0].head;
