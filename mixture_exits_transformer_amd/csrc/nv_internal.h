@@ -98,8 +98,11 @@ hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st);
 // Decode-sized row blocks (<= ATTN_DEC_ROWS rows): each item is one split of one
 // (row block, head); split partials are merged by launch_attn_combine.
 constexpr int ATTN_DEC_ROWS = 8;
-constexpr int ATTN_DEC_ITERS = 4;
-constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds   // key groups per wave: a split covers <= 16 * (512 / head_dim) keys
+// key groups per wave: a split covers at most 4 waves x (512 / head_dim) keys x 8 groups
+// (128 keys at head_dim 128; 8 groups measured better than 4 at batch 1, 16 and an 8K
+// context: fewer, longer splits with more loads in flight per wave)
+constexpr int ATTN_DEC_ITERS = 8;
+constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
                            float* out, hipStream_t st);
