@@ -612,10 +612,11 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
 // ------------------------------------------------------------------------------------------
 // Long-chunk products on bf16 activations.  k_rows_bf16 writes each row of A once as bf16
 // (RMSNormed and scaled by the norm weight when norm_w is set) into a contiguous [R][K]
-// scratch; k_gemm_bf16 then computes 128-row x BN-column tiles with four waves in a 2x2
-// layout (64 x BN/2 each), K staged through LDS in double-buffered 64-wide steps, on
-// v_mfma_f32_16x16x32_bf16 (lane layout as in k_gemm_mfma).  Epilogues as for the other
-// products (row i of the chunk keeps its a_rows / o_rows entries).
+// scratch; k_gemm_bf16 then computes 128-row x BN-column tiles with eight waves in a 4x2
+// layout (32 x BN/2 each), K in 64-wide steps through two or three LDS stages filled by
+// direct global-to-LDS loads, on v_mfma_f32_16x16x32_bf16 (lane layout as in
+// k_gemm_mfma).  Epilogues as for the other products (row i of the chunk keeps its
+// a_rows / o_rows entries).
 // ------------------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_rows_bf16(const float* A, int64_t lda, const RowInfo* rows, int R, int K,
@@ -737,13 +738,20 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-template <int BN, int HEAD, int EPI, int ST>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
-    constexpr int WN = BN / 2;                        // columns per wave
+// Eight waves per block (NW/2 x 2, each 32 rows x BN/2 columns): against four waves of
+// 64 rows, twice the waves per CU to cover latency for a third more fragment reads.
+constexpr int GB_NW = 8;
+
+template <int BN, int HEAD, int EPI, int ST, int NW = GB_NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
+    constexpr int NTH = 64 * NW;                      // threads
+    constexpr int WN = BN / 2;                        // columns per wave (waves in NW/2 x 2)
     constexpr int NT = WN / 16;
-    constexpr int MT = 4;                             // 64 rows per wave
-    constexpr int ACH = GB_BM * GB_BK / 8 / 256;      // 16-byte chunks per thread per tile
-    constexpr int WCH = BN * GB_BK / 8 / 256;
+    constexpr int WR = GB_BM / (NW / 2);              // rows per wave
+    constexpr int MT = WR / 16;
+    constexpr int ACH = GB_BM * GB_BK / 8 / NTH;      // 16-byte chunks per thread per tile
+    constexpr int WCH = BN * GB_BK / 8 / NTH;
+    static_assert(ACH * NTH * 8 == GB_BM * GB_BK && WCH * NTH * 8 == BN * GB_BK, "tile chunks per thread");
     constexpr int NL = ACH + WCH;                     // loads per thread per tile
     constexpr int A_EL = GB_BM * GB_LDK, W_EL = BN * GB_LDK;
     constexpr int CLD = BN + 4;                       // fp32 output tile row stride
@@ -761,7 +769,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     const uint16_t* Ab = a.abf;
     const uint16_t* Wb = (const uint16_t*)a.W;
     // tile kt into stage s: load j of a wave fills chunk slots p0 .. p0 + 63 of the stage
-    // (p0 = 256 j + 64 wave); slot p is row p / 8, position p % 8, which holds the row's
+    // (p0 = 64 NW j + 64 wave); slot p is row p / 8, position p % 8, which holds the row's
     // k-chunk (p % 8) ^ gb_swz(row)
     auto issue = [&](int kt, int s) __attribute__((always_inline)) {
         const int k0 = kt * GB_BK;
@@ -769,7 +777,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         uint16_t* const Wd = Ws + s * W_EL;
 #pragma unroll
         for (int j = 0; j < ACH; ++j) {
-            const int p0 = 256 * j + 64 * wave, p = p0 + lane, row = p >> 3;
+            const int p0 = NTH * j + 64 * wave, p = p0 + lane, row = p >> 3;
             const int grow = min(m0 + row, a.R - 1);   // rows past R are computed and dropped
             const int g = (p & 7) ^ gb_swz(row);
             __builtin_amdgcn_global_load_lds((const void*)(Ab + (int64_t)grow * K + k0 + 8 * g), NV_LDS(Ad + 8 * p0),
@@ -777,7 +785,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < WCH; ++j) {
-            const int p0 = 256 * j + 64 * wave, p = p0 + lane, row = p >> 3;
+            const int p0 = NTH * j + 64 * wave, p = p0 + lane, row = p >> 3;
             const int g = (p & 7) ^ gb_swz(row);
             __builtin_amdgcn_global_load_lds((const void*)(Wb + (int64_t)(n0 + row) * K + k0 + 8 * g),
                                              NV_LDS(Wd + 8 * p0), 16, 0, 0);
@@ -814,7 +822,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
             const int kch = 4 * h + (lane >> 4);          // 16-byte k-chunk of this lane
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
-                const int row = wm * 64 + i * 16 + (lane & 15);
+                const int row = wm * WR + i * 16 + (lane & 15);
                 af[h][i] = __builtin_bit_cast(bf16x8_t,
                                               *(const u32x4*)&Ab_l[row * GB_LDK + ((kch ^ gb_swz(row)) << 3)]);
             }
@@ -851,10 +859,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                Cs[(wm * 64 + i * 16 + 4 * (lane >> 4) + e) * CLD + wn * WN + t * 16 + (lane & 15)] = acc[i][t][e];
+                Cs[(wm * WR + i * 16 + 4 * (lane >> 4) + e) * CLD + wn * WN + t * 16 + (lane & 15)] = acc[i][t][e];
     __syncthreads();
     const int rows = min(GB_BM, a.R - m0);
-    for (int idx = tid; idx < rows * (BN / 2); idx += 256) {
+    for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
         const int r = idx / (BN / 2), c = 2 * (idx - r * (BN / 2));
         const float2 v = *(const float2*)&Cs[r * CLD + c];
         epi_pair_t<EPI>(a, m0 + r, n0 + c, v.x, v.y);
@@ -862,18 +870,19 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
 }
 
-template <int BN, int ST>
+template <int BN, int ST, int NW = GB_NW>
 static void launch_gemm_bf16_bn(const GemmArgs& a, dim3 grid, hipStream_t st) {
+    const dim3 blk(64 * NW);
     if (a.head) {
-        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE, ST>), grid, dim3(256), 0, st, a);
+        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE, ST, NW>), grid, blk, 0, st, a);
         return;
     }
     switch (a.epi) {
-        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE, ST>), grid, dim3(256), 0, st, a); break;
-        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID, ST>), grid, dim3(256), 0, st, a); break;
-        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU, ST>), grid, dim3(256), 0, st, a); break;
-        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV, ST>), grid, dim3(256), 0, st, a); break;
-        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU, ST>), grid, dim3(256), 0, st, a); break;
+        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE, ST, NW>), grid, blk, 0, st, a); break;
+        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID, ST, NW>), grid, blk, 0, st, a); break;
+        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU, ST, NW>), grid, blk, 0, st, a); break;
+        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV, ST, NW>), grid, blk, 0, st, a); break;
+        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU, ST, NW>), grid, blk, 0, st, a); break;
     }
 }
 
@@ -1304,9 +1313,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         const bool wide = a.N % 128 == 0 && 4 * b128 >= 3 * 512 * ((b128 + 511) / 512);
         const int stg = wide ? 2 : b64 <= 512 ? 3 : 2;
         if (t_ev_stop)
-            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d, %d>(nv::GemmArgs)",
+            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d, %d, %d>(nv::GemmArgs)",
                      a.abf_ready ? "" : "nv::k_rows_bf16 + ", wide ? 128 : 64, a.head ? 1 : 0,
-                     a.head ? (int)EPI_STORE : a.epi, stg);
+                     a.head ? (int)EPI_STORE : a.epi, stg, GB_NW);
         if (wide) launch_gemm_bf16_bn<128, 2>(b, dim3(a.N / 128, mt), st);
         else if (stg == 3) launch_gemm_bf16_bn<64, 3>(b, dim3(a.N / 64, mt), st);
         else launch_gemm_bf16_bn<64, 2>(b, dim3(a.N / 64, mt), st);
