@@ -109,6 +109,8 @@ hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, con
 // Matrix-core variant of launch_attn for a bf16 KV cache and head_dim 32, 64 or 128:
 // items of up to 64 rows, key ranges starting at multiples of 64.
 bool attn_mfma_ok(const LayerDims& D);
+// Rows per item of the matrix-core chunk attention: one wave per 16 rows (4 or 8 waves).
+constexpr int ATTN_MFMA_ROWS = 128;
 hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
                             int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st);
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,

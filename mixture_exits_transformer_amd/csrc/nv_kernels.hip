@@ -1511,7 +1511,6 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
 // partials that k_attn_combine merges, as k_attn writes them.
 // ------------------------------------------------------------------------------------------
 
-constexpr int AM_ROWS = 64;   // rows per item
 constexpr int AM_KT = 64;     // keys per tile
 
 // Column swizzle of the transposed V tile: row r (one value dim) holds key k at column
@@ -1520,8 +1519,8 @@ constexpr int AM_KT = 64;     // keys per tile
 // 8 apart hit 16 different banks instead of 2.
 __device__ __forceinline__ int vt_swz(int r) { return ((r >> 3) & 15) * 4; }
 
-template <int HD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(
+template <int HD, int NWA>
+__global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(
     const AttnItem* items, const RowInfo* rows, const float* q, const uint16_t* kv, int layer, LayerDims D,
     float* part_ml, float* part_o, float* out, unsigned long long* stamp) {
     const unsigned long long t_begin = stamp_begin(stamp);
@@ -1530,7 +1529,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     constexpr int NKS = HD / 32;        // k-steps of the score product
     constexpr int NHT = HD / 16;        // 16-wide output tiles
     constexpr int CPR = HD / 8;         // 16-byte chunks per key row
-    constexpr int CPT = AM_KT * CPR / 256;   // chunks per thread per tile, for K and for V
+    constexpr int NTH = 64 * NWA;
+    constexpr int NCH = AM_KT * CPR;              // 16-byte chunks per tile, for K and for V
+    constexpr int CPT = (NCH + NTH - 1) / NTH;    // per thread (threads past NCH load none)
     __shared__ __align__(16) uint16_t Ks[2][AM_KT * KLD];
     __shared__ __align__(16) uint16_t Vt[2][HD * VLD];
     const AttnItem it = items[blockIdx.x];
@@ -1567,7 +1568,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     auto gload = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const int c = tid + 256 * j;
+            const int c = tid + NTH * j;
+            if (NCH % NTH != 0 && c >= NCH) break;
             const int key = min(t0 + c / CPR, it.hi - 1);   // rows past the range are masked
             const int col = (c % CPR) * 8;
             kr[j] = *(const u32x4*)(Kg + (int64_t)key * HD + col);
@@ -1577,7 +1579,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const int c = tid + 256 * j;
+            const int c = tid + NTH * j;
+            if (NCH % NTH != 0 && c >= NCH) break;
             const int key = c / CPR, col = (c % CPR) * 8;
             *(u32x4*)&Ks[buf][key * KLD + col] = kr[j];
             const uint32_t w4[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
@@ -1687,15 +1690,18 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
                             int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st) {
     if (n_items <= 0) return hipSuccess;
     if (!attn_mfma_ok(D)) return hipErrorInvalidValue;
+    constexpr int NWA = ATTN_MFMA_ROWS / 16;
+    static_assert(NWA * 16 == ATTN_MFMA_ROWS && (NWA == 4 || NWA == 8), "64 or 128 rows per item");
     const uint16_t* k16 = (const uint16_t*)kv;
+    const dim3 blk(64 * NWA);
     if (D.hd == 128)
-        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128, NWA>), dim3(n_items), blk, 0, st, items, rows, q, k16, layer, D,
                   part_ml, part_o, out, t_stamp);
     else if (D.hd == 64)
-        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64, NWA>), dim3(n_items), blk, 0, st, items, rows, q, k16, layer, D,
                   part_ml, part_o, out, t_stamp);
     else
-        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32>), dim3(n_items), dim3(256), 0, st, items, rows, q, k16, layer, D,
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32, NWA>), dim3(n_items), blk, 0, st, items, rows, q, k16, layer, D,
                   part_ml, part_o, out, t_stamp);
     return hipGetLastError();
 }

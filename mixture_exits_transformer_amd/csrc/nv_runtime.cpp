@@ -29,7 +29,6 @@ namespace {
 
 constexpr int kMaxExits = 4;
 constexpr int kAttnRowsPerItem = 32;
-constexpr int AM_ROWS_PER_ITEM = 64;   // rows per item of the matrix-core chunk attention
 constexpr int kDecodeRows = 64;          // launch groups up to this many rows use decode attention
 constexpr int kAttnBlocksTarget = 512;   // decode attention: aim for about this many blocks
 constexpr size_t kAlign = 256;
@@ -559,7 +558,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         // long chunks: row blocks of 32 rows (64 on the matrix cores) sharing LDS key tiles;
         // the key range is split into pieces of split_len keys (doubling until the partial
         // slots fit), combined by a separate pass
-        const int rpi = attn_mfma_ok(m->dims()) ? AM_ROWS_PER_ITEM : kAttnRowsPerItem;
+        const int rpi = attn_mfma_ok(m->dims()) ? ATTN_MFMA_ROWS : kAttnRowsPerItem;
         int split_len = 512;
         for (;;) {
             long slots = 0, items = 0;

@@ -1,9 +1,10 @@
 """Matrix-core chunk attention (launch groups of more than 64 rows on a bf16 KV cache)
 against the oracle, for head_dim 32, 64 and 128.
 
-A full-depth prefill of 65, 200 and 1100 positions (one row block plus a 1-row tail;
-several row blocks with a ragged tail; key ranges split at 512 and merged by the combine
-pass) on small 4-layer bf16 models.  Every layer's keys and values (each layer's input
+A full-depth prefill of 65, 200 and 1100 positions on small 4-layer bf16 models, with
+128-row items of eight 16-row waves: one item holding 65 rows (four full waves, one with a
+single row, three with none); a full item and a ragged 72-row one; nine items with key
+ranges split at 512 and merged by the combine pass.  Every layer's keys and values (each layer's input
 went through the previous layer's attention) and the final hidden states (through the
 last layer's attention) within 2e-2 relative."""
 import numpy as np
