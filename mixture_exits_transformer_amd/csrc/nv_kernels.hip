@@ -742,29 +742,29 @@ __device__ __forceinline__ void barrier_nofence() {
 // 64 rows, twice the waves per CU to cover latency for a third more fragment reads.
 constexpr int GB_NW = 8;
 
-template <int BN, int HEAD, int EPI, int ST, int NW = GB_NW>
+template <int BN, int HEAD, int EPI, int ST, int NW = GB_NW, int BM = GB_BM>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
     constexpr int NTH = 64 * NW;                      // threads
     constexpr int WN = BN / 2;                        // columns per wave (waves in NW/2 x 2)
     constexpr int NT = WN / 16;
-    constexpr int WR = GB_BM / (NW / 2);              // rows per wave
+    constexpr int WR = BM / (NW / 2);              // rows per wave
     constexpr int MT = WR / 16;
-    constexpr int ACH = GB_BM * GB_BK / 8 / NTH;      // 16-byte chunks per thread per tile
+    constexpr int ACH = BM * GB_BK / 8 / NTH;      // 16-byte chunks per thread per tile
     constexpr int WCH = BN * GB_BK / 8 / NTH;
-    static_assert(ACH * NTH * 8 == GB_BM * GB_BK && WCH * NTH * 8 == BN * GB_BK, "tile chunks per thread");
+    static_assert(ACH * NTH * 8 == BM * GB_BK && WCH * NTH * 8 == BN * GB_BK, "tile chunks per thread");
     constexpr int NL = ACH + WCH;                     // loads per thread per tile
-    constexpr int A_EL = GB_BM * GB_LDK, W_EL = BN * GB_LDK;
+    constexpr int A_EL = BM * GB_LDK, W_EL = BN * GB_LDK;
     constexpr int CLD = BN + 4;                       // fp32 output tile row stride
-    constexpr int OPER_B = ST * (A_EL + W_EL) * 2, OUT_B = GB_BM * CLD * 4;
+    constexpr int OPER_B = ST * (A_EL + W_EL) * 2, OUT_B = BM * CLD * 4;
     static_assert(ST == 2 || ST == 3, "two or three operand stages");
     __shared__ __align__(16) unsigned char smem[OPER_B > OUT_B ? OPER_B : OUT_B];
-    uint16_t* const As = (uint16_t*)smem;             // [ST][GB_BM][GB_LDK]
+    uint16_t* const As = (uint16_t*)smem;             // [ST][BM][GB_LDK]
     uint16_t* const Ws = As + ST * A_EL;              // [ST][BN][GB_LDK]
-    float* const Cs = (float*)smem;                   // [GB_BM][CLD] after the last product
+    float* const Cs = (float*)smem;                   // [BM][CLD] after the last product
     const unsigned long long t_begin = stamp_begin(a.stamp);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * GB_BM;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int K = a.K;
     const uint16_t* Ab = a.abf;
     const uint16_t* Wb = (const uint16_t*)a.W;
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
             for (int e = 0; e < 4; ++e)
                 Cs[(wm * WR + i * 16 + 4 * (lane >> 4) + e) * CLD + wn * WN + t * 16 + (lane & 15)] = acc[i][t][e];
     __syncthreads();
-    const int rows = min(GB_BM, a.R - m0);
+    const int rows = min(BM, a.R - m0);
     for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
         const int r = idx / (BN / 2), c = 2 * (idx - r * (BN / 2));
         const float2 v = *(const float2*)&Cs[r * CLD + c];
@@ -870,19 +870,19 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
     stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
 }
 
-template <int BN, int ST, int NW = GB_NW>
+template <int BN, int ST, int NW = GB_NW, int BM = GB_BM>
 static void launch_gemm_bf16_bn(const GemmArgs& a, dim3 grid, hipStream_t st) {
     const dim3 blk(64 * NW);
     if (a.head) {
-        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE, ST, NW>), grid, blk, 0, st, a);
+        NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 1, EPI_STORE, ST, NW, BM>), grid, blk, 0, st, a);
         return;
     }
     switch (a.epi) {
-        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE, ST, NW>), grid, blk, 0, st, a); break;
-        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID, ST, NW>), grid, blk, 0, st, a); break;
-        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU, ST, NW>), grid, blk, 0, st, a); break;
-        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV, ST, NW>), grid, blk, 0, st, a); break;
-        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU, ST, NW>), grid, blk, 0, st, a); break;
+        case EPI_STORE: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_STORE, ST, NW, BM>), grid, blk, 0, st, a); break;
+        case EPI_RESID: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_RESID, ST, NW, BM>), grid, blk, 0, st, a); break;
+        case EPI_SWIGLU: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SWIGLU, ST, NW, BM>), grid, blk, 0, st, a); break;
+        case EPI_QKV: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_QKV, ST, NW, BM>), grid, blk, 0, st, a); break;
+        default: NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_bf16<BN, 0, EPI_SILU, ST, NW, BM>), grid, blk, 0, st, a); break;
     }
 }
 
@@ -1312,11 +1312,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         const long b128 = (a.N / 128) * (long)mt, b64 = (a.N / 64) * (long)mt;
         const bool wide = a.N % 128 == 0 && 4 * b128 >= 3 * 512 * ((b128 + 511) / 512);
         const int stg = wide ? 2 : b64 <= 512 ? 3 : 2;
+        // narrow products on up to 1024 rows take 64-row tiles (twice the blocks; prefill of
+        // 256 rows 5.4 -> 4.8 ms at 1.5B); at 2047 rows the 128-row tiles measured faster
+        const bool half = !wide && stg == 3 && mt <= 8;
         if (t_ev_stop)
-            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d, %d, %d>(nv::GemmArgs)",
+            snprintf(t_name, sizeof(t_name), "%svoid nv::k_gemm_bf16<%d, %d, %d, %d, %d, %d>(nv::GemmArgs)",
                      a.abf_ready ? "" : "nv::k_rows_bf16 + ", wide ? 128 : 64, a.head ? 1 : 0,
-                     a.head ? (int)EPI_STORE : a.epi, stg, GB_NW);
+                     a.head ? (int)EPI_STORE : a.epi, stg, GB_NW, half ? 64 : GB_BM);
         if (wide) launch_gemm_bf16_bn<128, 2>(b, dim3(a.N / 128, mt), st);
+        else if (stg == 3 && half) launch_gemm_bf16_bn<64, 3, GB_NW, 64>(b, dim3(a.N / 64, (a.R + 63) / 64), st);
         else if (stg == 3) launch_gemm_bf16_bn<64, 3>(b, dim3(a.N / 64, mt), st);
         else launch_gemm_bf16_bn<64, 2>(b, dim3(a.N / 64, mt), st);
         return hipGetLastError();
