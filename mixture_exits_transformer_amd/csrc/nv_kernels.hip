@@ -1916,49 +1916,57 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
     const int64_t kb = kv_base(D, seq, layer, 0, it.head) + dl * DPL;
     const int64_t vb = kv_base(D, seq, layer, 1, it.head) + dl * DPL;
 
-    // queries first, then every key/value group of this wave, all in flight before any use
-    const float scale = 1.0f / sqrtf((float)HD);
-    float qv[RM][DPL];
+    // the raw query first, then every key/value group of this wave; the query is scaled
+    // only after the key loads are issued (scaling it earlier would make them wait for it),
+    // so the first key groups can be used while later ones are still arriving
+    // (unconditional: rows past nr read the last row and are masked when scaled)
+    float4 qa[RM][2];
     int qpos[RM];
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-        qpos[r] = -1;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) qv[r][e] = 0.f;
-        if (r < nr) {
-            const float* qp = q + (int64_t)(it.row0 + r) * D.d + it.head * HD + dl * DPL;
-            const float4 a0 = *(const float4*)qp, a1 = *(const float4*)(qp + 4);
-            qv[r][0] = a0.x * scale; qv[r][1] = a0.y * scale; qv[r][2] = a0.z * scale; qv[r][3] = a0.w * scale;
-            qv[r][4] = a1.x * scale; qv[r][5] = a1.y * scale; qv[r][6] = a1.z * scale; qv[r][7] = a1.w * scale;
-            qpos[r] = rows[it.row0 + r].pos;
-        }
+        const int rr = it.row0 + min(r, nr - 1);
+        const float* qp = q + (int64_t)rr * D.d + it.head * HD + dl * DPL;
+        qa[r][0] = *(const float4*)qp;
+        qa[r][1] = *(const float4*)(qp + 4);
+        qpos[r] = rows[rr].pos;
     }
 
     uint4 kr[NIT], vr[NIT];
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {
-        const int key = it.lo + (i * 4 + wave) * KPI + g;
-        if (key < it.hi) {
-            if constexpr (KVBF) {
-                kr[i] = *(const uint4*)((const uint16_t*)kv + kb + (int64_t)key * HD);
-                vr[i] = *(const uint4*)((const uint16_t*)kv + vb + (int64_t)key * HD);
-            } else {
-                kr[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD);
-                vr[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD);
-            }
+        // keys past the range load the last key (masked below): every load is unconditional,
+        // so all are issued back to back and waited for in order
+        const int key = min(it.lo + (i * 4 + wave) * KPI + g, it.hi - 1);
+        if constexpr (KVBF) {
+            kr[i] = *(const uint4*)((const uint16_t*)kv + kb + (int64_t)key * HD);
+            vr[i] = *(const uint4*)((const uint16_t*)kv + vb + (int64_t)key * HD);
+        } else {
+            kr[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD);
+            vr[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD);
         }
     }
     uint4 kr2[KVBF ? 1 : NIT], vr2[KVBF ? 1 : NIT];   // fp32 keys need a second 16-byte load
     if constexpr (!KVBF) {
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            const int key = it.lo + (i * 4 + wave) * KPI + g;
-            if (key < it.hi) {
-                kr2[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD + 4);
-                vr2[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD + 4);
-            }
+            const int key = min(it.lo + (i * 4 + wave) * KPI + g, it.hi - 1);
+            kr2[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD + 4);
+            vr2[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD + 4);
         }
     }
+
+    __builtin_amdgcn_sched_barrier(0);
+    const float scale = 1.0f / sqrtf((float)HD);
+    float qv[RM][DPL];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        const float sr = r < nr ? scale : 0.f;
+        qv[r][0] = qa[r][0].x * sr; qv[r][1] = qa[r][0].y * sr; qv[r][2] = qa[r][0].z * sr;
+        qv[r][3] = qa[r][0].w * sr; qv[r][4] = qa[r][1].x * sr; qv[r][5] = qa[r][1].y * sr;
+        qv[r][6] = qa[r][1].z * sr; qv[r][7] = qa[r][1].w * sr;
+        if (r >= nr) qpos[r] = -1;
+    }
+
     float m[RM], l[RM], o[RM][DPL];
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
