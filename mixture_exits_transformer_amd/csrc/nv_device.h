@@ -14,12 +14,14 @@ namespace nv {
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t b = __float_as_uint(f);
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return (uint16_t)(b >> 16);
+// float -> bf16 bits, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one instruction
+// for a pair).
+typedef __bf16 nv_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float nv_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((nv_f32x2_t){lo, hi}, nv_bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)cvt_bf2(f, 0.0f); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -510,9 +510,7 @@ __global__ __launch_bounds__(256) void k_row_rms(const float* A, int64_t lda, co
     if (lane == 0) inv[r] = 1.0f / sqrtf(ss / (float)K + eps);
 }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return cvt_bf2(lo, hi); }
 
 template <int BN, int HEAD>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
@@ -1548,10 +1546,12 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     const uint16_t* Kg = kv + kv_base(D, seq, layer, 0, it.head);
     const uint16_t* Vg = kv + kv_base(D, seq, layer, 1, it.head);
 
-    // queries (B operand of the score product), pre-scaled by 1/sqrt(hd)
+    // queries (B operand of the score product), pre-scaled by log2(e)/sqrt(hd): the scores
+    // come out in base-2 units, so each probability is one exp2 (the running max is
+    // converted back to natural-log units where split partials are written)
     bf16x8_t qf[NKS];
     {
-        const float scale = 1.0f / sqrtf((float)HD);
+        const float scale = 1.4426950408889634f / sqrtf((float)HD);
         const float* qr = q + (int64_t)(it.row0 + (rv ? r : 0)) * D.d + it.head * HD;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -1599,6 +1599,11 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
     for (int t = 0; t < NHT; ++t) o[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
+    // the wave's lowest query position (rows past nrows excluded): key tiles wholly at or
+    // below it, and inside the item's range, need no mask
+    int qmin = rv ? qpos : INT_MAX;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) qmin = min(qmin, __shfl_xor(qmin, off, 64));
 
     const int ntile = (it.hi - it.lo + AM_KT - 1) / AM_KT;
     gload(it.lo);
@@ -1619,30 +1624,50 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
                                                                  0, 0, 0);
             }
         }
-        // mask (causal and the item's key range) and the running max of this lane's query
+        // mask (causal and the item's key range; only on tiles that cross either bound) and
+        // the running max of this lane's query
+        const bool full = t0 + AM_KT <= it.hi && t0 + AM_KT - 1 <= qmin;   // wave-uniform
         float tmax = -INFINITY;
+        if (full) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = t0 + 16 * mt + 4 * g + i;
-                const bool ok = key < it.hi && key <= qpos;
-                sc[mt][i] = ok ? sc[mt][i] : -INFINITY;
-                tmax = fmaxf(tmax, sc[mt][i]);
-            }
+                for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[mt][i]);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = t0 + 16 * mt + 4 * g + i;
+                    const bool ok = key < it.hi && key <= qpos;
+                    sc[mt][i] = ok ? sc[mt][i] : -INFINITY;
+                    tmax = fmaxf(tmax, sc[mt][i]);
+                }
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mn = fmaxf(m, tmax);
-        const float alpha = (mn == -INFINITY) ? 1.0f : __expf(m - mn);
+        const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
         float ps = 0.f;
+        if (full) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pv = (sc[mt][i] == -INFINITY) ? 0.f : __expf(sc[mt][i] - mn);
-                sc[mt][i] = pv;
-                ps += pv;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = __builtin_amdgcn_exp2f(sc[mt][i] - mn);
+                    sc[mt][i] = pv;
+                    ps += pv;
+                }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = (sc[mt][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[mt][i] - mn);
+                    sc[mt][i] = pv;
+                    ps += pv;
+                }
+        }
         lsum = lsum * alpha + ps;
         m = mn;
 #pragma unroll
@@ -1678,7 +1703,7 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     } else if (rv) {
         const int64_t slot = it.part + r;
         if (g == 0) {
-            part_ml[2 * slot] = m;
+            part_ml[2 * slot] = m * 0.6931471805599453f;   // back to natural-log units
             part_ml[2 * slot + 1] = lsum;
         }
         float* po = part_o + slot * HD;
@@ -1714,9 +1739,12 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
 // threads per pair.  The split maxima and the weights exp(m_s - M) are formed by all
 // threads together (block reductions, weights kept in LDS); each value dim's weighted sum
 // is then spread over 512 / hd thread subsets that take every (512 / hd)-th split, and the
-// subsets are added in LDS.
+// subsets are added in LDS.  The first splits' (max, sum) pairs and partial outputs are
+// loaded before the reductions (indexes clamped to the last split, never summed), so the
+// block waits on memory once for them.
 constexpr int COMB_MAX = 4096;   // splits of one (row, head) whose weights LDS holds
 constexpr int COMB_WAVE_MIN_PAIRS = 2048;   // (row, head) pairs from which one wave per pair is used
+constexpr int COMB_PRE = 8;      // partial outputs per thread loaded ahead of the reductions
 
 __global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci, int R, LayerDims D,
                                                           const float* part_ml, const float* part_o, float* out,
@@ -1731,8 +1759,14 @@ __global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci,
     if (c.nsplit > 1) {
         const int ns = c.nsplit, hd = D.hd;
         const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
-        float mx = -INFINITY;
-        for (int sp = tid; sp < ns; sp += 512) mx = fmaxf(mx, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
+        const int Q = 512 / hd, e = tid % hd, q = tid / hd;
+        float pre[COMB_PRE];
+#pragma unroll
+        for (int j = 0; j < COMB_PRE; ++j)
+            pre[j] = part_o[(base + (int64_t)min(q + j * Q, ns - 1) * c.nrows) * hd + e];
+        const float2 ml0 = *(const float2*)(part_ml + 2 * (base + (int64_t)min(tid, ns - 1) * c.nrows));
+        float mx = tid < ns ? ml0.x : -INFINITY;
+        for (int sp = tid + 512; sp < ns; sp += 512) mx = fmaxf(mx, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
         mx = wave_max(mx);
         if (lane == 0) wred[wave] = mx;
         __syncthreads();
@@ -1741,7 +1775,12 @@ __global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci,
         for (int w = 1; w < 8; ++w) M = fmaxf(M, wred[w]);
         __syncthreads();
         float ls = 0.f;
-        for (int sp = tid; sp < ns; sp += 512) {
+        if (tid < ns) {
+            const float w = ml0.x == -INFINITY ? 0.f : expf(ml0.x - M);
+            wsh[tid] = w;
+            ls += w * ml0.y;
+        }
+        for (int sp = tid + 512; sp < ns; sp += 512) {
             const float2 ml = *(const float2*)(part_ml + 2 * (base + (int64_t)sp * c.nrows));
             const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
             wsh[sp] = w;
@@ -1753,10 +1792,12 @@ __global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci,
         float L = 0.f;
 #pragma unroll
         for (int w = 0; w < 8; ++w) L += wred[w];
-        const int Q = 512 / hd, e = tid % hd, q = tid / hd;
         float o = 0.f;
+#pragma unroll
+        for (int j = 0; j < COMB_PRE; ++j)
+            if (q + j * Q < ns) o += wsh[q + j * Q] * pre[j];
 #pragma unroll 4
-        for (int sp = q; sp < ns; sp += Q) o += wsh[sp] * part_o[(base + (int64_t)sp * c.nrows) * hd + e];
+        for (int sp = q + COMB_PRE * Q; sp < ns; sp += Q) o += wsh[sp] * part_o[(base + (int64_t)sp * c.nrows) * hd + e];
         red[tid] = o;
         __syncthreads();
         if (tid < hd) {
@@ -1768,10 +1809,67 @@ __global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci,
     stamp_end(stamp, t_begin);
 }
 
-// Merge the split partials of one (row, head), one wave each (four per block): every lane
-// folds the (max, sum) pairs of all splits (the max first, then the weights exp(max - M)),
-// then forms two output dims as the weighted sum of the splits' partial outputs.  Rows
-// whose key range was not split were written by the attention kernel and are skipped.
+// The softmax merge of one (row, head)'s split partials for this lane's two output dims
+// e, e+1: the max M of the splits' maxima first, then the weights exp(max - M) applied to
+// the sums and partial outputs, in split order.  Up to NS splits: every (max, sum) pair
+// and partial output is loaded before any is used (indexes clamped to the last split,
+// which the folds stop before), so the wave waits on memory once, not once per split.
+template <int NS>
+__device__ __forceinline__ float2 merge_splits_n(const float* part_ml, const float* part_o, int64_t base, int ns,
+                                                 int nrows, int hd, int e) {
+    float2 ml[NS], v[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int64_t slot = base + (int64_t)min(j, ns - 1) * nrows;
+        ml[j] = *(const float2*)(part_ml + 2 * slot);
+        v[j] = *(const float2*)(part_o + slot * hd + e);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+        if (j < ns) M = fmaxf(M, ml[j].x);
+    float L = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+        if (j < ns) {
+            const float w = ml[j].x == -INFINITY ? 0.f : expf(ml[j].x - M);
+            L += w * ml[j].y;
+            a0 += w * v[j].x;
+            a1 += w * v[j].y;
+        }
+    return make_float2(a0 / L, a1 / L);
+}
+
+// The same merge for any number of splits, one split at a time.
+__device__ __forceinline__ float2 merge_splits_any(const float* part_ml, const float* part_o, int64_t base, int ns,
+                                                   int nrows, int hd, int e) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[2 * (base + (int64_t)sp * nrows)]);
+    float L = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+        const int64_t slot = base + (int64_t)sp * nrows;
+        const float2 ml = *(const float2*)(part_ml + 2 * slot);
+        const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
+        L += w * ml.y;
+        const float2 v = *(const float2*)(part_o + slot * hd + e);
+        a0 += w * v.x;
+        a1 += w * v.y;
+    }
+    return make_float2(a0 / L, a1 / L);
+}
+
+// Dispatch on the split count (uniform across the wave: one wave per (row, head)).
+__device__ __forceinline__ float2 merge_splits(const float* part_ml, const float* part_o, int64_t base, int ns,
+                                               int nrows, int hd, int e) {
+    if (ns <= 2) return merge_splits_n<2>(part_ml, part_o, base, ns, nrows, hd, e);
+    if (ns <= 4) return merge_splits_n<4>(part_ml, part_o, base, ns, nrows, hd, e);
+    if (ns <= 8) return merge_splits_n<8>(part_ml, part_o, base, ns, nrows, hd, e);
+    return merge_splits_any(part_ml, part_o, base, ns, nrows, hd, e);
+}
+
+// Merge the split partials of one (row, head), one wave each (four per block), each lane
+// forming two output dims.  Rows whose key range was not split were written by the
+// attention kernel and are skipped.
 __global__ __launch_bounds__(256) void k_attn_combine(const CombineInfo* ci, int R, LayerDims D, const float* part_ml,
                                                       const float* part_o, float* out, unsigned long long* stamp) {
     const unsigned long long t_begin = stamp_begin(stamp);
@@ -1780,25 +1878,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(const CombineInfo* ci, int
     if (p < R * D.H) {
         const int i = p / D.H, h = p - i * D.H;
         const CombineInfo c = ci[i];
-        if (c.nsplit > 1) {
-            const int ns = c.nsplit, hd = D.hd;
-            const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
-            float M = -INFINITY;
-            for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
-            float L = 0.f, o0 = 0.f, o1 = 0.f;
-            const int e = 2 * lane;
-            for (int sp = 0; sp < ns; ++sp) {
-                const int64_t slot = base + (int64_t)sp * c.nrows;
-                const float2 ml = *(const float2*)(part_ml + 2 * slot);
-                const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
-                L += w * ml.y;
-                if (e < hd) {
-                    const float2 v = *(const float2*)(part_o + slot * hd + e);
-                    o0 += w * v.x;
-                    o1 += w * v.y;
-                }
-            }
-            if (e < hd) *(float2*)(out + (int64_t)i * D.d + h * hd + e) = make_float2(o0 / L, o1 / L);
+        const int e = 2 * lane;
+        if (c.nsplit > 1 && e < D.hd) {
+            const int64_t base = c.base + (int64_t)h * c.nsplit * c.nrows + c.off;   // split s adds s * nrows
+            *(float2*)(out + (int64_t)i * D.d + h * D.hd + e) =
+                merge_splits(part_ml, part_o, base, c.nsplit, c.nrows, D.hd, e);
         }
     }
     stamp_end(stamp, t_begin);
@@ -1819,30 +1903,14 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(const CombineInfo* ci
     const int hd = D.hd, e = 2 * lane;
     if (e >= hd) return;
     const int64_t o = (int64_t)i * D.d + h * hd + e;
-    float o0, o1;
+    float2 v;
     if (c.nsplit > 1) {
-        const int ns = c.nsplit;
-        const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
-        float M = -INFINITY;
-        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[2 * (base + (int64_t)sp * c.nrows)]);
-        float L = 0.f, a0 = 0.f, a1 = 0.f;
-        for (int sp = 0; sp < ns; ++sp) {
-            const int64_t slot = base + (int64_t)sp * c.nrows;
-            const float2 ml = *(const float2*)(part_ml + 2 * slot);
-            const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
-            L += w * ml.y;
-            const float2 v = *(const float2*)(part_o + slot * hd + e);
-            a0 += w * v.x;
-            a1 += w * v.y;
-        }
-        o0 = a0 / L;
-        o1 = a1 / L;
+        const int64_t base = c.base + (int64_t)h * c.nsplit * c.nrows + c.off;   // split s adds s * nrows
+        v = merge_splits(part_ml, part_o, base, c.nsplit, c.nrows, hd, e);
     } else {
-        const float2 v = *(const float2*)(attn_o + o);
-        o0 = v.x;
-        o1 = v.y;
+        v = *(const float2*)(attn_o + o);
     }
-    *(uint32_t*)(out_bf16 + o) = pack_bf2(o0, o1);
+    *(uint32_t*)(out_bf16 + o) = pack_bf2(v.x, v.y);
 }
 
 hipError_t launch_attn_combine_bf16(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,
