@@ -1515,11 +1515,17 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
 
 constexpr int AM_KT = 64;     // keys per tile
 
-// Column swizzle of the transposed V tile: row r (one value dim) holds key k at column
-// k ^ vt_swz(r).  The mask is a multiple of 4, so aligned groups of four keys stay
-// contiguous for the 8-byte operand reads, and the 16 lanes that store one key into rows
-// 8 apart hit 16 different banks instead of 2.
-__device__ __forceinline__ int vt_swz(int r) { return ((r >> 3) & 15) * 4; }
+// V operand reads: ds_read_b64_tr_b16 treats each group of 16 lanes as a 16 x 4 block of
+// 16-bit values (lane j's 8 bytes are row j) and returns to lane i the values
+// (row 4e + i/4, column i%4), e = 0..3.  With lane j of group g pointing at key row
+// 4g + j/4 and dims 4(j%4) .. +3 of a row-major V tile, lane i receives dim i of four
+// consecutive keys: exactly its slice of the transposed operand.  So V is staged like K
+// (coalesced 16-byte loads, one 16-byte LDS store per chunk) and transposed by the read.
+typedef short nv_s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) nv_s16x4_t*)(p)));
+}
 
 template <int HD, int NWA>
 __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(
@@ -1527,7 +1533,8 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     float* part_ml, float* part_o, float* out, unsigned long long* stamp) {
     const unsigned long long t_begin = stamp_begin(stamp);
     constexpr int KLD = HD + 8;         // K tile row stride (bf16)
-    constexpr int VLD = AM_KT + 8;      // transposed V tile row stride (bf16)
+    constexpr int VLD = HD + 16;        // V tile row stride (bf16): rows an odd multiple of 8
+                                        // banks apart, so the transposing reads are conflict-free
     constexpr int NKS = HD / 32;        // k-steps of the score product
     constexpr int NHT = HD / 16;        // 16-wide output tiles
     constexpr int CPR = HD / 8;         // 16-byte chunks per key row
@@ -1535,7 +1542,7 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     constexpr int NCH = AM_KT * CPR;              // 16-byte chunks per tile, for K and for V
     constexpr int CPT = (NCH + NTH - 1) / NTH;    // per thread (threads past NCH load none)
     __shared__ __align__(16) uint16_t Ks[2][AM_KT * KLD];
-    __shared__ __align__(16) uint16_t Vt[2][HD * VLD];
+    __shared__ __align__(16) uint16_t Vs[2][AM_KT * VLD];
     const AttnItem it = items[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qn = lane & 15, g = lane >> 4;
@@ -1587,11 +1594,7 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
             if (NCH % NTH != 0 && c >= NCH) break;
             const int key = c / CPR, col = (c % CPR) * 8;
             *(u32x4*)&Ks[buf][key * KLD + col] = kr[j];
-            const uint32_t w4[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                Vt[buf][(col + e) * VLD + (key ^ vt_swz(col + e))] =
-                    (uint16_t)((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
+            *(u32x4*)&Vs[buf][key * VLD + col] = vr[j];
         }
     };
 
@@ -1679,12 +1682,11 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
                                         pack_bf2(sc[2 * ks + 1][0], sc[2 * ks + 1][1]),
                                         pack_bf2(sc[2 * ks + 1][2], sc[2 * ks + 1][3]));
             const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+            const uint16_t* vb = &Vs[buf][(32 * ks + 4 * g + (qn >> 2)) * VLD + 4 * (qn & 3)];
 #pragma unroll
             for (int t = 0; t < NHT; ++t) {
-                const int vr_ = 16 * t + qn;
-                const uint16_t* vrow = &Vt[buf][vr_ * VLD];
-                const uint2 lo = *(const uint2*)(vrow + ((32 * ks + 4 * g) ^ vt_swz(vr_)));
-                const uint2 hi = *(const uint2*)(vrow + ((32 * ks + 16 + 4 * g) ^ vt_swz(vr_)));
+                const uint2 lo = lds_read_tr16(vb + 16 * t);              // keys 32ks + 4g + 0..3
+                const uint2 hi = lds_read_tr16(vb + 16 * VLD + 16 * t);   // keys 32ks + 16 + 4g + 0..3
                 const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pf, o[t], 0, 0, 0);
             }
