@@ -183,7 +183,15 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
-    p.loss_ch = (int)std::min<size_t>(256, rmax);
+    // rows per head pass of the mixture objective: every pass re-reads the head weights, so
+    // a pass takes as many rows as a 256 MiB logits workspace holds (at least 256, at most
+    // the row capacity); NVIUM_LOSS_ROWS sets it instead (tests of ragged passes)
+    size_t lch = std::max<size_t>(256, (size_t(256) << 20) / ((size_t)V * 4));
+    if (const char* e = std::getenv("NVIUM_LOSS_ROWS")) {
+        const long v = std::atol(e);
+        if (v > 0) lch = (size_t)v;
+    }
+    p.loss_ch = (int)std::min<size_t>(lch, rmax);
     p.loss = align_up((size_t)p.loss_ch * V * 4) + 4 * align_up((size_t)max_ctx * 32) + align_up(64) +
              2 * align_up((size_t)max_ctx * 4) + align_up((size_t)max_ctx * sizeof(RowInfo)) +
              align_up((size_t)p.loss_ch * (c.router_dim > 0 ? c.router_dim : 1) * 8);

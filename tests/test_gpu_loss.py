@@ -3,7 +3,8 @@ mixture_loss: L_mix, L_compute, L_total and every position's router outputs,
 log pi_k of the target, -log pi_mix and expected depth.
 
 - Tiny fp32 model, both exit forms (own heads + linear gate; shared head with adapters +
-  router MLP): 299 positions, i.e. head passes of 256 and a ragged 43 rows.  Router
+  router MLP): 299 positions, in one head pass per exit (the default, as many rows as a
+  256 MiB logits workspace holds) and in passes of 256 and a ragged 43 rows.  Router
   outputs within 1e-6, log-probabilities within 1e-4 absolute, the means within 1e-6
   relative.
 - The shortest sequence (two tokens, one position) and the argument errors.
@@ -54,8 +55,11 @@ def _compare(got, pp, want, tol_w, tol_lp, tol_mean, tag):
     assert abs(L_tot - want.L_total) < tol_mean * abs(want.L_total)
 
 
+@pytest.mark.parametrize("rows", [None, "256"], ids=["one-pass", "passes-256-43"])
 @pytest.mark.parametrize("shape", [OWN, FORMS], ids=["own-heads", "shared-head"])
-def test_loss_tiny_fp32(lib, weights_dir, shape):
+def test_loss_tiny_fp32(lib, weights_dir, shape, rows, monkeypatch):
+    if rows:
+        monkeypatch.setenv("NVIUM_LOSS_ROWS", rows)   # read by nv_load
     path = cached_weights(shape, weights_dir)
     M = om.OracleModel(path)
     rng = np.random.default_rng(299)
