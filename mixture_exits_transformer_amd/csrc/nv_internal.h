@@ -65,6 +65,14 @@ struct GemmArgs {
     const struct CombineInfo* comb;
     const float* part_ml;
     const float* part_o;
+    // Exit heads of the mixture objective on the long-chunk path (k_gemm_bf16 only): when
+    // xent_part is set, the logits are not stored.  Each block writes, per row and per
+    // 64-column group g, (max, sum of exp(z - max)) at xent_part[2 (row * N/64 + g)], and
+    // the block holding a row's target column writes that logit to xent_tgt[row];
+    // launch_xent_merge then forms the log-probabilities.
+    float* xent_part;     // [R][N/64][2]
+    float* xent_tgt;      // [R]
+    const int* xent_targets;   // [R] target token ids in [0, N)
 };
 
 // One row of a chunk: position `pos` of sequence `seq`; hrow = seq * max_ctx + pos
@@ -141,6 +149,10 @@ hipError_t launch_gate_mlp(const RowInfo* rows, const int* seqs, int n, const fl
 // dst row i = Hs row rows[i].hrow (d floats each).
 hipError_t launch_copy_rows(const RowInfo* rows, int n, const float* Hs, int d, float* dst, hipStream_t st);
 // out[i * ostride + ocol] = log softmax(logits row i)[targets[i]] (float64).
+// Log-probability of each row's target from the per-group partials of a fused head
+// product (GemmArgs::xent_part): out[i * ostride + ocol] = z_y - M - log sum_g s_g e^(m_g - M).
+hipError_t launch_xent_merge(const float* part, const float* tgt, int n, int ngroups, double* out, int ostride,
+                             int ocol, hipStream_t st);
 hipError_t launch_xent(const float* logits, int64_t ld, int n, int V, const int* targets, double* out, int ostride,
                        int ocol, hipStream_t st);
 // Exit layers l_k and the layer count L, for the expected depth sum_k p_k l_k / L.

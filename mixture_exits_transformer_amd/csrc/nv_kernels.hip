@@ -860,6 +860,44 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
                 Cs[(wm * WR + i * 16 + 4 * (lane >> 4) + e) * CLD + wn * WN + t * 16 + (lane & 15)] = acc[i][t][e];
     __syncthreads();
     const int rows = min(BM, a.R - m0);
+    if constexpr (HEAD != 0) {
+        if (a.xent_part) {
+            // fused cross-entropy: TPR threads per row (adjacent lanes) reduce each 64-column
+            // group of the row to (max, sum of exp(z - max)); reading column q + TPR k of
+            // rows 132 floats apart, the 16 rows x 4 lanes of a wave cover every bank once
+            constexpr int TPR = NTH / BM;
+            static_assert(TPR >= 1 && TPR <= 64 && (TPR & (TPR - 1)) == 0 && 64 % TPR == 0, "threads per row");
+            const int r = tid / TPR, q = tid % TPR;
+            const bool live = r < rows;
+            const int ng = a.N / 64;
+#pragma unroll
+            for (int h = 0; h < BN / 64; ++h) {
+                const float* cr = &Cs[r * CLD + 64 * h];
+                float mx = -INFINITY;
+                if (live) {
+#pragma unroll
+                    for (int c = q; c < 64; c += TPR) mx = fmaxf(mx, cr[c]);
+                }
+#pragma unroll
+                for (int off = 1; off < TPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                float sm = 0.f;
+                if (live) {
+#pragma unroll
+                    for (int c = q; c < 64; c += TPR) sm += expf(cr[c] - mx);
+                }
+#pragma unroll
+                for (int off = 1; off < TPR; off <<= 1) sm += __shfl_xor(sm, off, 64);
+                if (live && q == 0)
+                    *(float2*)&a.xent_part[2 * ((int64_t)(m0 + r) * ng + n0 / 64 + h)] = make_float2(mx, sm);
+            }
+            if (live && q == 0) {
+                const int tc = a.xent_targets[m0 + r] - n0;
+                if (tc >= 0 && tc < BN) a.xent_tgt[m0 + r] = Cs[r * CLD + tc];
+            }
+            stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
+            return;
+        }
+    }
     for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
         const int r = idx / (BN / 2), c = 2 * (idx - r * (BN / 2));
         const float2 v = *(const float2*)&Cs[r * CLD + c];
@@ -1222,6 +1260,9 @@ hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.R <= 0) return hipSuccess;
+    // the fused cross-entropy exists only in the long-chunk head product
+    if (a.xent_part && (!a.head || !a.xent_tgt || !a.xent_targets || !gemm_uses_bf16_rows(a)))
+        return hipErrorInvalidValue;
     const int epc = a.wbf16 ? 8 : 4;
     GemmArgs b = a;
     b.stamp = t_stamp;
@@ -2359,6 +2400,35 @@ __global__ __launch_bounds__(1024) void k_xent(const float* logits, int64_t ld, 
         for (int w = 0; w < nw; ++w) tot += ssum[w];
         out[(int64_t)i * ostride + ocol] = (double)zt - (double)mx - log(tot);
     }
+}
+
+// One wave per row: lane l folds groups l, l + 64, ... (the maximum first, then
+// s_g exp(m_g - M) in float64), and the wave adds the lanes in a fixed tree order.
+__global__ __launch_bounds__(256) void k_xent_merge(const float* part, const float* tgt, int n, int ngroups,
+                                                    double* out, int ostride, int ocol) {
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= n) return;
+    const float2* p = (const float2*)part + (int64_t)i * ngroups;
+    float mx = -INFINITY;
+    for (int gi = lane; gi < ngroups; gi += 64) mx = fmaxf(mx, p[gi].x);
+    mx = wave_max(mx);
+    double acc = 0.0;
+    for (int gi = lane; gi < ngroups; gi += 64) {
+        const float2 v = p[gi];
+        acc += (double)v.y * exp((double)v.x - (double)mx);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) out[(int64_t)i * ostride + ocol] = (double)tgt[i] - (double)mx - log(acc);
+}
+
+hipError_t launch_xent_merge(const float* part, const float* tgt, int n, int ngroups, double* out, int ostride,
+                             int ocol, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    if (ngroups <= 0) return hipErrorInvalidValue;
+    NV_LAUNCH(k_xent_merge, dim3((n + 3) / 4), dim3(256), 0, st, part, tgt, n, ngroups, out, ostride, ocol);
+    return hipGetLastError();
 }
 
 hipError_t launch_xent(const float* logits, int64_t ld, int n, int V, const int* targets, double* out, int ostride,

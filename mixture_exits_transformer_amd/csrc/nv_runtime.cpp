@@ -194,7 +194,8 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.loss_ch = (int)std::min<size_t>(lch, rmax);
     p.loss = align_up((size_t)p.loss_ch * V * 4) + 4 * align_up((size_t)max_ctx * 32) + align_up(64) +
              2 * align_up((size_t)max_ctx * 4) + align_up((size_t)max_ctx * sizeof(RowInfo)) +
-             align_up((size_t)p.loss_ch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
+             align_up((size_t)p.loss_ch * (c.router_dim > 0 ? c.router_dim : 1) * 8) +
+             align_up((size_t)p.loss_ch * ((V + 63) / 64) * 8) + align_up((size_t)p.loss_ch * 4);
     p.total = p.abf + p.loss + p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head +
               p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
               p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
@@ -238,6 +239,8 @@ struct nv_model {
     int *loss_tgt = nullptr, *loss_ids = nullptr;       // [max_ctx] target tokens, row ids 0..n-1
     RowInfo* loss_rows = nullptr;   // [max_ctx]
     double* loss_hid = nullptr;     // [loss_ch][router_dim]
+    float* loss_xpart = nullptr;    // [loss_ch][V/64][2] fused cross-entropy partials
+    float* loss_xtgt = nullptr;     // [loss_ch] target logits
     // chunks of at least this many rows use the matrix cores: at 5-8 rows the vector-ALU
     // GEMV holds 5-8 rows of activations per lane and moves about 1 TB/s, the matrix-core
     // path 1.5-1.7 TB/s (batch-16 decode +7 %)
@@ -437,6 +440,8 @@ double gemm_bytes(const nv_model* m, const GemmArgs& g) {
     const double out_rw = g.epi == EPI_RESID ? 2.0 : 1.0;
     const double in_es = gemm_uses_bf16_rows(g) ? 2.0 : 4.0;   // the product reads bf16 rows
     const double out_es = g.out_bf16 ? 2.0 : 4.0;
+    if (g.xent_part)   // fused cross-entropy: per-row group partials and the target logit
+        return (double)g.N * g.K * es + (double)g.R * g.K * in_es + (double)g.R * ((g.N / 64) * 8.0 + 8.0);
     return (double)g.N * g.K * es + (double)g.R * g.K * in_es + (double)g.R * nout * out_es * out_rw;
 }
 
@@ -1146,6 +1151,8 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->loss_ids = (int*)m->take((size_t)max_ctx * 4);
     m->loss_rows = (RowInfo*)m->take((size_t)max_ctx * sizeof(RowInfo));
     m->loss_hid = (double*)m->take((size_t)P.loss_ch * (m->cfg.router_dim > 0 ? m->cfg.router_dim : 1) * 8);
+    m->loss_xpart = (float*)m->take((size_t)P.loss_ch * ((m->V + 63) / 64) * 8);
+    m->loss_xtgt = (float*)m->take((size_t)P.loss_ch * 4);
     m->seg_base = m->take(P.seg);
     if (m->arena_off > P.total) return fail(m, NV_ECAPACITY, "internal: arena plan too small");
 
@@ -1815,6 +1822,21 @@ static nv_status loss_exit(nv_model* m, int sg, int o, int k) {
     g.out = m->loss_logits;
     g.ldo = m->V;
     g.head = 1;
+    // on the long-chunk path the head product reduces its logits to per-row partials in
+    // its epilogue (the logits never reach memory); elsewhere they are stored and k_xent
+    // reads them back
+    if (gemm_uses_bf16_rows(g)) {
+        g.out = nullptr;
+        g.xent_part = m->loss_xpart;
+        g.xent_tgt = m->loss_xtgt;
+        g.xent_targets = m->loss_tgt + o;
+        NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, g));
+        NV_TRY(timed(m, NV_TIME_OTHER, (double)k * (m->V / 64) * 8, [&] {
+            return launch_xent_merge(m->loss_xpart, m->loss_xtgt, k, m->V / 64, m->loss_lp + (int64_t)o * 4, 4, sg,
+                                     m->st);
+        }, "nv::k_xent_merge"));
+        return NV_OK;
+    }
     NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, g));
     NV_TRY(timed(m, NV_TIME_OTHER, (double)k * m->V * 4, [&] {
         return launch_xent(m->loss_logits, m->V, k, m->V, m->loss_tgt + o, m->loss_lp + (int64_t)o * 4, 4, sg, m->st);
