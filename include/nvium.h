@@ -75,6 +75,13 @@ size_t nv_mem_required(const char *weights_path, int32_t max_batch, int32_t max_
  *                 the caller and kept alive until nv_free, or NULL to let the
  *                 library allocate (hipMalloc).
  *   hip_stream:   a hipStream_t to issue all work on, or NULL for the null stream.
+ * Environment, read here (and, for the sizes, by nv_mem_required; set it the
+ * same way for both calls):
+ *   NVIUM_MFMA_MIN_ROWS  rows from which products use the matrix cores (default 5;
+ *                        0: never), for tests of the vector-ALU paths;
+ *   NVIUM_SEGMENT=1      one-row decode segments in the persistent segment kernel;
+ *   NVIUM_LOSS_ROWS      rows per head pass of nv_mixture_loss (default: as many as
+ *                        a 256 MiB logits workspace holds, at least 256).
  * Errors: NV_EINVAL (NULL path/out, sizes < 1), NV_EIO (file), NV_ECAPACITY
  * (arena too small), NV_EDEVICE. */
 nv_status nv_load(const char *weights_path, int32_t max_batch, int32_t max_ctx,
