@@ -8,6 +8,7 @@
 #include "nv_device.h"
 
 #include <hip/hip_ext.h>
+#include <limits.h>
 #include <math.h>
 #include <stdio.h>
 
@@ -1540,14 +1541,14 @@ __global__ __launch_bounds__(256) void k_attn(const AttnItem* items, const RowIn
 
 // ------------------------------------------------------------------------------------------
 // Chunked causal attention on the matrix cores (bf16 KV cache), for launch groups of many
-// rows.  An item is up to 64 consecutive rows of one sequence, one head and one key range;
-// wave w takes rows 16w..16w+15.  Per 64-key tile (double-buffered in LDS, keys as rows,
-// values transposed) the wave forms the transposed scores S^T = K Q^T with
+// rows.  An item is up to 16 NWA consecutive rows of one sequence, one head and one key
+// range; wave w takes rows 16w..16w+15.  Per 64-key tile (K and V double-buffered in LDS,
+// both with keys as rows) the wave forms the transposed scores S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16: lane l then holds the scores of query l%16 for keys
 // 16t + 4(l/16) + i (t = 0..3, i = 0..3).  That is, with keys permuted inside each
 // 32-key step, the B operand of O^T = V^T P^T, so the probabilities go from the
-// accumulators to the second product without leaving the registers; V^T is read with the
-// same key permutation.  Every value a lane holds belongs to its one query, so the online
+// accumulators to the second product without leaving the registers; the V^T operand is
+// read from the row-major V tile by transposing LDS reads, with the same key permutation.  Every value a lane holds belongs to its one query, so the online
 // softmax rescales a lane's accumulators by one factor; the row max crosses the four lane
 // groups of a query once per tile, the row sum only at the end.
 // Outputs: the normalised row (single split) or the (max, sum, unnormalised output)
