@@ -141,6 +141,25 @@ def test_loss_tiny_bf16_long(lib, weights_dir):
     _compare(got, pp, want, 2e-2, 2e-1, 2e-2, "tiny bf16 4500 tokens")
 
 
+def test_loss_tiny_bf16_mixed_passes(lib, weights_dir, monkeypatch):
+    """Head passes of 280 and 19 rows: the first runs the long-chunk head product with the
+    cross-entropy fused into its epilogue, the second (below that product's 33-row
+    minimum) stores its logits for k_xent.  Both against the oracle, as the other bf16
+    cases."""
+    monkeypatch.setenv("NVIUM_LOSS_ROWS", "280")   # read by nv_load
+    path = cached_weights(BF16_TINY, weights_dir)
+    M = om.OracleModel(path)
+    rng = np.random.default_rng(2800)
+    tokens = rng.integers(0, M.V, size=300)
+    want = om.mixture_loss(M, tokens, 0.25)
+    h = lib.nv_load(path, 1, 300)
+    try:
+        got, pp = lib.nv_mixture_loss(h, 0, tokens, 0.25, per_pos=True)
+    finally:
+        lib.nv_free(h)
+    _compare(got, pp, want, 2e-2, 2e-1, 2e-2, "tiny bf16 passes 280 + 19")
+
+
 def test_loss_1p5b_bf16(lib, weights_dir):
     """Expected values from tests/golden/loss_1p5b_a128.json (written by
     tests/golden/make_loss_1p5b.py, which runs the oracle; about a minute on the CPU)."""
