@@ -106,6 +106,12 @@ hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st);
 // Decode-sized row blocks (<= ATTN_DEC_ROWS rows): each item is one split of one
 // (row block, head); split partials are merged by launch_attn_combine.
 constexpr int ATTN_DEC_ROWS = 8;
+// Decode groups whose row blocks reach this many rows run on the matrix-core attention
+// (one wave per item); one- to three-row blocks stay on the vector-ALU decode kernel.
+// At an 8K context a 4- to 8-row block costs 24-41 us per layer there, about 30 on the
+// matrix cores; at one row the vector kernel is as fast.
+constexpr int ATTN_DEC_MFMA_ROWS = 4;
+static_assert(ATTN_DEC_ROWS <= 16, "a decode row block fits one 16-row wave of the matrix-core attention");
 // key groups per wave: a split covers at most 4 waves x (512 / head_dim) keys x 8 groups
 // (128 keys at head_dim 128; 8 groups measured better than 4 at batch 1, 16 and an 8K
 // context: fewer, longer splits with more loads in flight per wave)
@@ -121,6 +127,11 @@ bool attn_mfma_ok(const LayerDims& D);
 constexpr int ATTN_MFMA_ROWS = 128;
 hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* rows, const float* q, const void* kv,
                             int layer, const LayerDims& D, float* part_ml, float* part_o, float* out, hipStream_t st);
+// Decode groups on the matrix cores: one wave per item (at most 16 rows), used for groups
+// whose row blocks reach ATTN_DEC_MFMA_ROWS rows.
+hipError_t launch_attn_mfma16(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
+                              const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
+                              float* out, hipStream_t st);
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
                        const void* kv, int layer, const LayerDims& D, float* part_ml,
                        float* part_o, float* out, hipStream_t st);

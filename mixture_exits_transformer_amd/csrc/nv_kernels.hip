@@ -1779,6 +1779,27 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
     return hipGetLastError();
 }
 
+// The same kernel with one wave per block, for decode groups (items of up to 16 rows: the
+// decode row blocks, with their key splits).  Its cost barely grows with the rows an item
+// holds, where the vector-ALU decode kernel repeats its dot products per row.
+hipError_t launch_attn_mfma16(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
+                              const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
+                              float* out, hipStream_t st) {
+    if (n_items <= 0) return hipSuccess;
+    if (!attn_mfma_ok(D)) return hipErrorInvalidValue;
+    const uint16_t* k16 = (const uint16_t*)kv;
+    if (D.hd == 128)
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128, 1>), dim3(n_items), dim3(64), 0, st, items, rows, q, k16, layer, D,
+                  part_ml, part_o, out, t_stamp);
+    else if (D.hd == 64)
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64, 1>), dim3(n_items), dim3(64), 0, st, items, rows, q, k16, layer, D,
+                  part_ml, part_o, out, t_stamp);
+    else
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32, 1>), dim3(n_items), dim3(64), 0, st, items, rows, q, k16, layer, D,
+                  part_ml, part_o, out, t_stamp);
+    return hipGetLastError();
+}
+
 // Decode-sized groups (few (row, head) pairs, possibly many splits): one block of 512
 // threads per pair.  The split maxima and the weights exp(m_s - M) are formed by all
 // threads together (block reductions, weights kept in LDS); each value dim's weighted sum

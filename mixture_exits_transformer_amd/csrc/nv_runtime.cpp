@@ -701,10 +701,16 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             });
         };
         if (t.dec) {
-            NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
-                return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
-                                       m->part_o, m->attn_o, m->st);
-            }, "nv::k_attn_dec"));
+            if (t.max_rows >= ATTN_DEC_MFMA_ROWS && attn_mfma_ok(D))
+                NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
+                    return launch_attn_mfma16(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
+                                              m->part_o, m->attn_o, m->st);
+                }, "nv::k_attn_mfma (decode items)"));
+            else
+                NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
+                    return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
+                                           m->part_o, m->attn_o, m->st);
+                }, "nv::k_attn_dec"));
             // one row: the O projection merges the splits itself (no combine pass)
             if (t.any_split && !fuse_merge(m, t))
                 NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
