@@ -1583,8 +1583,11 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     constexpr int NTH = 64 * NWA;
     constexpr int NCH = AM_KT * CPR;              // 16-byte chunks per tile, for K and for V
     constexpr int CPT = (NCH + NTH - 1) / NTH;    // per thread (threads past NCH load none)
-    __shared__ __align__(16) uint16_t Ks[2][AM_KT * KLD];
-    __shared__ __align__(16) uint16_t Vs[2][AM_KT * VLD];
+    // one wave per block (decode items of one or two tiles): a single buffer, so that four
+    // blocks share a CU; otherwise the next tile is staged while the current one is used
+    constexpr int NB = NWA == 1 ? 1 : 2;
+    __shared__ __align__(16) uint16_t Ks[NB][AM_KT * KLD];
+    __shared__ __align__(16) uint16_t Vs[NB][AM_KT * VLD];
     const AttnItem it = items[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qn = lane & 15, g = lane >> 4;
@@ -1655,7 +1658,7 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     lstore(0);
     __syncthreads();
     for (int tt = 0; tt < ntile; ++tt) {
-        const int buf = tt & 1, t0 = it.lo + tt * AM_KT;
+        const int buf = NB == 1 ? 0 : tt & 1, t0 = it.lo + tt * AM_KT;
         if (tt + 1 < ntile) gload(t0 + AM_KT);
         // S^T for this tile: 4 key tiles of 16
         f32x4_t sc[4];
@@ -1733,7 +1736,10 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
                 o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pf, o[t], 0, 0, 0);
             }
         }
-        if (tt + 1 < ntile) lstore(buf ^ 1);
+        if (tt + 1 < ntile) {
+            if constexpr (NB == 1) __syncthreads();   // the tile's reads are done before it is overwritten
+            lstore(NB == 1 ? 0 : buf ^ 1);
+        }
         __syncthreads();
     }
     lsum += __shfl_xor(lsum, 16, 64);
