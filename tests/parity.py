@@ -8,7 +8,14 @@ step is then compared with the oracle's.
 Token and exit rule: they must be equal, except that a difference is accepted when
 the draw lies within `band` of the oracle's decision boundary (|u_k - w_k| for a
 walked gate, distance of u_4 to the oracle CDF interval of either token).  Such
-draws are counted and reported.
+draws are counted and reported.  On bf16 paths a difference is also accepted when the
+draw lies between the oracle's and the device's gate value, or inside the CDF shift
+that the device's tolerance-checked logits imply; `finish` bounds how often that may
+happen and how far the device's gate values may sit from the oracle's.
+
+Tensor comparisons are made per row (one position, or one (position, head) of the KV
+cache), so that an error confined to a few decoded or deferred rows is not diluted by
+hundreds of prompt rows.
 """
 from __future__ import annotations
 
@@ -20,12 +27,28 @@ import numpy as np
 from oracle import model as om
 
 BAND = 1e-5
+# bf16 paths: largest accepted |w_device - w_oracle| of a walked gate.  The 1.5B model's
+# residual stream has norm ~85-180 after a segment, so bf16 rounding in 12-48 layers moves
+# g . h by a few 1e-3 (measured up to 5.9e-3).
+GATE_BOUND_BF16 = 1e-2
 
 
 def rel(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def row_rel(a, b, width: int) -> np.ndarray:
+    """Relative error of every row of `width` values: ||a_i - b_i|| / ||b_i||."""
+    a = np.asarray(a, np.float64).reshape(-1, width)
+    b = np.asarray(b, np.float64).reshape(-1, width)
+    return np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-300)
+
+
+def row_rel_max(a, b, width: int) -> float:
+    r = row_rel(a, b, width)
+    return float(r.max()) if r.size else 0.0
 
 
 @dataclass
@@ -47,6 +70,18 @@ class StepCheck:
                 f"within-gate-shift {self.gate_explained} "
                 f"max logit rel {self.max_logit_rel:.2e} max gate abs {self.max_gate_abs:.2e} "
                 f"max cdf shift {self.max_cdf_shift:.2e}")
+
+    def finish(self, logit_tol: float, gate_bound: float = GATE_BOUND_BF16, max_logit_explained: int = 1,
+               max_gate_explained: int = 1) -> None:
+        """Assert the run's verdict: no unexplained mismatch, logits within `logit_tol`,
+        walked gates within `gate_bound` of the oracle's, and at most the given number of
+        draws accepted only through the widened (bf16) bands."""
+        print(self.summary())
+        assert not self.unexplained, self.unexplained
+        assert self.max_logit_rel < logit_tol, self.max_logit_rel
+        assert self.max_gate_abs < gate_bound, self.max_gate_abs
+        assert self.logit_explained <= max_logit_explained, self.logit_explained
+        assert self.gate_explained <= max_gate_explained, self.gate_explained
 
 
 def cdf_shift(g_logits, pi_oracle) -> float:
@@ -76,7 +111,7 @@ def check_step(t: int, o: om.StepOut, g_tok: int, g_exit: int, g_logits, g_w, re
         wshift = abs(float(g_w[k]) - o.w[k]) if (logit_band and np.isfinite(g_w[k])) else 0.0
         if dist < band:
             res.near_boundary += 1
-        elif dist <= wshift:                     # the draw lies between the two gate values
+        elif dist <= wshift <= GATE_BOUND_BF16:  # the draw lies between the two gate values
             res.gate_explained += 1
         else:
             res.unexplained.append(f"step {t}: exit device {g_exit} oracle {o.exit} (gate distance {dist:.3g})")
@@ -101,6 +136,48 @@ def check_step(t: int, o: om.StepOut, g_tok: int, g_exit: int, g_logits, g_w, re
         res.logit_explained += 1
     else:
         res.unexplained.append(f"step {t}: token device {g_tok} oracle {want} (cdf distance {min(d1, d2):.3g})")
+
+
+def kv_rows_worst(lib, h, seq: int, st, layers, positions) -> float:
+    """Largest per-(position, head) relative error of K and V over `layers` at the given
+    positions (device after a flush against the oracle's cache `st`)."""
+    positions = np.asarray(sorted(positions), dtype=np.int64)
+    if positions.size == 0:
+        return 0.0
+    p0, p1 = int(positions[0]), int(positions[-1]) + 1
+    worst = 0.0
+    for l in layers:
+        k, v = lib.nv_debug_kv(h, seq, l, p0, p1 - p0)
+        sel = positions - p0
+        hd = k.shape[-1]
+        worst = max(worst, row_rel_max(k[sel], st.kv.K[l, positions], hd),
+                    row_rel_max(v[sel], st.kv.V[l, positions], hd))
+    return worst
+
+
+def decoded_kv_report(lib, h, seq: int, st, layers, pos0: int, exits, seg_layers: int) -> dict:
+    """Per-row KV errors at the decoded positions pos0, pos0+1, ..., split by how each
+    (position, layer) was computed: 'direct' when the position's own token reached the
+    layer, 'deferred' when it ran later in a catch-up chunk or at the flush; plus the
+    prompt rows before pos0.  Returns the worst value of each group."""
+    out = {"direct": 0.0, "deferred": 0.0, "prompt": 0.0}
+    for l in layers:
+        s = l // seg_layers
+        direct = [pos0 + t for t, e in enumerate(exits) if s < e]
+        deferred = [pos0 + t for t, e in enumerate(exits) if s >= e]
+        out["direct"] = max(out["direct"], kv_rows_worst(lib, h, seq, st, [l], direct))
+        out["deferred"] = max(out["deferred"], kv_rows_worst(lib, h, seq, st, [l], deferred))
+        out["prompt"] = max(out["prompt"], kv_rows_worst(lib, h, seq, st, [l], range(pos0)))
+    return out
+
+
+def hidden_rows_worst(lib, h, seq: int, outs, pos0: int) -> float:
+    """After a flush every decoded position has completed the last layer: its hidden row
+    must equal the oracle's state after the last layer (per-row relative error)."""
+    n = len(outs)
+    got = lib.nv_debug_hidden(h, seq, pos0, n)
+    want = np.stack([o.h[-1] for o in outs])
+    return row_rel_max(got, want, want.shape[-1])
 
 
 def run_forced(h, lib, outs: List[om.StepOut], seq_index: int = 0, batch: int = 1, other_inputs=None):

@@ -2,9 +2,13 @@
 configuration the benchmark uses, on sampled outputs the oracle computes one by one:
 a few decode steps after the full prompt, then KV of sampled layers after a flush.
 
-Rule (see tests/parity.py): logits and KV within 2e-2 relative; exits equal unless a
-draw is within 1e-5 of a gate; tokens equal unless the draw is within 1e-5 of an
-oracle CDF boundary or within the CDF shift implied by the checked logits."""
+Rule (see tests/parity.py): logits and every KV row (one position and head) within 2e-2
+relative, reported separately for prompt rows, decoded rows computed when their token
+passed, and deferred rows computed later in catch-up chunks or at the flush; hidden rows
+of the decoded positions within 2e-2; exits equal unless a draw is within 1e-5 of a gate
+or between the device's and the oracle's gate value (gates within 1e-2 of the oracle's,
+at most one such draw); tokens equal unless the draw is within 1e-5 of an oracle CDF
+boundary or (at most once) within the CDF shift implied by the checked logits."""
 import math
 from dataclasses import replace
 
@@ -14,7 +18,7 @@ import pytest
 from oracle import model as om
 from synth import cached_weights, prompts, uniforms, workload
 from synth.configs import BIAS_ALL_LAST
-from tests.parity import StepCheck, check_step, rel, run_forced
+from tests.parity import StepCheck, check_step, decoded_kv_report, hidden_rows_worst, rel, run_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -39,14 +43,6 @@ def model_a(weights_dir):
     return path, om.OracleModel(path)
 
 
-def _kv_worst(lib, h, seq, st, n, layers):
-    worst = 0.0
-    for l in layers:
-        k, v = lib.nv_debug_kv(h, seq, l, 0, n)
-        worst = max(worst, rel(k, st.kv.K[l, :n]), rel(v, st.kv.V[l, :n]))
-    return worst
-
-
 def test_workload_A_sampled(lib, model_a):
     path, M = model_a
     w = workload("A")
@@ -65,15 +61,16 @@ def test_workload_A_sampled(lib, model_a):
         res = StepCheck()
         for t, (o, (tok, ex, lg, gw)) in enumerate(zip(outs, recs)):
             check_step(t, o, tok, ex, lg, gw, res, logit_band=True)
-        print("\nA:", res.summary())
-        assert [r[1] for r in recs][4:] == [1, 1, 1, 4]
-        assert not res.unexplained, res.unexplained
-        assert res.max_logit_rel < TOL
+        print("\nA:", end=" ")
+        exits = [r[1] for r in recs]
+        assert exits[4:] == [1, 1, 1, 4]
+        res.finish(TOL)
         lib.nv_flush(h)
-        n = len(prompt) - 1 + len(U)
-        worst = _kv_worst(lib, h, 0, st, n, SAMPLED_LAYERS)
-        print("A KV worst rel", worst)
-        assert worst < TOL
+        P = len(prompt) - 1
+        rep = decoded_kv_report(lib, h, 0, st, SAMPLED_LAYERS, P, exits, w.model.seg_layers)
+        hid = hidden_rows_worst(lib, h, 0, outs, P)
+        print("A per-row KV worst", {k: f"{v:.2e}" for k, v in rep.items()}, f"hidden rows {hid:.2e}")
+        assert max(rep.values()) < TOL and hid < TOL
     finally:
         lib.nv_free(h)
 
@@ -95,12 +92,15 @@ def test_workload_B_exit4_forced(lib, weights_dir, model_a):
         for t, (o, (tok, ex, lg, gw)) in enumerate(zip(outs, recs)):
             assert ex == 4 and o.p == [0.0, 0.0, 0.0, 1.0]
             check_step(t, o, tok, ex, lg, gw, res, logit_band=True)
-        print("\nB:", res.summary())
-        assert not res.unexplained, res.unexplained
-        assert res.max_logit_rel < TOL
+        print("\nB:", end=" ")
+        res.finish(TOL)
         n, f = lib.nv_debug_frontiers(h, 0)
         assert list(f) == [n] * 4
-        assert _kv_worst(lib, h, 0, st, n, SAMPLED_LAYERS) < TOL
+        P = len(prompt) - 1
+        rep = decoded_kv_report(lib, h, 0, st, SAMPLED_LAYERS, P, [4] * len(U), w.model.seg_layers)
+        hid = hidden_rows_worst(lib, h, 0, outs, P)
+        print("B per-row KV worst", {k: f"{v:.2e}" for k, v in rep.items()}, f"hidden rows {hid:.2e}")
+        assert max(rep.values()) < TOL and hid < TOL
     finally:
         lib.nv_free(h)
         del M
@@ -131,9 +131,8 @@ def test_workload_C_batch16_sampled(lib, model_a):
             all_exits.append(ex.copy())
             check_step(t, o, int(tok[j]), int(ex[j]), lib.nv_debug_logits(h, j), lib.nv_debug_gates(h, j), res,
                        logit_band=True)
-        print("\nC seq", j, ":", res.summary())
-        assert not res.unexplained, res.unexplained
-        assert res.max_logit_rel < TOL
+        print("\nC seq", j, ":", end=" ")
+        res.finish(TOL)
         # frontiers follow each sequence's exits
         E = np.stack(all_exits)                       # [steps][batch]
         for i, p in enumerate(ps):
@@ -143,9 +142,10 @@ def test_workload_C_batch16_sampled(lib, model_a):
                 reached = [t for t in range(steps) if E[t, i] > s]
                 assert f[s] == (len(p) - 1 + reached[-1] + 1 if reached else len(p) - 1)
         lib.nv_flush(h)
-        n = len(ps[j]) - 1 + steps
-        worst = _kv_worst(lib, h, j, st, n, SAMPLED_LAYERS)
-        print("C KV worst rel", worst)
-        assert worst < TOL
+        P = len(ps[j]) - 1
+        rep = decoded_kv_report(lib, h, j, st, SAMPLED_LAYERS, P, [int(e[j]) for e in E], w.model.seg_layers)
+        hid = hidden_rows_worst(lib, h, j, outs, P)
+        print("C per-row KV worst", {k: f"{v:.2e}" for k, v in rep.items()}, f"hidden rows {hid:.2e}")
+        assert max(rep.values()) < TOL and hid < TOL
     finally:
         lib.nv_free(h)

@@ -10,7 +10,7 @@ import pytest
 
 from oracle import model as om
 from synth import cached_weights, tiny_variant
-from tests.parity import StepCheck, check_step, rel, run_forced
+from tests.parity import StepCheck, check_step, decoded_kv_report, hidden_rows_worst, rel, run_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -57,17 +57,14 @@ def _run_case(lib, path, M, prompt, pattern, rng, tag):
             if pattern[t]:
                 assert ex == pattern[t]
             check_step(t, o, tok, ex, lg, gw, res, logit_band=True)
-        print(f"\n{tag}:", res.summary())
-        assert not res.unexplained, res.unexplained
-        assert res.max_logit_rel < TOL
+        print(f"\n{tag}:", end=" ")
+        res.finish(TOL)
         lib.nv_flush(h)
-        n = len(prompt) - 1 + len(pattern)
-        worst = 0.0
-        for l in range(M.L):
-            k, v = lib.nv_debug_kv(h, 0, l, 0, n)
-            worst = max(worst, rel(k, st.kv.K[l, :n]), rel(v, st.kv.V[l, :n]))
-        print(f"{tag} KV worst rel", worst)
-        assert worst < TOL
+        P = len(prompt) - 1
+        rep = decoded_kv_report(lib, h, 0, st, range(M.L), P, [r[1] for r in recs], M.L // 4)
+        hid = hidden_rows_worst(lib, h, 0, outs, P)
+        print(f"{tag} per-row KV worst", {k: f"{v:.2e}" for k, v in rep.items()}, f"hidden rows {hid:.2e}")
+        assert max(rep.values()) < TOL and hid < TOL
     finally:
         lib.nv_free(h)
 
