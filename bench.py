@@ -34,6 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# exit masses the workloads state (the gate biases are calibrated to give them)
+STATED_MASS = {"A": (0.4, 0.25, 0.2, 0.15), "C": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1),
+               "E": (0.4, 0.25, 0.2, 0.15)}
 MFMA_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("mixture_exits_transformer_amd/csrc/nv_kernels.hip",
                   "mixture_exits_transformer_amd/csrc/nv_segment.hip",
@@ -133,6 +136,8 @@ def cpu_baseline(wl, path, prompt, U, budget_s):
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "precision": "float64 (the oracle as written: sequential, full depth, all exits' heads skipped but "
+                         "the stopping one; slower than a float32 CPU implementation would be)",
             "sample": f"{n} decode steps of workload {wl.name} (positions {len(prompt) - 1}.."
                       f"{len(prompt) - 2 + n}) after an untimed {len(prompt) - 1}-token prefill, "
                       f"{dt:.1f} s"}
@@ -425,8 +430,10 @@ def main():
         "vs_baseline": None,
         "dtype": wl.model.wdtype,
         "data": "synthetic: uniform-random token ids, seeded uniforms, random-init N(0,0.02) weights",
-        "config": {"workload": f"{wl.name}: {wl.note}", "batch": wl.batch, "prompt": len(prompt),
-                   "decode_steps": steps},
+        "config": {"workload": f"{wl.name}: {wl.note}" + (
+                       f"; timed: decode steps 1-{steps} of {wl.decode_steps} (positions {len(prompt) - 1}-"
+                       f"{len(prompt) - 2 + steps})" if steps < wl.decode_steps else ""),
+                   "batch": wl.batch, "prompt": len(prompt), "decode_steps": steps},
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -443,6 +450,8 @@ def main():
         "exit4_forced_tokens_per_s": round(base, 2) if base else None,
         "speedup_vs_exit4": round(tok_s / base - 1.0, 4) if base else None,
         "exit_histogram": [int(x) for x in hist],
+        "exit_mass_stated": list(STATED_MASS.get(wl.name, ())) or None,
+        "exit_mass_realised": [round(float(x) / steps, 4) for x in hist],
         "mean_segments_per_token": round(float(np.mean(exits)), 4),
         # the step's cost per segment a token runs: tokens/s moves with the realised exit mix
         # (which last-bit rounding changes on random-init weights), this figure does not

@@ -1,0 +1,90 @@
+"""Gate biases that realise the stated exit masses on the 1.5B model (calls only oracle/).
+
+With random-init weights the residual stream after a segment has norm ~85-180, so the
+linear term g_k . h of a gate (g_k ~ N(0, 0.02^2)) has a standard deviation near 2 and
+sigmoid(b_k) alone does not give the stated marginal exit masses.  The marginal mass of
+exit k is the mean over tokens of p_k = w_k prod_{j<k} (1 - w_j), with w_k = sigmoid(g_k .
+h^(l_k) + b_k) (gist.science summary, section 2 "Methodik", part "Architektur": equation
+for p_k).  This script runs the oracle's float64 forward over a seeded calibration prompt
+(512 uniform-random tokens, numpy default_rng(3)), keeps z_k = g_k . h^(l_k) at positions
+64..510, and solves, exit by exit, for the b_k whose sample mean of p_k equals the stated
+mass (p_k is increasing in b_k when the earlier biases are fixed; bisection in float64).
+
+    python tests/golden/make_gate_bias.py       # writes tests/golden/gate_bias_1p5b.json
+"""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+from oracle import model as om                       # noqa: E402
+from synth import M15B, cached_weights              # noqa: E402
+
+MASSES = {"A": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1)}
+PROMPT_SEED, PROMPT_LEN, FIRST_POS = 3, 512, 64
+
+
+def sig(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def solve_biases(z: np.ndarray, masses) -> list:
+    """z: [n][3] linear terms; the biases b_1..b_3 whose sample-mean exit masses equal
+    masses[0..2] (the last exit takes the rest)."""
+    rest = np.ones(z.shape[0])
+    out = []
+    for k in range(3):
+        target = masses[k]
+        lo, hi = -60.0, 60.0
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if float(np.mean(rest * sig(z[:, k] + mid))) < target:
+                lo = mid
+            else:
+                hi = mid
+        b = 0.5 * (lo + hi)
+        out.append(b)
+        rest = rest * (1.0 - sig(z[:, k] + b))
+    return out
+
+
+def main():
+    path = cached_weights(M15B)
+    M = om.OracleModel(path)
+    rng = np.random.default_rng(PROMPT_SEED)
+    tokens = rng.integers(0, M.V, size=PROMPT_LEN)
+    n = PROMPT_LEN - 1
+    kv = om.KVCache(M, n)
+    pos = np.arange(n)
+    X = np.asarray(M.embed[tokens[:n]], dtype=np.float64)
+    z = np.zeros((n, 3))
+    for l in range(M.L):
+        X = om.layer_rows(M, l, X, pos, kv)
+        for k in range(3):
+            if l + 1 == M.exit_layers[k]:
+                z[:, k] = X @ M.gate_w[k]
+        print(f"layer {l + 1}/{M.L}", flush=True)
+    zs = z[FIRST_POS:]
+    res = {"source": "tests/golden/make_gate_bias.py (oracle float64 forward, 1.5B model, seed-0 weights)",
+           "prompt": f"{PROMPT_LEN} uniform-random tokens, numpy default_rng({PROMPT_SEED})",
+           "positions": [FIRST_POS, n - 1],
+           "z_std": [float(np.std(zs[:, k])) for k in range(3)],
+           "z": [[round(float(v), 9) for v in row] for row in zs]}
+    for name, m in MASSES.items():
+        b = solve_biases(zs, m)
+        res[f"bias_{name}"] = b
+        res[f"mass_{name}"] = list(m)
+        print(name, "biases", b, flush=True)
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gate_bias_1p5b.json")
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print("wrote", out)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,48 @@
+"""The calibrated gate biases of the 1.5B workloads reproduce the stated exit masses on
+the calibration sample that tests/golden/make_gate_bias.py stored (the oracle's linear
+terms z_k = g_k . h^(l_k) at 447 prompt positions): the mean over positions of the
+stick-breaking p_k (gist.science summary, section 2 "Methodik", part "Architektur":
+equation for p_k) with w_k = sigmoid(z_k + b_k) equals the stated mass.  The biases the
+workloads carry are the stored ones."""
+import json
+import os
+
+import numpy as np
+
+from synth import workload
+from synth.configs import BIAS_CAL_1P5B_40_25_20_15, BIAS_CAL_1P5B_60_20_10_10
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gate_bias_1p5b.json")
+
+
+def _masses(z, b):
+    w = 1.0 / (1.0 + np.exp(-(z + np.asarray(b)[None, :])))
+    p = np.zeros((z.shape[0], 4))
+    rest = np.ones(z.shape[0])
+    for k in range(3):
+        p[:, k] = rest * w[:, k]
+        rest = rest * (1.0 - w[:, k])
+    p[:, 3] = rest
+    return p.mean(axis=0)
+
+
+def test_calibrated_biases_give_stated_masses():
+    g = json.load(open(GOLDEN))
+    z = np.asarray(g["z"])
+    assert z.shape == (447, 3)
+    for name, b_cfg in (("A", BIAS_CAL_1P5B_40_25_20_15), ("D", BIAS_CAL_1P5B_60_20_10_10)):
+        assert np.allclose(g[f"bias_{name}"], b_cfg, rtol=0, atol=1e-12)
+        m = _masses(z, b_cfg)
+        assert np.allclose(m, g[f"mass_{name}"], rtol=0, atol=1e-6), (name, m)
+        # the header stores the biases as float32: the masses move by far less than 1e-3
+        m32 = _masses(z, np.asarray(b_cfg, np.float32).astype(np.float64))
+        assert np.allclose(m32, g[f"mass_{name}"], rtol=0, atol=1e-5)
+    # without calibration (sigmoid(b) alone) the same sample misses the stated masses
+    from synth.configs import BIAS_MASS_40_25_20_15
+    assert np.max(np.abs(_masses(z, BIAS_MASS_40_25_20_15) - np.asarray(g["mass_A"]))) > 0.05
+
+
+def test_workloads_carry_the_calibrated_biases():
+    assert workload("A").model.gate_bias == BIAS_CAL_1P5B_40_25_20_15
+    assert workload("C").model.gate_bias == BIAS_CAL_1P5B_40_25_20_15
+    assert workload("D").model.gate_bias == BIAS_CAL_1P5B_60_20_10_10
