@@ -40,17 +40,23 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
     inc = ["-I", CSRC, "-I", os.path.join(ROOT, "include")]
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        out = _run([hipcc()] + HIP_FLAGS + inc + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
-        if verbose and out.strip():
-            print(out)
-        objs.append(obj)
+        jobs.append((obj, [hipcc()] + HIP_FLAGS + inc + lang + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    # the translation units are independent: compile them side by side
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        outs = list(ex.map(lambda j: _run(j[1]), jobs))
+    if verbose:
+        for out in outs:
+            if out.strip():
+                print(out)
+    objs = [j[0] for j in jobs]
     tmp = LIB + f".tmp{os.getpid()}"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)

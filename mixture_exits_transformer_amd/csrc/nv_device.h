@@ -52,6 +52,40 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Sum over all 64 lanes, every lane gets it: DPP within rows of 16, then the four row sums
+// read as scalars (no LDS round trips).
+__device__ __forceinline__ float wave_total(float v) {
+    v = group_sum<16>(v);
+    const int iv = __float_as_int(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) + __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) + __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
+}
+
+// Sum N values per lane (N a power of two, 4 <= N <= 64) over the 64 lanes of a wave with
+// gfx950's half swaps and DPP, without LDS traffic.  v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, v_permlane16_swap the odd
+// 16-lane rows of the first with the even rows of the second (layout checked on the
+// device), so one swap and one add give each half (row) the pairwise sums of half of the
+// values.  Afterwards slot j < N/4 of every lane of row r (lanes 16r..16r+15) holds the sum
+// of value index r * N/4 + j.
+template <int N>
+__device__ __forceinline__ void wave_rowsum_transpose(float (&v)[N]) {
+    static_assert((N & (N - 1)) == 0 && N >= 4 && N <= 64, "N must be a power of two in [4, 64]");
+    constexpr int H = N / 2, Q = N / 4;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + H]), false, false);
+        v[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + Q]), false, false);
+        v[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) v[i] = group_sum<16>(v[i]);
+}
+
 __device__ __forceinline__ float kv_load(const void* kv, int bf16, int64_t i) {
     if (bf16) return __uint_as_float(((uint32_t)((const uint16_t*)kv)[i]) << 16);
     return ((const float*)kv)[i];

@@ -46,9 +46,13 @@ struct GemmArgs {
     uint16_t* out_bf16;   // EPI_SWIGLU only, or null: silu(g) * u goes here as bf16 [R][ldo],
                           // rounded as launch_rows_bf16 would round it, instead of to out
     int mfma_min_rows;    // use the matrix-core path when R >= this (0: never)
-    // R == 1 only: when set, the one row of A is A + a_row0 * lda (the vector-ALU kernel
-    // then issues its loads without waiting for a_rows[0])
-    int a_row0_set, a_row0;
+    // Rows of one contiguous chunk (vector-ALU decode kernel only): when `contig` is set, row r
+    // is position pos0 + r of sequence seq0, its row of A is a_row0 + r (when a_rows is set;
+    // else r) and its row of out is o_row0 + r (when o_rows is set; else r).  The kernel then
+    // computes every address without loading the row tables, issues all its weight loads
+    // before any wait, and fetches the epilogue's inputs (RoPE table entries, residual
+    // values) right after them.
+    int contig, a_row0, o_row0, seq0, pos0;
     // EPI_QKV only.  Weight row 2p + i (i = 0, 1) of the fused QKV matrix is original
     // row part*d + h*hd + j + i*hd/2, where p = part*(d/2) + h*(hd/2) + j, part 0/1/2 = q/k/v.
     float* q_out;         // [R][d]

@@ -202,11 +202,20 @@ struct EpiCtx {
     int orow;      // output row (hidden-state row for EPI_RESID)
     int seq, pos;  // EPI_QKV: sequence and position of the row
     float c, s;    // EPI_QKV: RoPE cos / sin for this pair
+    float r0, r1;  // EPI_RESID with has_res: the residual values of columns n, n+1
+    bool has_res;
 };
 
+// E: the epilogue kind when fixed at compile time, or -1 to read a.epi (each decode product's
+// kernel then holds only its own epilogue, and no load of another kind's path can hold up
+// this one's registers).
+template <int E>
+__device__ __forceinline__ int epi_kind(const GemmArgs& a) { return E >= 0 ? E : a.epi; }
+
+template <int E = -1>
 __device__ __forceinline__ EpiCtx epi_prepare(const GemmArgs& a, int row, int n) {
     EpiCtx e{};
-    if (a.epi == EPI_QKV) {
+    if (epi_kind<E>(a) == EPI_QKV) {
         const RowInfo ri = a.a_rows[row];
         e.seq = ri.seq;
         e.pos = ri.pos;
@@ -222,10 +231,40 @@ __device__ __forceinline__ EpiCtx epi_prepare(const GemmArgs& a, int row, int n)
     return e;
 }
 
+// The same context for a contiguous chunk (GemmArgs::contig): every address is known without
+// a table load, so these loads can be issued after the weight loads; the residual values
+// of EPI_RESID are fetched here too (only this thread writes them).
+template <int E = -1>
+__device__ __forceinline__ EpiCtx epi_prefetch(const GemmArgs& a, int row, int n) {
+    EpiCtx e{};
+    const int epi = epi_kind<E>(a);
+    if (epi == EPI_QKV) {
+        e.seq = a.seq0;
+        e.pos = a.pos0 + row;
+        const int half = a.D.hd >> 1;
+        const int pp = (n >> 1) % (a.D.d >> 1);
+        const int j = pp % half;
+        const float2 cs = *(const float2*)(a.rope + ((int64_t)e.pos * half + j) * 2);
+        e.c = cs.x;
+        e.s = cs.y;
+    } else {
+        e.orow = a.o_rows ? a.o_row0 + row : row;
+        if (epi == EPI_RESID) {
+            const float2 r = *(const float2*)(a.out + (int64_t)e.orow * a.ldo + n);
+            e.r0 = r.x;
+            e.r1 = r.y;
+            e.has_res = true;
+        }
+    }
+    return e;
+}
+
+template <int E = -1>
 __device__ __forceinline__ void epi_apply(const GemmArgs& a, const EpiCtx& e, int row, int n, float v0, float v1) {
-    if (a.epi == EPI_SWIGLU) {
+    const int epi = epi_kind<E>(a);
+    if (epi == EPI_SWIGLU) {
         a.out[(int64_t)e.orow * a.ldo + (n >> 1)] = v0 / (1.0f + expf(-v0)) * v1;
-    } else if (a.epi == EPI_QKV) {
+    } else if (epi == EPI_QKV) {
         const LayerDims& D = a.D;
         const int half = D.hd >> 1;
         const int p = n >> 1;
@@ -250,12 +289,15 @@ __device__ __forceinline__ void epi_apply(const GemmArgs& a, const EpiCtx& e, in
         }
     } else {
         float* o = a.out + (int64_t)e.orow * a.ldo + n;
-        if (a.epi == EPI_STORE) {
+        if (epi == EPI_STORE) {
             o[0] = v0;
             o[1] = v1;
-        } else if (a.epi == EPI_SILU) {
+        } else if (epi == EPI_SILU) {
             o[0] = v0 / (1.0f + expf(-v0));
             o[1] = v1 / (1.0f + expf(-v1));
+        } else if (e.has_res) {
+            o[0] = e.r0 + v0;
+            o[1] = e.r1 + v1;
         } else {
             o[0] += v0;
             o[1] += v1;
@@ -942,7 +984,7 @@ bool gemm_uses_bf16_rows(const GemmArgs& a) {
 
 constexpr int KS_CPB = 8;          // output columns per block (vector-ALU kernel)
 
-template <bool WBF, int RM, int HEAD, bool COMB = false>
+template <bool WBF, int RM, int HEAD, bool COMB = false, int EPIT = -1>
 __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
     static_assert(!COMB || RM == 1, "the fused attention merge handles one row");
     constexpr int EPC = WBF ? 8 : 4;
@@ -959,11 +1001,12 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
     const bool act = ch < nch;
     const int k0 = (act ? ch : nch - 1) * EPC;
 
-    // epilogue context of the thread that will finish (row er, columns n0+ec, n0+ec+1)
+    // epilogue context of the thread that will finish (row er, columns n0+ec, n0+ec+1); for a
+    // contiguous chunk it is fetched after the weight loads (below)
     const bool ethr = threadIdx.x < KS_CPB / 2 * RM;
     const int er = threadIdx.x % RM, ec = 2 * (threadIdx.x / RM);
     EpiCtx ectx{};
-    if (ethr && er < R) ectx = epi_prepare(a, er, n0 + ec);
+    if (!a.contig && ethr && er < R) ectx = epi_prepare<EPIT>(a, er, n0 + ec);
 
     // activation chunks (rows past R repeat row R-1; their results are never written)
     float av[RM][EPC];
@@ -972,7 +1015,7 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
             const int rr = r < R ? r : R - 1;
-            const int ar = a.a_row0_set ? a.a_row0 : a.a_rows ? a.a_rows[rr].hrow : rr;
+            const int ar = !a.a_rows ? rr : a.contig ? a.a_row0 + rr : a.a_rows[rr].hrow;
             const float4* ap = (const float4*)(a.A + (int64_t)ar * a.lda + k0);
 #pragma unroll
             for (int e = 0; e < EPC / 4; ++e) {
@@ -1020,6 +1063,10 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
     uint4 w[KS_CPB];
 #pragma unroll
     for (int c = 0; c < KS_CPB; ++c) w[c] = *(const uint4*)((const char*)a.W + ((size_t)(n0 + c) * K + k0) * ESZ);
+    // every weight load is issued before anything waits on the activations
+    __builtin_amdgcn_sched_barrier(0);
+    if (a.contig && ethr && er < R) ectx = epi_prefetch<EPIT>(a, er, n0 + ec);
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (COMB) {
         if (merge) {
@@ -1086,14 +1133,16 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) acc[c * RM + r] = fmaf(wf[e], av[r][e], acc[c * RM + r]);
     }
-    // value index c*RM + r ends up in lanes whose top log2(NV) bits equal it
-    const float tot = wave_transpose_sum<NV>(acc, lane);
-    constexpr int SH = (NV == 64) ? 0 : (NV == 32) ? 1 : (NV == 16) ? 2 : (NV == 8) ? 3 : (NV == 4) ? 4 : (NV == 2) ? 5 : 6;
-    if ((lane & ((1 << SH) - 1)) == 0) red[wave][lane >> SH] = tot;
+    // value index c*RM + r: row (lane / 16) holds indices [row * NV/4, (row + 1) * NV/4)
+    wave_rowsum_transpose<NV>(acc);
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int j = 0; j < NV / 4; ++j) red[wave][(lane >> 4) * (NV / 4) + j] = acc[j];
+    }
     if (a.norm_w) {
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
-            const float t = wave_sum(ss[r]);
+            const float t = wave_total(ss[r]);
             if (lane == 0) ssr[wave][r] = t;
         }
     }
@@ -1110,7 +1159,7 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
             v0 *= inv;
             v1 *= inv;
         }
-        epi_apply(a, ectx, er, n0 + ec, v0, v1);
+        epi_apply<EPIT>(a, ectx, er, n0 + ec, v0, v1);
     }
     stamp_end(a.stamp, t_begin);
 }
@@ -1270,8 +1319,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.comb) {   // single row, attention output merged on the fly (vector-ALU path only)
         const int nw = (a.K / epc + 63) / 64;
         if (a.R != 1 || !a.wbf16 || a.K % epc || a.N % KS_CPB || nw > 8 || a.D.hd % 8) return hipErrorInvalidValue;
-        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<true, 1, 0, true>(nv::GemmArgs)");
-        NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<true, 1, 0, true>), dim3(a.N / KS_CPB), dim3(64 * nw), 0, st, b);
+        if (a.epi != EPI_RESID) return hipErrorInvalidValue;
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<true, 1, 0, true, %d>(nv::GemmArgs)", EPI_RESID);
+        NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<true, 1, 0, true, EPI_RESID>), dim3(a.N / KS_CPB), dim3(64 * nw), 0, st, b);
         return hipGetLastError();
     }
     // decode-sized rows, vector ALUs (rows <= 8, and below the matrix-core threshold)
@@ -1280,19 +1330,31 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         const int nw = (a.K / epc + 63) / 64;
         const dim3 grid(a.N / KS_CPB), block(64 * nw);
         const int rm = a.R <= 1 ? 1 : a.R <= 2 ? 2 : a.R <= 4 ? 4 : 8;
-#define NV_KS(WB, RMV)                                                                                        \
+        // bf16: one instance per epilogue kind (the head's is EPI_STORE); fp32: run-time kind
+        const int ek = !a.wbf16 ? -1 : a.head ? (int)EPI_STORE : a.epi;
+#define NV_KS_E(WB, RMV, HD, E) NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, HD, false, E>), grid, block, 0, st, b)
+#define NV_KS(RMV)                                                                                            \
     do {                                                                                                     \
-        if (a.head) NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 1>), grid, block, 0, st, b);       \
-        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<WB, RMV, 0>), grid, block, 0, st, b);              \
+        if (!a.wbf16) {                                                                                      \
+            if (a.head) NV_KS_E(false, RMV, 1, -1); else NV_KS_E(false, RMV, 0, -1);                         \
+        } else if (a.head) {                                                                                 \
+            NV_KS_E(true, RMV, 1, EPI_STORE);                                                                \
+        } else {                                                                                             \
+            switch (a.epi) {                                                                                 \
+                case EPI_QKV: NV_KS_E(true, RMV, 0, EPI_QKV); break;                                         \
+                case EPI_RESID: NV_KS_E(true, RMV, 0, EPI_RESID); break;                                     \
+                case EPI_SWIGLU: NV_KS_E(true, RMV, 0, EPI_SWIGLU); break;                                   \
+                case EPI_SILU: NV_KS_E(true, RMV, 0, EPI_SILU); break;                                       \
+                default: NV_KS_E(true, RMV, 0, EPI_STORE); break;                                            \
+            }                                                                                                \
+        }                                                                                                    \
     } while (0)
-        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<%s, %d, %d>(nv::GemmArgs)",
-                                a.wbf16 ? "true" : "false", rm, a.head ? 1 : 0);
-        if (a.wbf16) {
-            if (rm == 1) NV_KS(true, 1); else if (rm == 2) NV_KS(true, 2); else if (rm == 4) NV_KS(true, 4); else NV_KS(true, 8);
-        } else {
-            if (rm == 1) NV_KS(false, 1); else if (rm == 2) NV_KS(false, 2); else if (rm == 4) NV_KS(false, 4); else NV_KS(false, 8);
-        }
+        if (a.wbf16 && !a.head && (a.epi < EPI_STORE || a.epi > EPI_SILU)) return hipErrorInvalidValue;
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<%s, %d, %d, false, %d>(nv::GemmArgs)",
+                                a.wbf16 ? "true" : "false", rm, a.head ? 1 : 0, ek);
+        if (rm == 1) NV_KS(1); else if (rm == 2) NV_KS(2); else if (rm == 4) NV_KS(4); else NV_KS(8);
 #undef NV_KS
+#undef NV_KS_E
         return hipGetLastError();
     }
     // decode-sized rows on the matrix cores (rows <= 32): K split across the waves, S k-steps each

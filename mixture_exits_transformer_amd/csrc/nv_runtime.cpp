@@ -483,7 +483,9 @@ struct Tables {
     CombineInfo* comb;
     AttnItem* items;
     int R, n_items;
-    int hrow0;         // hidden-state row of the first row (passed by value for one-row groups)
+    int hrow0;         // hidden-state row of the first row
+    bool contig;       // one chunk: row r is position pos0 + r of sequence seq0, hidden row hrow0 + r
+    int seq0, pos0;
     bool dec;          // decode-sized group: attention combines its splits in-kernel
     int max_rows;      // most rows in one decode-attention row block
     bool any_split;    // some row's key range was split (the combine pass is needed)
@@ -622,6 +624,9 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
     }
     t->dec = dec;
     t->hrow0 = R > 0 ? hrows[0].hrow : 0;
+    t->contig = chunks.size() == 1;
+    t->seq0 = R > 0 ? hrows[0].seq : 0;
+    t->pos0 = R > 0 ? hrows[0].pos : 0;
     t->any_split = false;
     t->max_split = 1;
     for (int i = 0; i < n_items; ++i) {
@@ -659,12 +664,14 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.rms_ws = m->rms_ws;
         g.abf = m->abf;
         g.mfma_min_rows = m->mfma_min_rows;
+        g.contig = t.contig ? 1 : 0;
+        g.a_row0 = g.o_row0 = t.hrow0;
+        g.seq0 = t.seq0;
+        g.pos0 = t.pos0;
         // q, k, v = RMSNorm(x) W_qkv^T
         g.A = m->Hs;
         g.lda = d;
         g.a_rows = t.rows;
-        g.a_row0_set = t.R == 1 ? 1 : 0;
-        g.a_row0 = t.hrow0;
         g.norm_w = W.attn_norm;
         g.W = W.wqkv;
         g.N = 3 * d;
@@ -684,7 +691,6 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         go.A = m->attn_o;
         go.lda = d;
         go.a_rows = nullptr;
-        go.a_row0_set = 0;
         go.norm_w = nullptr;
         go.W = W.wo;
         go.N = d;
@@ -734,7 +740,6 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.A = m->attn_o;
         g.lda = d;
         g.a_rows = nullptr;
-        g.a_row0_set = 0;
         g.norm_w = nullptr;
         g.W = W.wo;
         if (fuse_merge(m, t)) {
@@ -757,8 +762,6 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.A = m->Hs;
         g.lda = d;
         g.a_rows = t.rows;
-        g.a_row0_set = t.R == 1 ? 1 : 0;
-        g.a_row0 = t.hrow0;
         g.norm_w = W.mlp_norm;
         g.W = W.wgu;
         g.N = 2 * m->F;
@@ -772,7 +775,6 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         gd.A = m->mlp;
         gd.lda = m->F;
         gd.a_rows = nullptr;
-        gd.a_row0_set = 0;
         gd.norm_w = nullptr;
         gd.W = W.wd;
         gd.N = d;
@@ -1399,11 +1401,11 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
         g.A = m->Hs;
         g.lda = m->d;
         g.a_rows = m->lrows(m->d_headlist);
-        if (ns == 1) {
-            g.a_row0_set = 1;
-            g.a_row0 = m->lrows(hl)[0].hrow;
-        }
+        g.a_row0 = m->lrows(hl)[0].hrow;
     }
+    // one stopping sequence: its logits row (the sequence index) is known here
+    g.contig = ns == 1 ? 1 : 0;
+    g.o_row0 = seqs[0];
     g.norm_w = m->exits[ex0].norm;
     g.W = m->exits[ex0].head;
     g.N = m->V;

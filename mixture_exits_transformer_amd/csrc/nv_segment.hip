@@ -90,13 +90,6 @@ __device__ __forceinline__ void seg_bar() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Sum over the 64 lanes (DPP within rows of 16, then the 4 row sums read as scalars).
-__device__ __forceinline__ float wave_total(float v) {
-    v = group_sum<16>(v);
-    const int iv = __float_as_int(v);
-    return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) + __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) + __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
-}
 
 __device__ __forceinline__ void give_up(SegShared& sh, uint32_t* err) {
     sh.bad = 1;

@@ -146,7 +146,7 @@ def test_workload_E_sampled(lib, weights_dir):
         print("\nE:", end=" ")
         exits = [r[1] for r in recs]
         assert exits[4:] == [1, 2, 1, 4]
-        res.finish(2e-2)
+        res.finish(2e-2, max_logit_explained=None)   # V = 32000: token intervals ~3e-5
         lib.nv_flush(h)
         P = len(prompt) - 1
         rep = decoded_kv_report(lib, h, 0, st, (0, 11, 12, 23, 24, 47), P, exits, w.model.seg_layers)

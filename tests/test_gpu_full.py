@@ -5,10 +5,14 @@ a few decode steps after the full prompt, then KV of sampled layers after a flus
 Rule (see tests/parity.py): logits and every KV row (one position and head) within 2e-2
 relative, reported separately for prompt rows, decoded rows computed when their token
 passed, and deferred rows computed later in catch-up chunks or at the flush; hidden rows
-of the decoded positions within 2e-2; exits equal unless a draw is within 1e-5 of a gate
-or between the device's and the oracle's gate value (gates within 1e-2 of the oracle's,
-at most one such draw); tokens equal unless the draw is within 1e-5 of an oracle CDF
-boundary or (at most once) within the CDF shift implied by the checked logits."""
+of the decoded positions within 2e-2; the device's exit is exactly the walk over its own
+reported gate values and its token exactly the inverse-CDF draw of its own reported
+logits; exits equal the oracle's unless a draw is within 1e-5 of a gate or between the
+device's and the oracle's gate value (gates within 1e-2 of the oracle's, at most one such
+draw); tokens equal unless the draw is within 1e-5 of an oracle CDF boundary or within
+the CDF shift implied by the checked logits (at V = 32000 a token's interval, ~3e-5, is
+narrower than the shift a 2e-2 logit tolerance allows, so such draws are counted, not
+capped)."""
 import math
 from dataclasses import replace
 
@@ -64,7 +68,7 @@ def test_workload_A_sampled(lib, model_a):
         print("\nA:", end=" ")
         exits = [r[1] for r in recs]
         assert exits[4:] == [1, 1, 1, 4]
-        res.finish(TOL)
+        res.finish(TOL, max_logit_explained=None)   # V = 32000: token intervals ~3e-5
         lib.nv_flush(h)
         P = len(prompt) - 1
         rep = decoded_kv_report(lib, h, 0, st, SAMPLED_LAYERS, P, exits, w.model.seg_layers)
@@ -93,7 +97,7 @@ def test_workload_B_exit4_forced(lib, weights_dir, model_a):
             assert ex == 4 and o.p == [0.0, 0.0, 0.0, 1.0]
             check_step(t, o, tok, ex, lg, gw, res, logit_band=True)
         print("\nB:", end=" ")
-        res.finish(TOL)
+        res.finish(TOL, max_logit_explained=None)   # V = 32000: token intervals ~3e-5
         n, f = lib.nv_debug_frontiers(h, 0)
         assert list(f) == [n] * 4
         P = len(prompt) - 1
@@ -132,7 +136,7 @@ def test_workload_C_batch16_sampled(lib, model_a):
             check_step(t, o, int(tok[j]), int(ex[j]), lib.nv_debug_logits(h, j), lib.nv_debug_gates(h, j), res,
                        logit_band=True)
         print("\nC seq", j, ":", end=" ")
-        res.finish(TOL)
+        res.finish(TOL, max_logit_explained=None)   # V = 32000: token intervals ~3e-5
         # frontiers follow each sequence's exits
         E = np.stack(all_exits)                       # [steps][batch]
         for i, p in enumerate(ps):

@@ -103,7 +103,7 @@ def test_long_context_hd128_against_oracle(lib, weights_dir, prompt_len):
             assert ex == pattern[t]
             check_step(t, o, tok, ex, lg, gw, res, logit_band=True)
         print(f"\nhd128 ctx {prompt_len}:", end=" ")
-        res.finish(TOL)
+        res.finish(TOL, max_logit_explained=None)   # V = 1024: CDF shift ~1e-4 against intervals ~1e-3
         lib.nv_flush(h)
         P = prompt_len - 1
         rep = decoded_kv_report(lib, h, 0, st, range(M.L), P, pattern, HD128.seg_layers)
