@@ -69,6 +69,7 @@ struct GemmArgs {
     const struct CombineInfo* comb;
     const float* part_ml;
     const float* part_o;
+    int comb_ns;          // with contig and comb_ns > 0: comb[0] = {0, 0, comb_ns, 1}, by value
     // Exit heads of the mixture objective on the long-chunk path (k_gemm_bf16 only): when
     // xent_part is set, the logits are not stored.  Each block writes, per row and per
     // 64-column group g, (max, sum of exp(z - max)) at xent_part[2 (row * N/64 + g)], and
@@ -95,6 +96,36 @@ struct AttnItem {
     int pad[3];
 };
 
+
+// A decode group of one contiguous chunk of at most ATTN_DEC_ROWS rows (one row block):
+// everything its attention items, split-combine records and row table would hold, passed by
+// value so that no kernel starts with a dependent table load.  Block b of the attention
+// launch is split s = b % nsplit of head b / nsplit over keys [s * per, min(ctx, (s+1) * per)),
+// ctx = pos0 + nrows; its partial state for row r goes to slot (b * nrows + r).
+struct DecGeom {
+    int on;          // 0: read the uploaded tables instead
+    int seq, pos0, nrows, nsplit, per;
+};
+
+__host__ __device__ inline AttnItem dec_item(const DecGeom& g, int b) {
+    AttnItem it{};
+    const int h = b / g.nsplit, s = b - h * g.nsplit;
+    const int ctx = g.pos0 + g.nrows;
+    it.row0 = 0;
+    it.nrows = g.nrows;
+    it.head = h;
+    it.lo = s * g.per;
+    it.hi = ctx < it.lo + g.per ? ctx : it.lo + g.per;
+    it.part = b * g.nrows;
+    it.split = s;
+    it.nsplit = g.nsplit;
+    it.seq = g.seq;
+    return it;
+}
+
+__host__ __device__ inline CombineInfo dec_comb(const DecGeom& g, int row) {
+    return CombineInfo{0, row, g.nsplit, g.nrows};
+}
 
 // Launch wrappers (nv_kernels.hip).
 hipError_t launch_rope_table(float* cs, int max_ctx, int hd, float base, hipStream_t st);
@@ -123,7 +154,7 @@ constexpr int ATTN_DEC_ITERS = 8;
 constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
-                           float* out, hipStream_t st);
+                           float* out, hipStream_t st, const DecGeom& dg = DecGeom{});
 // Matrix-core variant of launch_attn for a bf16 KV cache and head_dim 32, 64 or 128:
 // items of up to 64 rows, key ranges starting at multiples of 64.
 bool attn_mfma_ok(const LayerDims& D);
@@ -135,13 +166,13 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
 // whose row blocks reach ATTN_DEC_MFMA_ROWS rows.
 hipError_t launch_attn_mfma16(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
                               const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
-                              float* out, hipStream_t st);
+                              float* out, hipStream_t st, const DecGeom& dg = DecGeom{});
 hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
                        const void* kv, int layer, const LayerDims& D, float* part_ml,
                        float* part_o, float* out, hipStream_t st);
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D,
                                const float* part_ml, const float* part_o, float* out,
-                               hipStream_t st);
+                               hipStream_t st, const DecGeom& dg = DecGeom{});
 // The combine for a product on bf16 rows: every (row, head) of the attention output goes
 // to out_bf16 [R][d] as bf16 (split rows merged, the others converted from out).
 hipError_t launch_attn_combine_bf16(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,

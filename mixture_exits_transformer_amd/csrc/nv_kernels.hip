@@ -1010,7 +1010,9 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 
     // activation chunks (rows past R repeat row R-1; their results are never written)
     float av[RM][EPC];
-    const CombineInfo cmb = COMB ? a.comb[0] : CombineInfo{0, 0, 1, 1};
+    const CombineInfo cmb = !COMB                       ? CombineInfo{0, 0, 1, 1}
+                            : (a.contig && a.comb_ns > 0) ? CombineInfo{0, 0, a.comb_ns, 1}
+                                                          : a.comb[0];
     if (!COMB || cmb.nsplit == 1) {
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
@@ -1634,7 +1636,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 template <int HD, int NWA>
 __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_mfma(
     const AttnItem* items, const RowInfo* rows, const float* q, const uint16_t* kv, int layer, LayerDims D,
-    float* part_ml, float* part_o, float* out, unsigned long long* stamp) {
+    float* part_ml, float* part_o, float* out, unsigned long long* stamp, DecGeom dg) {
     const unsigned long long t_begin = stamp_begin(stamp);
     constexpr int KLD = HD + 8;         // K tile row stride (bf16)
     constexpr int VLD = HD + 16;        // V tile row stride (bf16): rows an odd multiple of 8
@@ -1650,12 +1652,12 @@ __global__ __launch_bounds__(64 * NWA) __attribute__((amdgpu_waves_per_eu(1, 2))
     constexpr int NB = NWA == 1 ? 1 : 2;
     __shared__ __align__(16) uint16_t Ks[NB][AM_KT * KLD];
     __shared__ __align__(16) uint16_t Vs[NB][AM_KT * VLD];
-    const AttnItem it = items[blockIdx.x];
+    const AttnItem it = dg.on ? dec_item(dg, blockIdx.x) : items[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qn = lane & 15, g = lane >> 4;
     const int r = wave * 16 + qn;                  // this lane's query row within the item
     const bool rv = r < it.nrows;
-    const int qpos = rv ? rows[it.row0 + r].pos : -1;
+    const int qpos = !rv ? -1 : dg.on ? dg.pos0 + r : rows[it.row0 + r].pos;
     const int seq = it.seq;
     const uint16_t* Kg = kv + kv_base(D, seq, layer, 0, it.head);
     const uint16_t* Vg = kv + kv_base(D, seq, layer, 1, it.head);
@@ -1837,13 +1839,13 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
     const dim3 blk(64 * NWA);
     if (D.hd == 128)
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128, NWA>), dim3(n_items), blk, 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out, t_stamp);
+                  part_ml, part_o, out, t_stamp, DecGeom{});
     else if (D.hd == 64)
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64, NWA>), dim3(n_items), blk, 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out, t_stamp);
+                  part_ml, part_o, out, t_stamp, DecGeom{});
     else
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32, NWA>), dim3(n_items), blk, 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out, t_stamp);
+                  part_ml, part_o, out, t_stamp, DecGeom{});
     return hipGetLastError();
 }
 
@@ -1852,19 +1854,20 @@ hipError_t launch_attn_mfma(const AttnItem* items, int n_items, const RowInfo* r
 // holds, where the vector-ALU decode kernel repeats its dot products per row.
 hipError_t launch_attn_mfma16(const AttnItem* items, int n_items, const RowInfo* rows, const float* q,
                               const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
-                              float* out, hipStream_t st) {
+                              float* out, hipStream_t st, const DecGeom& dg) {
     if (n_items <= 0) return hipSuccess;
     if (!attn_mfma_ok(D)) return hipErrorInvalidValue;
+    if (dg.on && (dg.nrows < 1 || dg.nrows > 16 || n_items != D.H * dg.nsplit)) return hipErrorInvalidValue;
     const uint16_t* k16 = (const uint16_t*)kv;
     if (D.hd == 128)
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<128, 1>), dim3(n_items), dim3(64), 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out, t_stamp);
+                  part_ml, part_o, out, t_stamp, dg);
     else if (D.hd == 64)
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<64, 1>), dim3(n_items), dim3(64), 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out, t_stamp);
+                  part_ml, part_o, out, t_stamp, dg);
     else
         NV_LAUNCH(HIP_KERNEL_NAME(k_attn_mfma<32, 1>), dim3(n_items), dim3(64), 0, st, items, rows, q, k16, layer, D,
-                  part_ml, part_o, out, t_stamp);
+                  part_ml, part_o, out, t_stamp, dg);
     return hipGetLastError();
 }
 
@@ -1881,14 +1884,14 @@ constexpr int COMB_PRE = 8;      // partial outputs per thread loaded ahead of t
 
 __global__ __launch_bounds__(512) void k_attn_combine_blk(const CombineInfo* ci, int R, LayerDims D,
                                                           const float* part_ml, const float* part_o, float* out,
-                                                          unsigned long long* stamp) {
+                                                          unsigned long long* stamp, DecGeom dg) {
     const unsigned long long t_begin = stamp_begin(stamp);
     __shared__ float wsh[COMB_MAX];
     __shared__ float red[512];
     __shared__ float wred[8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = blockIdx.x / D.H, h = blockIdx.x - i * D.H;
-    const CombineInfo c = ci[i];
+    const CombineInfo c = dg.on ? dec_comb(dg, i) : ci[i];
     if (c.nsplit > 1) {
         const int ns = c.nsplit, hd = D.hd;
         const int64_t base = c.base + (int64_t)h * ns * c.nrows + c.off;   // split s adds s * nrows
@@ -2065,14 +2068,15 @@ hipError_t launch_attn(const AttnItem* items, int n_items, const RowInfo* rows, 
 }
 
 hipError_t launch_attn_combine(const CombineInfo* ci, int R, const LayerDims& D, const float* part_ml,
-                               const float* part_o, float* out, hipStream_t st) {
+                               const float* part_o, float* out, hipStream_t st, const DecGeom& dg) {
     if (R <= 0) return hipSuccess;
-    if (R * D.H >= COMB_WAVE_MIN_PAIRS) {
+    if (dg.on && dg.nrows != R) return hipErrorInvalidValue;
+    if (R * D.H >= COMB_WAVE_MIN_PAIRS && !dg.on) {
         if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_attn_combine");
         NV_LAUNCH(k_attn_combine, dim3((R * D.H + 3) / 4), dim3(256), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
     } else {
         if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_attn_combine_blk");
-        NV_LAUNCH(k_attn_combine_blk, dim3(R * D.H), dim3(512), 0, st, ci, R, D, part_ml, part_o, out, t_stamp);
+        NV_LAUNCH(k_attn_combine_blk, dim3(R * D.H), dim3(512), 0, st, ci, R, D, part_ml, part_o, out, t_stamp, dg);
     }
     return hipGetLastError();
 }
@@ -2102,14 +2106,14 @@ __device__ __forceinline__ void sm_merge(float& m, float& l, float* o, float m2,
 template <int HD, bool KVBF, int RM>
 __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const RowInfo* rows, const float* q,
                                                   const void* kv, int layer, LayerDims D, float* part_ml,
-                                                  float* part_o, float* out, unsigned long long* stamp) {
+                                                  float* part_o, float* out, unsigned long long* stamp, DecGeom dg) {
     const unsigned long long t_begin = stamp_begin(stamp);
     constexpr int DPL = 8;
     constexpr int LPK = HD / DPL;       // lanes per key
     constexpr int KPI = 64 / LPK;       // keys per wave instruction
     constexpr int NIT = ATTN_DEC_ITERS; // key groups per wave: a split holds at most 4 * KPI * NIT keys
     __shared__ float red[4][RM][HD + 2];
-    const AttnItem it = items[blockIdx.x];
+    const AttnItem it = dg.on ? dec_item(dg, blockIdx.x) : items[blockIdx.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / LPK, dl = lane - g * LPK;
     const int nr = it.nrows;
@@ -2129,7 +2133,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
         const float* qp = q + (int64_t)rr * D.d + it.head * HD + dl * DPL;
         qa[r][0] = *(const float4*)qp;
         qa[r][1] = *(const float4*)(qp + 4);
-        qpos[r] = rows[rr].pos;
+        qpos[r] = dg.on ? dg.pos0 + rr : rows[rr].pos;
     }
 
     uint4 kr[NIT], vr[NIT];
@@ -2271,11 +2275,13 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
 
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o, float* out,
-                           hipStream_t st) {
+                           hipStream_t st, const DecGeom& dg) {
     if (n_items <= 0) return hipSuccess;
+    if (dg.on && (dg.nrows < 1 || dg.nrows > ATTN_DEC_ROWS || dg.nrows > max_rows || n_items != D.H * dg.nsplit))
+        return hipErrorInvalidValue;
 #define NV_DEC(HDV, BF, RMV)                                                                                  \
     NV_LAUNCH(HIP_KERNEL_NAME(k_attn_dec<HDV, BF, RMV>), dim3(n_items), dim3(256), 0, st, items, rows, q, \
-                       kv, layer, D, part_ml, part_o, out, t_stamp)
+                       kv, layer, D, part_ml, part_o, out, t_stamp, dg)
 #define NV_DEC_R(HDV, BF)                                                                                     \
     do {                                                                                                     \
         if (max_rows <= 1) NV_DEC(HDV, BF, 1);                                                               \

@@ -486,12 +486,28 @@ struct Tables {
     int hrow0;         // hidden-state row of the first row
     bool contig;       // one chunk: row r is position pos0 + r of sequence seq0, hidden row hrow0 + r
     int seq0, pos0;
+    DecGeom dg;        // one chunk of at most ATTN_DEC_ROWS rows: the attention plan by value
+    bool on_device;    // the tables were uploaded (some kernel of this group reads them)
     bool dec;          // decode-sized group: attention combines its splits in-kernel
     int max_rows;      // most rows in one decode-attention row block
     bool any_split;    // some row's key range was split (the combine pass is needed)
     int max_split;     // most splits of one row's key range
     double kv_bytes;   // keys and values the attention items read
 };
+
+// Whether every block product of an R-row group runs on the vector-ALU decode GEMV (the one
+// kernel that needs no row table for a contiguous chunk): the shape limits of that path in
+// launch_gemm, for the four block products.
+bool gemv_only(const nv_model* m, int R) {
+    if (R < 1 || R > 8) return false;
+    if (m->bf16 && m->mfma_min_rows > 0 && R >= m->mfma_min_rows) return false;
+    const int epc = m->bf16 ? 8 : 4;
+    for (int K : {m->d, m->F})
+        if (K % epc || K % 4 || (K / epc + 63) / 64 > 8) return false;
+    for (int N : {3 * m->d, m->d, 2 * m->F})
+        if (N % 8) return false;
+    return true;
+}
 
 int c_max_ctx(const std::vector<Chunk>& chunks) {
     int mx = 0;
@@ -534,6 +550,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         const int max_keys = 4 * ATTN_DEC_ITERS * (64 / (m->hd / 8));
         int slot = 0, row0 = 0, rbi = 0;
         t->max_rows = 0;
+        t->dg = DecGeom{};
         for (const Chunk& c : chunks) {
             for (int rb = 0; rb < c.nrows; rb += ATTN_DEC_ROWS, ++rbi) {
                 const int nr = std::min(ATTN_DEC_ROWS, c.nrows - rb);
@@ -542,6 +559,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
                 const int ns = std::max((ctx + max_keys - 1) / max_keys, std::min(want, (ctx + 63) / 64));
                 if (ns > ATTN_COMB_MAX) return fail(m, NV_ECAPACITY, "internal: too many attention splits");
                 const int per = (ctx + ns - 1) / ns;
+                if (nrb == 1) t->dg = DecGeom{1, c.seq, c.pos0, nr, ns, per};   // the same plan, by value
                 for (int h = 0; h < m->H; ++h)
                     for (int s2 = 0; s2 < ns; ++s2) {
                         AttnItem& it = hitems[n_items++];
@@ -624,7 +642,6 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
     }
     t->dec = dec;
     t->hrow0 = R > 0 ? hrows[0].hrow : 0;
-    t->contig = chunks.size() == 1;
     t->seq0 = R > 0 ? hrows[0].seq : 0;
     t->pos0 = R > 0 ? hrows[0].pos : 0;
     t->any_split = false;
@@ -633,9 +650,16 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         t->any_split |= hitems[i].nsplit > 1;
         t->max_split = std::max(t->max_split, hitems[i].nsplit);
     }
-    const size_t bytes = items_off + sizeof(AttnItem) * (size_t)n_items;
-    NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, bytes, hipMemcpyHostToDevice, m->st));
-    m->stage_busy = true;
+    t->contig = chunks.size() == 1;
+    if (!t->contig) t->dg = DecGeom{};
+    // a one-chunk decode group whose products all take the vector-ALU decode GEMV reads no
+    // table: rows, attention items and split records are all passed by value
+    t->on_device = !(t->dg.on && gemv_only(m, R));
+    if (t->on_device) {
+        const size_t bytes = items_off + sizeof(AttnItem) * (size_t)n_items;
+        NV_HIP(m, hipMemcpyAsync(m->d_tables, m->h_stage, bytes, hipMemcpyHostToDevice, m->st));
+        m->stage_busy = true;
+    }
     t->rows = (RowInfo*)m->d_tables;
     t->comb = (CombineInfo*)(m->d_tables + comb_off);
     t->items = (AttnItem*)(m->d_tables + items_off);
@@ -710,17 +734,17 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             if (t.max_rows >= ATTN_DEC_MFMA_ROWS && attn_mfma_ok(D))
                 NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                     return launch_attn_mfma16(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
-                                              m->part_o, m->attn_o, m->st);
+                                              m->part_o, m->attn_o, m->st, t.dg);
                 }, "nv::k_attn_mfma (decode items)"));
             else
                 NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                     return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
-                                           m->part_o, m->attn_o, m->st);
+                                           m->part_o, m->attn_o, m->st, t.dg);
                 }, "nv::k_attn_dec"));
             // one row: the O projection merges the splits itself (no combine pass)
             if (t.any_split && !fuse_merge(m, t))
                 NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
-                    return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st);
+                    return launch_attn_combine(t.comb, t.R, D, m->part_ml, m->part_o, m->attn_o, m->st, t.dg);
                 }));
         } else if (attn_mfma_ok(D)) {
             NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes, [&] {
@@ -744,6 +768,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.W = W.wo;
         if (fuse_merge(m, t)) {
             g.comb = t.comb;
+            g.comb_ns = t.dg.on ? t.dg.nsplit : 0;
             g.part_ml = m->part_ml;
             g.part_o = m->part_o;
             g.D = D;
