@@ -77,7 +77,7 @@ size_t nv_mem_required(const char *weights_path, int32_t max_batch, int32_t max_
  *   hip_stream:   a hipStream_t to issue all work on, or NULL for the null stream.
  * Environment, read here (and, for the sizes, by nv_mem_required; set it the
  * same way for both calls):
- *   NVIUM_MFMA_MIN_ROWS  rows from which products use the matrix cores (default 5;
+ *   NVIUM_MFMA_MIN_ROWS  rows from which products use the matrix cores (default 9;
  *                        0: never), for tests of the vector-ALU paths;
  *   NVIUM_SEGMENT=1      one-row decode segments in the persistent segment kernel;
  *   NVIUM_LOSS_ROWS      rows per head pass of nv_mixture_loss (default: as many as

@@ -86,6 +86,27 @@ __device__ __forceinline__ void wave_rowsum_transpose(float (&v)[N]) {
     for (int i = 0; i < Q; ++i) v[i] = group_sum<16>(v[i]);
 }
 
+// Tagged words for exchanges between the blocks of one launch: the high 32 bits carry the
+// epoch of the write, the low 32 bits an fp32 value, so a reader knows a word is the one
+// it waits for without any fence.  Written with agent-scope stores, read with loads that
+// skip the caches a writer on another XCD cannot have updated.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint64_t tagv(uint32_t ep, float v) { return ((uint64_t)ep << 32) | __float_as_uint(v); }
+
+__device__ __forceinline__ void tstore(uint64_t* p, uint32_t ep, float v) {
+    __hip_atomic_store(p, tagv(ep, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ uint64_t tload_b(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 16);
+    return ((uint64_t)v.y << 32) | v.x;
+}
+
 __device__ __forceinline__ float kv_load(const void* kv, int bf16, int64_t i) {
     if (bf16) return __uint_as_float(((uint32_t)((const uint16_t*)kv)[i]) << 16);
     return ((const float*)kv)[i];

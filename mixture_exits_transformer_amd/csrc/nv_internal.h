@@ -78,7 +78,19 @@ struct GemmArgs {
     float* xent_part;     // [R][N/64][2]
     float* xent_tgt;      // [R]
     const int* xent_targets;   // [R] target token ids in [0, N)
+    // Exit head with the softmax partials (head == 2, one row, vector-ALU decode GEMV): block b
+    // also writes the (max, sum of exp(z - max)) of its KS_CPB logits to xd_part[2b], [2b+1];
+    // launch_exit_draw then draws the token from them without re-reading every logit.
+    float* xd_part;       // [N / 8][2]
 };
+
+// The exit draw: one block of XD_THREADS threads merges the head product's per-block
+// partials; a thread holds at most XD_PER of them (N / 8 <= XD_PER * XD_THREADS).
+constexpr int XD_THREADS = 512;
+constexpr int XD_PER = 16;
+// token[0] = inverse-CDF draw with u from softmax(logits[0..V)), V = 8 * nb, from the
+// partials `part` [nb][2] the head product wrote beside the logits.
+hipError_t launch_exit_draw(const float* part, int nb, const float* logits, float u, int* token, hipStream_t st);
 
 // One row of a chunk: position `pos` of sequence `seq`; hrow = seq * max_ctx + pos
 // indexes the hidden-state array.

@@ -984,9 +984,164 @@ bool gemm_uses_bf16_rows(const GemmArgs& a) {
 
 constexpr int KS_CPB = 8;          // output columns per block (vector-ALU kernel)
 
+// ------------------------------------------------------------------------------------------
+// Exit draw.  Inverse-CDF sampling of softmax(z) in token-id order (gist.science summary,
+// section 3: each exit's distribution is sampled exactly; the walk of the gates picked the
+// exit).  The one-row head product (k_gemv_ks with HEAD 2) ends with the online-softmax
+// step of each block: block b holds the logits of ids 8b..8b+7 and writes m_b = max z and
+// s_b = sum_j exp(z_j - m_b) (float32 exponentials summed in float32 in id order).  Then one
+// block (k_exit_draw) merges the partials:
+//   M = max_b m_b, t_b = s_b * exp(m_b - M) (float64), Z = sum_b t_b in block order;
+//   target = u * Z; b* = the block where the running sum of t_b first exceeds target;
+//   token = 8 b* + the first j with target < S_b* + c_j * exp(m_b* - M), c_j the float32
+//   running sum of exp(z_j - m_b*), which ends at s_b* exactly (the same operations).
+// If rounding leaves target at or past the total, the token is the last id with nonzero
+// mass.  The kernel boundary between the two makes the partials visible: on this chip a
+// completion count across the head product's 4000 blocks costs more than that boundary.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void exit_partial(const GemmArgs& a, const float* zb) {
+    __syncthreads();                                   // zb[] written by the epilogue threads
+    if (threadIdx.x == 0) {
+        float mb = -INFINITY;
+        for (int j = 0; j < KS_CPB; ++j) mb = fmaxf(mb, zb[j]);
+        float sb = 0.f;
+        if (mb != -INFINITY)
+            for (int j = 0; j < KS_CPB; ++j) sb += expf(zb[j] - mb);
+        *(float2*)(a.xd_part + 2 * (int64_t)blockIdx.x) = make_float2(mb, sb);
+    }
+}
+
+__global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int nb, const float* logits, float u,
+                                                          int* token) {
+    __shared__ float s_red[XD_THREADS / 64];
+    __shared__ double s_dred[XD_THREADS / 64];
+    __shared__ int s_bstar, s_last;
+    __shared__ double s_pre;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = XD_THREADS / 64;
+    const int per = (nb + XD_THREADS - 1) / XD_THREADS;          // <= XD_PER (checked at launch)
+    const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
+    if (tid == 0) {
+        s_bstar = -1;
+        s_last = -1;
+    }
+    float pm[XD_PER], ps[XD_PER];
+#pragma unroll
+    for (int i = 0; i < XD_PER; ++i) {
+        const float2 v = *(const float2*)(part + 2 * (b0 + i < b1 ? b0 + i : 0));   // past the range: block 0, unused
+        pm[i] = v.x;
+        ps[i] = v.y;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < XD_PER; ++i)
+        if (b0 + i < b1) mx = fmaxf(mx, pm[i]);
+    mx = wave_max(mx);
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    float M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+    // t_b in float64; this thread's sum in block order
+    double t[XD_PER];
+    double loc = 0.0;
+#pragma unroll
+    for (int i = 0; i < XD_PER; ++i) {
+        t[i] = (b0 + i < b1 && pm[i] != -INFINITY) ? (double)ps[i] * exp((double)pm[i] - (double)M) : 0.0;
+        loc += t[i];
+    }
+    // exclusive prefix of the thread sums in thread order (fixed order: waves, then lanes)
+    double inc = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
+    }
+    if (lane == 63) s_dred[wave] = inc;
+    __syncthreads();
+    double wpre = 0.0, Z = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        if (w < wave) wpre += s_dred[w];
+        Z += s_dred[w];
+    }
+    double exc = __shfl_up(inc, 1, 64);
+    if (lane == 0) exc = 0.0;
+    const double lo = wpre + exc, hi = wpre + inc;   // lo of a thread == hi of the one before
+    const double target = (double)u * Z;
+    if (b0 < b1 && lo <= target && target < hi) {
+        // the first block of this range whose running sum passes target (the last one if
+        // rounding keeps the walk below it)
+        double cum = lo, prev = lo, pre = lo;
+        int bs = -1;
+#pragma unroll
+        for (int i = 0; i < XD_PER; ++i) {
+            if (bs < 0 && b0 + i < b1) {
+                const double nx = cum + t[i];
+                if (target < nx) {
+                    bs = b0 + i;
+                    pre = cum;
+                }
+                prev = cum;
+                cum = nx;
+            }
+        }
+        if (bs < 0) {
+            bs = b1 - 1;
+            pre = prev;
+        }
+        s_bstar = bs;
+        s_pre = pre;
+    }
+    // the last block with a nonzero weight (for the fall-back)
+    int lb = -1;
+#pragma unroll
+    for (int i = 0; i < XD_PER; ++i)
+        if (b0 + i < b1 && t[i] > 0.0) lb = b0 + i;
+    if (lb >= 0) atomicMax(&s_last, lb);
+    __syncthreads();
+    if (tid == 0) {
+        int tok = -1;
+        const int bs = s_bstar;
+        if (bs >= 0) {
+            const float mb = part[2 * bs];
+            const double f = mb == -INFINITY ? 0.0 : exp((double)mb - (double)M);
+            float c = 0.f;
+            tok = bs * KS_CPB + KS_CPB - 1;
+            for (int j = 0; j < KS_CPB; ++j) {
+                c += expf(logits[bs * KS_CPB + j] - mb);
+                if (target < s_pre + (double)c * f) {
+                    tok = bs * KS_CPB + j;
+                    break;
+                }
+            }
+        } else if (s_last >= 0) {
+            // target at or past the rounded total: the last id with nonzero mass
+            const int L = s_last;
+            const float mb = part[2 * L];
+            for (int j = KS_CPB - 1; j >= 0; --j)
+                if (expf(logits[L * KS_CPB + j] - mb) > 0.f) {
+                    tok = L * KS_CPB + j;
+                    break;
+                }
+        }
+        *token = tok;
+    }
+}
+
+hipError_t launch_exit_draw(const float* part, int nb, const float* logits, float u, int* token, hipStream_t st) {
+    if (nb < 1 || nb > XD_PER * XD_THREADS || !part || !logits || !token || !(u >= 0.0f && u < 1.0f))
+        return hipErrorInvalidValue;
+    if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_exit_draw");
+    NV_LAUNCH(k_exit_draw, dim3(1), dim3(XD_THREADS), 0, st, part, nb, logits, u, token);
+    return hipGetLastError();
+}
+
 template <bool WBF, int RM, int HEAD, bool COMB = false, int EPIT = -1>
 __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
     static_assert(!COMB || RM == 1, "the fused attention merge handles one row");
+    static_assert(HEAD != 2 || (RM == 1 && !COMB), "the fused exit draw handles one row");
+    __shared__ float xd_z[HEAD == 2 ? KS_CPB : 1];
     constexpr int EPC = WBF ? 8 : 4;
     constexpr int ESZ = WBF ? 2 : 4;
     constexpr int NV = KS_CPB * RM;     // values per lane to reduce
@@ -1162,7 +1317,12 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
             v1 *= inv;
         }
         epi_apply<EPIT>(a, ectx, er, n0 + ec, v0, v1);
+        if constexpr (HEAD == 2) {
+            xd_z[ec] = v0;
+            xd_z[ec + 1] = v1;
+        }
     }
+    if constexpr (HEAD == 2) exit_partial(a, xd_z);
     stamp_end(a.stamp, t_begin);
 }
 
@@ -1351,6 +1511,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
             }                                                                                                \
         }                                                                                                    \
     } while (0)
+        if (a.head == 2) {
+            // the head product with its softmax partials: one row
+            if (a.R != 1 || !a.xd_part || a.epi != EPI_STORE || a.N / KS_CPB > XD_PER * XD_THREADS)
+                return hipErrorInvalidValue;
+            if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<%s, 1, 2, false, %d>(nv::GemmArgs)",
+                                    a.wbf16 ? "true" : "false", ek);
+            if (a.wbf16) NV_KS_E(true, 1, 2, EPI_STORE);
+            else NV_KS_E(false, 1, 2, -1);
+            return hipGetLastError();
+        }
         if (a.wbf16 && !a.head && (a.epi < EPI_STORE || a.epi > EPI_SILU)) return hipErrorInvalidValue;
         if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<%s, %d, %d, false, %d>(nv::GemmArgs)",
                                 a.wbf16 ? "true" : "false", rm, a.head ? 1 : 0, ek);

@@ -80,6 +80,7 @@ struct Plan {
     size_t qbuf = 0, attn_o = 0, mlp = 0, part_ml = 0, part_o = 0, rms = 0, abf = 0;
     size_t tables = 0, small = 0, logits = 0, router_hid = 0;
     size_t seg = 0;     // persistent segment kernel: tagged exchange buffers, counters, layer table
+    size_t xd = 0;      // exit draw: the head product's per-block softmax partials
     int loss_ch = 0;    // mixture objective: rows per head pass
     size_t loss = 0;    // its logits, per-row router outputs / log-probabilities / losses, row tables
     size_t total = 0;
@@ -183,6 +184,7 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
     p.seg = 6 * align_up((size_t)d * 8) + align_up((size_t)F * 8) +
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
+    p.xd = align_up((size_t)(V / 8) * 2 * 4);
     // rows per head pass of the mixture objective: every pass re-reads the head weights, so
     // a pass takes as many rows as a 256 MiB logits workspace holds (at least 256, at most
     // the row capacity); NVIUM_LOSS_ROWS sets it instead (tests of ragged passes)
@@ -198,7 +200,7 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
              align_up((size_t)p.loss_ch * ((V + 63) / 64) * 8) + align_up((size_t)p.loss_ch * 4);
     p.total = p.abf + p.loss + p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head +
               p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
-              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + kAlign;
+              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + p.xd + kAlign;
     return p;
 }
 
@@ -241,10 +243,11 @@ struct nv_model {
     double* loss_hid = nullptr;     // [loss_ch][router_dim]
     float* loss_xpart = nullptr;    // [loss_ch][V/64][2] fused cross-entropy partials
     float* loss_xtgt = nullptr;     // [loss_ch] target logits
-    // chunks of at least this many rows use the matrix cores: at 5-8 rows the vector-ALU
-    // GEMV holds 5-8 rows of activations per lane and moves about 1 TB/s, the matrix-core
-    // path 1.5-1.7 TB/s (batch-16 decode +7 %)
-    int mfma_min_rows = 5;
+    // chunks of at least this many rows use the matrix cores; up to 8 rows the vector-ALU
+    // decode GEMV (LDS-free reductions, every weight load in flight before any wait) beats
+    // the 16-row matrix-core tiles, which leave half their rows empty at 5-8 rows
+    // (batch-1 decode: 0.417 -> 0.411 ms per segment-token against a threshold of 5)
+    int mfma_min_rows = 9;
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
     // goes up in one copy.  step: [uniforms MB*4 f32][pending tokens MB i32][current rows MB]
@@ -252,6 +255,7 @@ struct nv_model {
     char* d_stepblk = nullptr;
     char* d_gatelist = nullptr;
     char* d_headlist = nullptr;
+    float* xd_part = nullptr;        // exit draw: the head product's per-block (max, sum exp)
     double* d_w = nullptr;
     int* d_stop = nullptr;
     int* d_tok_out = nullptr;
@@ -507,6 +511,14 @@ bool gemv_only(const nv_model* m, int R) {
     for (int N : {3 * m->d, m->d, 2 * m->F})
         if (N % 8) return false;
     return true;
+}
+
+// Whether a one-row exit head runs on the vector-ALU decode GEMV (the kernel that can write
+// the per-block softmax partials of the exit draw).
+bool head_gemv_ok(const nv_model* m) {
+    const int epc = m->bf16 ? 8 : 4;
+    return m->d % epc == 0 && m->d % 4 == 0 && (m->d / epc + 63) / 64 <= 8 && m->V % 8 == 0 &&
+           (!m->bf16 || m->mfma_min_rows == 0 || m->mfma_min_rows > 1);
 }
 
 int c_max_ctx(const std::vector<Chunk>& chunks) {
@@ -1187,6 +1199,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->loss_xpart = (float*)m->take((size_t)P.loss_ch * ((m->V + 63) / 64) * 8);
     m->loss_xtgt = (float*)m->take((size_t)P.loss_ch * 4);
     m->seg_base = m->take(P.seg);
+    m->xd_part = (float*)m->take(P.xd);
     if (m->arena_off > P.total) return fail(m, NV_ECAPACITY, "internal: arena plan too small");
 
     m->h_stage_bytes = P.tables;
@@ -1358,8 +1371,10 @@ nv_status nv_prefill(nv_model* m, int32_t seq, const int32_t* tokens, int32_t n)
 //   own heads:   the exit's RMSNorm and LM head on the hidden row (seqs share one exit);
 //   shared head: hidden rows are gathered (seqs ordered by exit), exits 1..3 add their
 //                adapter U silu(D h), then one pass of the final RMSNorm and LM head.
+// u4: host copy of each listed sequence's token uniform, indexed by sequence (one stopping
+// sequence takes the fused head product + draw), or null.
 static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std::vector<int>& exit_of,
-                           const float* d_unif) {
+                           const float* d_unif, const float* u4 = nullptr) {
     if (m->hl_busy[m->hl_next]) {
         NV_HIP(m, hipStreamSynchronize(m->st));
         stream_synced(m);
@@ -1441,6 +1456,17 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
     g.ldo = m->V;
     g.o_rows = m->lorows(m->d_headlist);
     g.head = 1;
+    if (ns == 1 && u4 && m->V % 8 == 0 && m->V / 8 <= XD_PER * XD_THREADS && head_gemv_ok(m)) {
+        // one stopping sequence: the head product also writes its per-block softmax partials,
+        // and one block draws the token from them
+        g.head = 2;
+        g.xd_part = m->xd_part;
+        NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, g));
+        const float* lg = m->logits + (int64_t)seqs[0] * m->V;
+        return timed(m, NV_TIME_OTHER, (double)(m->V / 8) * 8 + 32, [&] {
+            return launch_exit_draw(m->xd_part, m->V / 8, lg, u4[seqs[0]], m->d_tok_out + seqs[0], m->st);
+        }, "nv::k_exit_draw");
+    }
     NV_TRY(run_gemm(m, NV_TIME_EXIT_HEAD, g));
     NV_TRY(timed(m, NV_TIME_OTHER, (double)ns * m->V * 4, [&] {
         return launch_sample(m->logits, m->V, nv_model::lseqs(m->d_headlist), ns, m->V, d_unif, m->d_tok_out,
@@ -1546,6 +1572,8 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
     std::vector<int> active(n), exit_of(n, kMaxExits);
     for (int i = 0; i < n; ++i) active[i] = i;
     for (int i = 0; i < n * 4; ++i) m->last_w[i] = NAN;
+    std::vector<float> u4(n);
+    for (int i = 0; i < n; ++i) u4[i] = u[i * 4 + 3];
     int* htok_out = (int*)(m->h_out + (size_t)m->max_batch * 4);
     double* hw = (double*)(m->h_out + (size_t)m->max_batch * 8);
     std::vector<int> stopped;   // shared head: the step's stopping sequences, in exit order
@@ -1570,14 +1598,19 @@ static nv_status step_impl(nv_model* m, const float* u, const int32_t* forced, i
             // shared head: every stopping sequence of this step goes through one head pass
             for (int i : stopping) stopped.push_back(i);
         } else if (!stopping.empty()) {
-            NV_TRY(run_heads(m, stopping, exit_of, d_unif));
+            NV_TRY(run_heads(m, stopping, exit_of, d_unif, u4.data()));
         }
     }
-    if (!stopped.empty()) NV_TRY(run_heads(m, stopped, exit_of, d_unif));
+    if (!stopped.empty()) NV_TRY(run_heads(m, stopped, exit_of, d_unif, u4.data()));
     NV_HIP(m, hipMemcpyAsync(htok_out, m->d_tok_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->st));
     NV_HIP(m, hipMemcpyAsync(hw, m->d_w, (size_t)n * 32, hipMemcpyDeviceToHost, m->st));
     NV_TRY(sync_and_check(m));
     if (m->timing) NV_TRY(resolve_timing(m));
+    for (int i = 0; i < n; ++i)
+        if (htok_out[i] < 0 || htok_out[i] >= m->V) {
+            m->dead = true;
+            return fail(m, NV_EDEVICE, "exit draw: the head product's blocks did not all report");
+        }
     for (int i = 0; i < n; ++i) {
         SeqHost& S = m->seqs[i];
         const int e = exit_of[i];

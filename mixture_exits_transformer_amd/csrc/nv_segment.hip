@@ -65,22 +65,7 @@ struct SegShared {
     int bad;                    // a wait in this block gave up
 };
 
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint64_t tagv(uint32_t ep, float v) { return ((uint64_t)ep << 32) | __float_as_uint(v); }
-
-__device__ __forceinline__ void tstore(uint64_t* p, uint32_t ep, float v) {
-    __hip_atomic_store(p, tagv(ep, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-}
-
-__device__ __forceinline__ uint64_t tload_b(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 16);
-    return ((uint64_t)v.y << 32) | v.x;
-}
 
 
 // Block barrier that orders LDS only: global loads in flight stay in flight.
