@@ -5,10 +5,15 @@ linear term g_k . h of a gate (g_k ~ N(0, 0.02^2)) has a standard deviation near
 sigmoid(b_k) alone does not give the stated marginal exit masses.  The marginal mass of
 exit k is the mean over tokens of p_k = w_k prod_{j<k} (1 - w_j), with w_k = sigmoid(g_k .
 h^(l_k) + b_k) (gist.science summary, section 2 "Methodik", part "Architektur": equation
-for p_k).  This script runs the oracle's float64 forward over a seeded calibration prompt
-(512 uniform-random tokens, numpy default_rng(3)), keeps z_k = g_k . h^(l_k) at positions
-64..510, and solves, exit by exit, for the b_k whose sample mean of p_k equals the stated
-mass (p_k is increasing in b_k when the earlier biases are fixed; bisection in float64).
+for p_k).  The linear term drifts with the position (gate 1's mean falls from about +1.2
+at positions 64-164 to -1.0 at 896-1023), so each workload is calibrated where it decodes.
+This script runs the oracle's float64 forward over a seeded calibration prompt of
+uniform-random tokens through the first three segments (the gates need no more), keeps
+z_k = g_k . h^(l_k) at the workload's decode positions, and solves, exit by exit, for the
+b_k whose sample mean of p_k equals the stated mass (p_k is increasing in b_k when the
+earlier biases are fixed; bisection in float64):
+  A (512-token prompt, 512 steps):    1024 tokens, default_rng(3), positions 512..1022
+  D (8192-token prompt, 256 steps):   8448 tokens, default_rng(4), positions 8192..8446
 
     python tests/golden/make_gate_bias.py       # writes tests/golden/gate_bias_1p5b.json
 """
@@ -26,7 +31,7 @@ from oracle import model as om                       # noqa: E402
 from synth import M15B, cached_weights              # noqa: E402
 
 MASSES = {"A": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1)}
-PROMPT_SEED, PROMPT_LEN, FIRST_POS = 3, 512, 64
+SAMPLES = {"A": (3, 1024, 512), "D": (4, 8448, 8192)}     # prompt seed, prompt length, first position
 
 
 def sig(x):
@@ -53,32 +58,37 @@ def solve_biases(z: np.ndarray, masses) -> list:
     return out
 
 
-def main():
-    path = cached_weights(M15B)
-    M = om.OracleModel(path)
-    rng = np.random.default_rng(PROMPT_SEED)
-    tokens = rng.integers(0, M.V, size=PROMPT_LEN)
-    n = PROMPT_LEN - 1
+def sample_z(M, seed: int, n_tokens: int, first_pos: int) -> np.ndarray:
+    """The gates' linear terms z_k = g_k . h^(l_k) (k < 3) at positions first_pos..n_tokens-2
+    of a uniform-random prompt, from the oracle's layers (a causal chunk per layer)."""
+    rng = np.random.default_rng(seed)
+    tokens = rng.integers(0, M.V, size=n_tokens)
+    n = n_tokens - 1
     kv = om.KVCache(M, n)
     pos = np.arange(n)
     X = np.asarray(M.embed[tokens[:n]], dtype=np.float64)
     z = np.zeros((n, 3))
-    for l in range(M.L):
+    for l in range(M.exit_layers[2]):
         X = om.layer_rows(M, l, X, pos, kv)
         for k in range(3):
             if l + 1 == M.exit_layers[k]:
                 z[:, k] = X @ M.gate_w[k]
-        print(f"layer {l + 1}/{M.L}", flush=True)
-    zs = z[FIRST_POS:]
-    res = {"source": "tests/golden/make_gate_bias.py (oracle float64 forward, 1.5B model, seed-0 weights)",
-           "prompt": f"{PROMPT_LEN} uniform-random tokens, numpy default_rng({PROMPT_SEED})",
-           "positions": [FIRST_POS, n - 1],
-           "z_std": [float(np.std(zs[:, k])) for k in range(3)],
-           "z": [[round(float(v), 9) for v in row] for row in zs]}
-    for name, m in MASSES.items():
-        b = solve_biases(zs, m)
-        res[f"bias_{name}"] = b
-        res[f"mass_{name}"] = list(m)
+        print(f"seed {seed}: layer {l + 1}/{M.exit_layers[2]}", flush=True)
+    return z[first_pos:]
+
+
+def main():
+    path = cached_weights(M15B)
+    M = om.OracleModel(path)
+    res = {"source": "tests/golden/make_gate_bias.py (oracle float64 forward, 1.5B model, seed-0 weights)"}
+    for name, (seed, n_tokens, first) in SAMPLES.items():
+        zs = sample_z(M, seed, n_tokens, first)
+        b = solve_biases(zs, MASSES[name])
+        res[name] = {"prompt": f"{n_tokens} uniform-random tokens, numpy default_rng({seed})",
+                     "positions": [first, n_tokens - 2], "mass": list(MASSES[name]), "bias": b,
+                     "z_mean": [float(np.mean(zs[:, k])) for k in range(3)],
+                     "z_std": [float(np.std(zs[:, k])) for k in range(3)],
+                     "z": [[round(float(v), 9) for v in row] for row in zs]}
         print(name, "biases", b, flush=True)
     out = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gate_bias_1p5b.json")
     with open(out, "w") as f:

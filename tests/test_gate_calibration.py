@@ -1,6 +1,7 @@
 """The calibrated gate biases of the 1.5B workloads reproduce the stated exit masses on
-the calibration sample that tests/golden/make_gate_bias.py stored (the oracle's linear
-terms z_k = g_k . h^(l_k) at 447 prompt positions): the mean over positions of the
+the calibration samples that tests/golden/make_gate_bias.py stored (the oracle's linear
+terms z_k = g_k . h^(l_k) at the positions each workload decodes: 512..1022 for the
+512-token prompt, 8192..8446 for the 8192-token prompt): the mean over positions of the
 stick-breaking p_k (gist.science summary, section 2 "Methodik", part "Architektur":
 equation for p_k) with w_k = sigmoid(z_k + b_k) equals the stated mass.  The biases the
 workloads carry are the stored ones."""
@@ -28,18 +29,22 @@ def _masses(z, b):
 
 def test_calibrated_biases_give_stated_masses():
     g = json.load(open(GOLDEN))
-    z = np.asarray(g["z"])
-    assert z.shape == (447, 3)
-    for name, b_cfg in (("A", BIAS_CAL_1P5B_40_25_20_15), ("D", BIAS_CAL_1P5B_60_20_10_10)):
-        assert np.allclose(g[f"bias_{name}"], b_cfg, rtol=0, atol=1e-12)
+    for name, b_cfg, n in (("A", BIAS_CAL_1P5B_40_25_20_15, 511), ("D", BIAS_CAL_1P5B_60_20_10_10, 255)):
+        z = np.asarray(g[name]["z"])
+        assert z.shape == (n, 3)
+        assert np.allclose(g[name]["bias"], b_cfg, rtol=0, atol=1e-12)
         m = _masses(z, b_cfg)
-        assert np.allclose(m, g[f"mass_{name}"], rtol=0, atol=1e-6), (name, m)
+        assert np.allclose(m, g[name]["mass"], rtol=0, atol=1e-6), (name, m)
         # the header stores the biases as float32: the masses move by far less than 1e-3
         m32 = _masses(z, np.asarray(b_cfg, np.float32).astype(np.float64))
-        assert np.allclose(m32, g[f"mass_{name}"], rtol=0, atol=1e-5)
+        assert np.allclose(m32, g[name]["mass"], rtol=0, atol=1e-5)
     # without calibration (sigmoid(b) alone) the same sample misses the stated masses
     from synth.configs import BIAS_MASS_40_25_20_15
-    assert np.max(np.abs(_masses(z, BIAS_MASS_40_25_20_15) - np.asarray(g["mass_A"]))) > 0.05
+    zA = np.asarray(g["A"]["z"])
+    assert np.max(np.abs(_masses(zA, BIAS_MASS_40_25_20_15) - np.asarray(g["A"]["mass"]))) > 0.05
+    # and the A biases do not carry over to the 8K positions (the linear term drifts)
+    zD = np.asarray(g["D"]["z"])
+    assert np.max(np.abs(_masses(zD, BIAS_CAL_1P5B_40_25_20_15) - np.asarray(g["A"]["mass"]))) > 0.05
 
 
 def test_workloads_carry_the_calibrated_biases():
