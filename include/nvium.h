@@ -177,6 +177,37 @@ nv_status nv_mixture_loss(nv_model *m, int32_t seq, const int32_t *tokens, int32
  * no-op.  Errors: NV_EINVAL (seq out of range), NV_EDEVICE. */
 nv_status nv_flush(nv_model *m, int32_t seq);
 
+/* ---- one exit's draw on caller buffers --------------------------------------- */
+
+/* Bytes of device workspace nv_exit_draw needs for a vocabulary of `vocab` ids (0 if
+ * vocab is not a positive multiple of 8 up to 65536). */
+size_t nv_exit_draw_workspace(int32_t vocab);
+
+/* One exit's head and draw for one hidden row, the step nv_step takes for a sequence that
+ * stops at an exit (gist.science technical summary of the pages, section 2, part
+ * "Architektur": every exit has its own head; section 3: the exit's distribution is sampled
+ * exactly).  logits = W_head . RMSNorm(h) (RMSNorm weight norm_w, epsilon eps), then token =
+ * the smallest id i with u < F(i), F the running sum of softmax(logits) in id order
+ * (float32 exponentials, float64 sums and comparison); if rounding leaves u at or past the
+ * total, the last id with nonzero mass.
+ *   h         device float32 [d]: the residual stream after the exit's last layer
+ *   norm_w    device float32 [d]
+ *   head_w    device [vocab][d]: bf16 bit patterns if wdtype is 1, float32 if 0
+ *   u         the uniform, in [0, 1)
+ *   logits    device float32 [vocab], written
+ *   token     device int32 [1], written
+ *   workspace device memory of at least nv_exit_draw_workspace(vocab) bytes (scratch: the
+ *             head product's per-block softmax partials), owned by the caller
+ *   hip_stream the hipStream_t to enqueue on (NULL: the null stream)
+ * Shapes: d a multiple of 8 (bf16) or 4 (float32), d <= 4096 (bf16) or 2048 (float32);
+ * vocab a multiple of 8, at most 65536.  The call only enqueues work (it does not wait, and
+ * it allocates nothing); the outputs are valid once the stream has run it.  Errors:
+ * NV_EINVAL (NULL pointer, shape, u outside [0,1) or NaN, eps <= 0), NV_ECAPACITY
+ * (workspace too small), NV_EDEVICE (a launch failed). */
+nv_status nv_exit_draw(const float *h, const float *norm_w, const void *head_w, int32_t wdtype, int32_t d,
+                       int32_t vocab, float eps, float u, float *logits, int32_t *token, void *workspace,
+                       size_t workspace_bytes, void *hip_stream);
+
 /* ---- inspection (not on the timed path) ------------------------------------ */
 
 /* Positions consumed so far (prompt prefix + decode steps) and the four

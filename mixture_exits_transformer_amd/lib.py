@@ -61,6 +61,9 @@ _SIGS = {
     "nv_debug_kv": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _F32P,
                                    _F32P]),
     "nv_debug_hidden": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _F32P]),
+    "nv_exit_draw_workspace": (ctypes.c_size_t, [ctypes.c_int32]),
+    "nv_exit_draw": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                    ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "nv_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "nv_timing_read": (ctypes.c_int, [_P, _F64P, _F64P, ctypes.POINTER(ctypes.c_int64)]),
     "nv_timing_kernels": (ctypes.c_int, [_P, ctypes.c_char_p, ctypes.c_size_t]),
@@ -209,6 +212,39 @@ def nv_mixture_loss(h: Handle, seq: int, tokens, beta: float = 0.0, per_pos: boo
                                             _ptr(out, ctypes.c_double),
                                             _ptr(pp, ctypes.c_double) if per_pos else None))
     return (tuple(float(x) for x in out), pp) if per_pos else tuple(float(x) for x in out)
+
+
+def _dptr(t) -> int:
+    """Device address of a torch tensor (or an int address)."""
+    return t if isinstance(t, int) else t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def nv_exit_draw_workspace(vocab: int) -> int:
+    return int(library().nv_exit_draw_workspace(vocab))
+
+
+def nv_exit_draw(h, norm_w, head_w, wdtype: int, d: int, vocab: int, eps: float, u: float, logits, token,
+                 workspace, workspace_bytes: int, stream=None) -> None:
+    """Enqueue one exit's head + draw on device buffers (torch tensors or addresses); the
+    outputs `logits` [vocab] float32 and `token` [1] int32 are valid once the stream has run it."""
+    st = library().nv_exit_draw(_dptr(h), _dptr(norm_w), _dptr(head_w), wdtype, d, vocab, eps, u, _dptr(logits),
+                                _dptr(token), _dptr(workspace), workspace_bytes, _stream_ptr(stream))
+    if st != NV_OK:
+        raise NvError(st, "nv_exit_draw")
+
+
+def nv_get_config(h: Handle) -> nv_config:
+    """The model shape read from the weights file."""
+    c = nv_config()
+    _check(h.ptr, library().nv_get_config(h.ptr, ctypes.byref(c)))
+    return c
 
 
 def nv_flush(h: Handle, seq: int = -1) -> None:
