@@ -208,6 +208,17 @@ nv_status nv_exit_draw(const float *h, const float *norm_w, const void *head_w, 
                        int32_t vocab, float eps, float u, float *logits, int32_t *token, void *workspace,
                        size_t workspace_bytes, void *hip_stream);
 
+/* nv_exit_draw for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments
+ * without the workspace.  Its scratch is a 64 KiB array inside the library, one per GPU,
+ * held until the process ends (vocab up to 65536, as for nv_exit_draw).  It allocates
+ * nothing and only enqueues work.  Calls that overlap on one GPU (on different streams or
+ * threads) share that array and race; serialize them.  Errors: as nv_exit_draw, and
+ * NV_EDEVICE if the array's device address cannot be obtained. */
+nv_status nv_exit_draw_static(const float *h, const float *norm_w, const void *head_w, int32_t wdtype,
+                              int32_t d, int32_t vocab, float eps, float u, float *logits, int32_t *token,
+                              void *hip_stream);
+
 /* ---- inspection (not on the timed path) ------------------------------------ */
 
 /* Positions consumed so far (prompt prefix + decode steps) and the four

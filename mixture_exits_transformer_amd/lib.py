@@ -64,6 +64,8 @@ _SIGS = {
     "nv_exit_draw_workspace": (ctypes.c_size_t, [ctypes.c_int32]),
     "nv_exit_draw": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                     ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "nv_exit_draw_static": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, ctypes.c_float, _P, _P, _P]),
     "nv_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "nv_timing_read": (ctypes.c_int, [_P, _F64P, _F64P, ctypes.POINTER(ctypes.c_int64)]),
     "nv_timing_kernels": (ctypes.c_int, [_P, ctypes.c_char_p, ctypes.c_size_t]),
@@ -238,6 +240,16 @@ def nv_exit_draw(h, norm_w, head_w, wdtype: int, d: int, vocab: int, eps: float,
                                 _dptr(token), _dptr(workspace), workspace_bytes, _stream_ptr(stream))
     if st != NV_OK:
         raise NvError(st, "nv_exit_draw")
+
+
+def nv_exit_draw_static(h, norm_w, head_w, wdtype: int, d: int, vocab: int, eps: float, u: float, logits, token,
+                        stream=None) -> None:
+    """nv_exit_draw with the library's own per-GPU scratch (allocates nothing; calls that
+    overlap on one GPU race)."""
+    st = library().nv_exit_draw_static(_dptr(h), _dptr(norm_w), _dptr(head_w), wdtype, d, vocab, eps, u,
+                                       _dptr(logits), _dptr(token), _stream_ptr(stream))
+    if st != NV_OK:
+        raise NvError(st, "nv_exit_draw_static")
 
 
 def nv_get_config(h: Handle) -> nv_config:
