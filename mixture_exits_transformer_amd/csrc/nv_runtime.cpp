@@ -304,6 +304,7 @@ struct nv_model {
 
     // optional per-class kernel timing with HIP events on the work stream
     bool timing = false;
+    bool timing_stamps = false;   // also stamp every block (adds a fold kernel after each launch)
     std::vector<hipEvent_t> ev;   // pairs
     std::vector<int> ev_kind;
     std::vector<double> ev_bytes;
@@ -315,8 +316,10 @@ struct nv_model {
     struct KStat {
         std::string name;
         int kind;
-        double ms, bytes;
+        double ms, bytes;      // ms: launch to completion (HIP events around each launch)
         int64_t n;
+        double span_ms = 0.0;  // first block start to last block end (device stamps), if stamped
+        int64_t n_span = 0;
     };
     std::vector<KStat> kstats;
     size_t ev_used = 0;
@@ -381,8 +384,9 @@ nv_status resolve_timing(nv_model* m) {
     for (size_t i = 0; i < m->ev_used; ++i) {
         float ms = 0.f;
         NV_HIP(m, hipEventElapsedTime(&ms, m->ev[2 * i], m->ev[2 * i + 1]));
-        // stamped kernels: first block start to last block end on the device clock
-        if (m->ev_stamped[i] && st[2 * i + 1] > st[2 * i]) ms = (float)((st[2 * i + 1] - st[2 * i]) / m->wall_khz);
+        // stamped kernels also report first block start to last block end on the device clock
+        const bool spanned = m->ev_stamped[i] && st[2 * i + 1] > st[2 * i];
+        const double span = spanned ? (double)(st[2 * i + 1] - st[2 * i]) / m->wall_khz : 0.0;
         const int k = m->ev_kind[i];
         m->t_ms[k] += ms;
         m->t_bytes[k] += m->ev_bytes[i];
@@ -390,12 +394,16 @@ nv_status resolve_timing(nv_model* m) {
         auto it = std::find_if(m->kstats.begin(), m->kstats.end(),
                                [&](const nv_model::KStat& ks) { return ks.name == m->ev_name[i] && ks.kind == k; });
         if (it == m->kstats.end()) {
-            m->kstats.push_back({m->ev_name[i], k, 0.0, 0.0, 0});
+            m->kstats.push_back({m->ev_name[i], k, 0.0, 0.0, 0, 0.0, 0});
             it = m->kstats.end() - 1;
         }
         it->ms += ms;
         it->bytes += m->ev_bytes[i];
         it->n += 1;
+        if (spanned) {
+            it->span_ms += span;
+            it->n_span += 1;
+        }
     }
     m->ev_used = 0;
     // reset the spans: start = max, end = 0
@@ -420,18 +428,16 @@ nv_status timed(nv_model* m, int kind, double bytes, F&& launch, const char* nam
         nv_status s = resolve_timing(m);
         if (s != NV_OK) return s;
     }
-    // drain the stream first: with work queued ahead, the start stamp would include the
-    // time the dispatch waits behind it
-    NV_HIP(m, hipStreamSynchronize(m->st));
     const size_t i = m->ev_used++;
-    m->ev_stamped[i] = 1;   // kernels that support stamps use them; others leave (max, 0)
-    set_launch_stamp(m->d_blkstamps);
+    // kernels that support stamps use them; others leave (max, 0)
+    m->ev_stamped[i] = m->timing_stamps ? 1 : 0;
+    if (m->timing_stamps) set_launch_stamp(m->d_blkstamps);
     set_launch_events(m->ev[2 * i], m->ev[2 * i + 1]);
     const hipError_t le = launch();
     set_launch_events(nullptr, nullptr);
     set_launch_stamp(nullptr);
     NV_HIP(m, le);
-    NV_HIP(m, launch_stamp_reduce(m->d_blkstamps, STAMP_BLOCKS, m->d_stamps + 2 * i, m->st));
+    if (m->timing_stamps) NV_HIP(m, launch_stamp_reduce(m->d_blkstamps, STAMP_BLOCKS, m->d_stamps + 2 * i, m->st));
     m->ev_kind[i] = kind;
     m->ev_bytes[i] = bytes;
     m->ev_name[i] = name ? name : last_launch_name();
@@ -568,9 +574,12 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
                 const int nr = std::min(ATTN_DEC_ROWS, c.nrows - rb);
                 t->max_rows = std::max(t->max_rows, nr);
                 const int ctx = c.pos0 + rb + nr;
-                const int ns = std::max((ctx + max_keys - 1) / max_keys, std::min(want, (ctx + 63) / 64));
+                const int ns0 = std::max((ctx + max_keys - 1) / max_keys, std::min(want, (ctx + 63) / 64));
+                const int per = (ctx + ns0 - 1) / ns0;
+                // with per rounded up, fewer splits may cover the range: drop the empty ones
+                // (at 8K keys and 128 splits, per = 65 leaves the last split past ctx)
+                const int ns = (ctx + per - 1) / per;
                 if (ns > ATTN_COMB_MAX) return fail(m, NV_ECAPACITY, "internal: too many attention splits");
-                const int per = (ctx + ns - 1) / ns;
                 if (nrb == 1) t->dg = DecGeom{1, c.seq, c.pos0, nr, ns, per};   // the same plan, by value
                 for (int h = 0; h < m->H; ++h)
                     for (int s2 = 0; s2 < ns; ++s2) {
@@ -2085,6 +2094,7 @@ nv_status nv_debug_hidden(nv_model* m, int32_t seq, int32_t pos0, int32_t n, flo
 
 nv_status nv_timing_enable(nv_model* m, int32_t on) {
     if (!m) return NV_EINVAL;
+    if (on < 0 || on > 2) return fail(m, NV_EINVAL, "timing mode must be 0, 1 or 2");
     if (m->dead) return fail(m, NV_EDEVICE, "model handle unusable after a device error");
     NV_HIP(m, hipStreamSynchronize(m->st));
     if (on && m->ev.empty()) {
@@ -2114,6 +2124,7 @@ nv_status nv_timing_enable(nv_model* m, int32_t on) {
         m->t_n[k] = 0;
     }
     m->timing = on != 0;
+    m->timing_stamps = on == 2;
     return NV_OK;
 }
 
@@ -2136,8 +2147,8 @@ nv_status nv_timing_kernels(nv_model* m, char* out, size_t cap) {
     std::string txt;
     char line[512];
     for (const auto& ks : m->kstats) {
-        snprintf(line, sizeof(line), "%d\t%lld\t%.6f\t%.0f\t%s\n", ks.kind, (long long)ks.n, ks.ms, ks.bytes,
-                 ks.name.c_str());
+        snprintf(line, sizeof(line), "%d\t%lld\t%.6f\t%.0f\t%.6f\t%s\n", ks.kind, (long long)ks.n, ks.ms, ks.bytes,
+                 ks.n_span == ks.n ? ks.span_ms : -1.0, ks.name.c_str());
         txt += line;
     }
     if (txt.size() + 1 > cap) return fail(m, NV_ECAPACITY, "timing report buffer too small");

@@ -13,7 +13,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libnvium.so")
+# NVIUM_LIBRARY names another build of the same library (for example one built with host
+# sanitizers); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("NVIUM_LIBRARY") or os.path.join(HERE, "libnvium.so")
 
 NV_OK, NV_EINVAL, NV_ESTATE, NV_ECAPACITY, NV_EIO, NV_EDEVICE = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "NV_OK", -1: "NV_EINVAL", -2: "NV_ESTATE", -3: "NV_ECAPACITY", -4: "NV_EIO",
@@ -297,8 +299,9 @@ def nv_debug_hidden(h: Handle, seq: int, pos0: int, n: int) -> np.ndarray:
     return out
 
 
-def nv_timing_enable(h: Handle, on: bool = True) -> None:
-    _check(h.ptr, library().nv_timing_enable(h.ptr, 1 if on else 0))
+def nv_timing_enable(h: Handle, on=True) -> None:
+    """on: False/0 stop, True/1 events, 2 events and per-block device stamps."""
+    _check(h.ptr, library().nv_timing_enable(h.ptr, int(on)))
 
 
 def nv_timing_read(h: Handle) -> dict:
@@ -312,11 +315,13 @@ def nv_timing_read(h: Handle) -> dict:
 
 
 def nv_timing_kernels(h: Handle) -> list:
-    """[(class, launches, device ms, algorithmic bytes, symbol)] since nv_timing_enable."""
+    """[(class, launches, device ms, algorithmic bytes, symbol, span ms or None)] since
+    nv_timing_enable; device ms is launch to completion (HIP events), span ms the first
+    block start to last block end (device stamps) of the kernels that record them."""
     buf = ctypes.create_string_buffer(1 << 16)
     _check(h.ptr, library().nv_timing_kernels(h.ptr, buf, len(buf)))
     out = []
     for line in buf.value.decode().splitlines():
-        k, n, ms, by, name = line.split("\t", 4)
-        out.append((TIME_CLASSES[int(k)], int(n), float(ms), float(by), name))
+        k, n, ms, by, span, name = line.split("\t", 5)
+        out.append((TIME_CLASSES[int(k)], int(n), float(ms), float(by), name, float(span) if float(span) >= 0 else None))
     return out
