@@ -34,6 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TIMING_NOTE = ("avg_launch_us: hipExtLaunchKernelGGL start/stop events on each launch on the model's stream, "
+               "in an untimed pass identical to the timed one (launch to completion, as a rocprofv3 kernel "
+               "trace counts it); avg_span_us: first block start to last block end from device clock stamps, "
+               "in a second untimed pass of its own")
 # exit masses the workloads state (the gate biases are calibrated to give them)
 STATED_MASS = {"A": (0.4, 0.25, 0.2, 0.15), "C": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1),
                "E": (0.4, 0.25, 0.2, 0.15)}
@@ -101,18 +105,35 @@ def run_decode(lib, h, prompt, U, steps, warmup):
     return time.perf_counter() - t0, exits
 
 
-def timing_pass(lib, h, prompt, U, steps):
-    """The same decode again with per-launch device timing: the stream is drained
-    before each launch, and the launch is timed by per-block wall-clock stamps (or HIP
-    events for kernels without stamps) on the work stream."""
-    lib.nv_prefill(h, 0, prompt)
-    lib.nv_timing_enable(h, True)
-    for t in range(steps):
-        lib.nv_step(h, U[t:t + 1])
-    res = lib.nv_timing_read(h)
+def two_pass_timing(lib, h, setup, work):
+    """Per-launch device timing of `work` (after `setup`) in two untimed passes: HIP events
+    only, then per-block device clock stamps as well (the small kernel that folds each
+    launch's stamps perturbs the events, so the spans come from a pass of their own).
+    Returns the events pass's class totals and its per-kernel rows, each with the stamp
+    pass's summed span (ms) of the same symbol in place of its own."""
+    setup()
+    lib.nv_timing_enable(h, 1)
+    work()
+    tim = lib.nv_timing_read(h)
     ker = lib.nv_timing_kernels(h)
-    lib.nv_timing_enable(h, False)
-    return res, ker
+    setup()
+    lib.nv_timing_enable(h, 2)
+    work()
+    spans = {(k[0], k[4]): (k[1], k[5]) for k in lib.nv_timing_kernels(h)}
+    lib.nv_timing_enable(h, 0)
+    rows = []
+    for k in ker:
+        n2, span = spans.get((k[0], k[4]), (0, None))
+        rows.append(k[:5] + (span * k[1] / n2 if span is not None and n2 else None,))
+    return tim, rows
+
+
+def timing_pass(lib, h, prompt, U, steps):
+    """The same decode again with per-launch device timing (events, then stamps)."""
+    def work():
+        for t in range(steps):
+            lib.nv_step(h, U[t:t + 1])
+    return two_pass_timing(lib, h, lambda: lib.nv_prefill(h, 0, prompt), work)
 
 
 def cpu_baseline(wl, path, prompt, U, budget_s):
@@ -180,11 +201,7 @@ def bench_loss(args, wl):
         L = lib.nv_mixture_loss(h, 0, tokens, 0.5)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    lib.nv_timing_enable(h, True)
-    lib.nv_mixture_loss(h, 0, tokens, 0.5)
-    tim = lib.nv_timing_read(h)
-    ker = lib.nv_timing_kernels(h)
-    lib.nv_timing_enable(h, False)
+    tim, ker = two_pass_timing(lib, h, lambda: None, lambda: lib.nv_mixture_loss(h, 0, tokens, 0.5))
     lib.nv_free(h)
     m = wl.model
     d, F, Lr, V, r = m.d_model, m.ffn, m.n_layers, m.vocab, n - 1
@@ -193,7 +210,7 @@ def bench_loss(args, wl):
     # 2 SwiGLU = gate/up, 3 QKV), so each symbol's algorithmic FLOPs follow from it.
     per_epi = {1: 2.0 * r * Lr * (d * d + F * d), 2: 2.0 * r * Lr * 2 * F * d, 3: 2.0 * r * Lr * 3 * d * d}
     gemms = sorted([k for k in ker if k[0] == "block_gemm" and "k_gemm_bf16<" in k[4]], key=lambda k: -k[2])
-    _, nl, ms, by, kname = gemms[0]
+    _, nl, ms, by, kname, span = gemms[0]
     epi = int(kname.split("k_gemm_bf16<")[1].split(">")[0].split(",")[2]) if "k_gemm_bf16<" in kname else None
     assert epi in per_epi, f"dominant block GEMM {kname} is not the long-chunk kernel"
     flops = per_epi[epi]
@@ -290,12 +307,7 @@ def bench_batch(args, wl):
         lib.nv_step(h, Ut[:, t, :])
     torch.cuda.synchronize()
     dt_s = time.perf_counter() - t0
-    prefill_all(h)
-    lib.nv_timing_enable(h, True)
-    lib.nv_generate(h, slots, Ut, lib.SCHED_GREEDY)
-    tim = lib.nv_timing_read(h)
-    ker = lib.nv_timing_kernels(h)
-    lib.nv_timing_enable(h, False)
+    tim, ker = two_pass_timing(lib, h, lambda: prefill_all(h), lambda: lib.nv_generate(h, slots, Ut, lib.SCHED_GREEDY))
     lib.nv_free(h)
     base = None
     if not args.no_baseline:
@@ -306,7 +318,7 @@ def bench_batch(args, wl):
         base = B * steps / dt4
     tok_s = B * steps / dt_g
     gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
-    _, nl, ms, by, kname = gemms[0]
+    _, nl, ms, by, kname, span = gemms[0]
     achieved = by / (ms * 1e-3) / 1e9
     counted = counted_traffic(kname)
     top = sorted(ker, key=lambda k: -k[2])[:8]
@@ -332,7 +344,8 @@ def bench_batch(args, wl):
                      "traffic": counted[0] if counted else None,
                      "traffic_source": counted[1] if counted else None,
                      "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
-                     "bytes_per_launch": round(by / max(nl, 1))},
+                     "avg_span_us": round(span / max(nl, 1) * 1e3, 3) if span else None,
+                     "bytes_per_launch": round(by / max(nl, 1)), "timing": TIMING_NOTE},
         "lockstep_policy_tokens_per_s": round(B * steps / dt_l, 2),
         "nv_step_loop_tokens_per_s": round(B * steps / dt_s, 2),
         "greedy_vs_lockstep": round(dt_l / dt_g - 1.0, 4),
@@ -412,7 +425,7 @@ def main():
 
     # dominant kernel: the block-GEMM symbol with the most device time
     gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
-    _, nl, ms, by, kname = gemms[0]
+    _, nl, ms, by, kname, span = gemms[0]
     achieved = by / (ms * 1e-3) / 1e9
     counted = counted_traffic(kname)
     top = sorted(ker, key=lambda k: -k[2])[:8]
@@ -440,7 +453,8 @@ def main():
                      "traffic": counted[0] if counted else None,
                      "traffic_source": counted[1] if counted else None,
                      "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
-                     "bytes_per_launch": round(by / max(nl, 1))},
+                     "avg_span_us": round(span / max(nl, 1) * 1e3, 3) if span else None,
+                     "bytes_per_launch": round(by / max(nl, 1)), "timing": TIMING_NOTE},
         "block_gemm_all": {"achieved_GBps": round(tim["block_gemm"][1] / (tim["block_gemm"][0] * 1e-3) / 1e9, 1),
                            "launches": tim["block_gemm"][2]},
         "top_kernels": [{"kernel": k[4], "class": k[0], "launches": k[1],

@@ -250,10 +250,15 @@ nv_status nv_debug_hidden(nv_model *m, int32_t seq, int32_t pos0, int32_t n, flo
 #define NV_TIME_OTHER 3        /* embedding gather, router gates, sampling */
 #define NV_TIME_CLASSES 4
 
-/* on != 0: from now on bracket every kernel launch with HIP events on the model's
- * stream and accumulate per-class device time, launch counts and algorithmic bytes
- * (bytes each launch must move at minimum: weights read once, activations in/out,
- * keys/values read); on == 0: stop.  Either way the counters restart at zero. */
+/* on == 1: from now on bracket every kernel launch with HIP events on the model's
+ * stream (hipExtLaunchKernelGGL's start/stop events: launch to completion, as a
+ * profiler's kernel trace counts it) and accumulate per-class device time, launch counts
+ * and algorithmic bytes (bytes each launch must move at minimum: weights read once,
+ * activations in/out, keys/values read).  on == 2: the same, and the decode products and
+ * attention kernels also record per-block device clock stamps (first block start to last
+ * block end), folded by one small kernel after each launch, which perturbs the event
+ * durations; take events and spans from separate passes.  on == 0: stop.  Either way the
+ * counters restart at zero.  Other values: NV_EINVAL. */
 nv_status nv_timing_enable(nv_model *m, int32_t on);
 
 /* Totals since nv_timing_enable: ms[k] device milliseconds, bytes[k] algorithmic
@@ -261,8 +266,9 @@ nv_status nv_timing_enable(nv_model *m, int32_t on);
 nv_status nv_timing_read(nv_model *m, double *ms, double *bytes, int64_t *launches);
 
 /* The same totals per kernel symbol, as text: one line per kernel,
- * "class<TAB>launches<TAB>device ms<TAB>algorithmic bytes<TAB>symbol\n" (symbols as
- * profilers print them).  NV_ECAPACITY if `cap` bytes cannot hold it. */
+ * "class<TAB>launches<TAB>device ms<TAB>algorithmic bytes<TAB>span ms<TAB>symbol\n"
+ * (device ms from the events; span ms the summed stamp spans, -1 for kernels without
+ * stamps; symbols as profilers print them).  NV_ECAPACITY if `cap` bytes cannot hold it. */
 nv_status nv_timing_kernels(nv_model *m, char *out, size_t cap);
 
 #ifdef __cplusplus
