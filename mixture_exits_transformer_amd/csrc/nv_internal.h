@@ -164,9 +164,18 @@ static_assert(ATTN_DEC_ROWS <= 16, "a decode row block fits one 16-row wave of t
 // context: fewer, longer splits with more loads in flight per wave)
 constexpr int ATTN_DEC_ITERS = 8;
 constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds
+// Long contexts (row blocks of at most ATTN_DEC_WIDE_ROWS rows, some context past
+// ATTN_DEC_WIDE_MIN_KEYS keys, bf16 K/V): blocks of ATTN_DEC_WIDE_WAVES waves, a split covering
+// up to 16 x 8 x (64 / (head_dim / 8)) keys (512 at head_dim 128), at most one block per CU.
+// An 8K context then takes about 21 splits per head at 12 heads instead of 65, so the one-row O
+// product merges them as it loads (no combine launch), and every CU streams one long range.
+constexpr int ATTN_DEC_WIDE_WAVES = 16;
+constexpr int ATTN_DEC_WIDE_ROWS = 2;
+constexpr int ATTN_DEC_WIDE_MIN_KEYS = 4096;
+// wide: use the ATTN_DEC_WIDE_WAVES-wave blocks (bf16 K/V, max_rows <= ATTN_DEC_WIDE_ROWS)
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o,
-                           float* out, hipStream_t st, const DecGeom& dg = DecGeom{});
+                           float* out, hipStream_t st, const DecGeom& dg = DecGeom{}, int wide = 0);
 // Matrix-core variant of launch_attn for a bf16 KV cache and head_dim 32, 64 or 128:
 // items of up to 64 rows, key ranges starting at multiples of 64.
 bool attn_mfma_ok(const LayerDims& D);

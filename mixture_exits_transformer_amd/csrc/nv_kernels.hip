@@ -2273,16 +2273,17 @@ __device__ __forceinline__ void sm_merge(float& m, float& l, float* o, float m2,
     m = M;
 }
 
-template <int HD, bool KVBF, int RM>
-__global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const RowInfo* rows, const float* q,
-                                                  const void* kv, int layer, LayerDims D, float* part_ml,
-                                                  float* part_o, float* out, unsigned long long* stamp, DecGeom dg) {
+template <int HD, bool KVBF, int RM, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_dec(const AttnItem* items, const RowInfo* rows, const float* q,
+                                                      const void* kv, int layer, LayerDims D, float* part_ml,
+                                                      float* part_o, float* out, unsigned long long* stamp,
+                                                      DecGeom dg) {
     const unsigned long long t_begin = stamp_begin(stamp);
     constexpr int DPL = 8;
     constexpr int LPK = HD / DPL;       // lanes per key
     constexpr int KPI = 64 / LPK;       // keys per wave instruction
-    constexpr int NIT = ATTN_DEC_ITERS; // key groups per wave: a split holds at most 4 * KPI * NIT keys
-    __shared__ float red[4][RM][HD + 2];
+    constexpr int NIT = ATTN_DEC_ITERS; // key groups per wave: a split holds at most NW * KPI * NIT keys
+    __shared__ float red[NW][RM][HD + 2];
     const AttnItem it = dg.on ? dec_item(dg, blockIdx.x) : items[blockIdx.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / LPK, dl = lane - g * LPK;
@@ -2311,7 +2312,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
     for (int i = 0; i < NIT; ++i) {
         // keys past the range load the last key (masked below): every load is unconditional,
         // so all are issued back to back and waited for in order
-        const int key = min(it.lo + (i * 4 + wave) * KPI + g, it.hi - 1);
+        const int key = min(it.lo + (i * NW + wave) * KPI + g, it.hi - 1);
         if constexpr (KVBF) {
             kr[i] = *(const uint4*)((const uint16_t*)kv + kb + (int64_t)key * HD);
             vr[i] = *(const uint4*)((const uint16_t*)kv + vb + (int64_t)key * HD);
@@ -2324,7 +2325,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
     if constexpr (!KVBF) {
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            const int key = min(it.lo + (i * 4 + wave) * KPI + g, it.hi - 1);
+            const int key = min(it.lo + (i * NW + wave) * KPI + g, it.hi - 1);
             kr2[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD + 4);
             vr2[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD + 4);
         }
@@ -2352,8 +2353,8 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
     }
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {
-        const int key = it.lo + (i * 4 + wave) * KPI + g;
-        if (it.lo + (i * 4 + wave) * KPI >= it.hi) break;      // wave-uniform
+        const int key = it.lo + (i * NW + wave) * KPI + g;
+        if (it.lo + (i * NW + wave) * KPI >= it.hi) break;     // wave-uniform
         const bool kin = key < it.hi;
         float kf[DPL], vf[DPL];
         if constexpr (KVBF) {
@@ -2419,10 +2420,10 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
     for (int idx = threadIdx.x; idx < nr * HD; idx += blockDim.x) {
         const int r = idx / HD, e = idx - r * HD;
         float M = -INFINITY;
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][r][0]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w][r][0]);
         float L = 0.f, O = 0.f;
         if (M != -INFINITY) {
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 const float a = expf(red[w][r][0] - M);
                 L += a * red[w][r][1];
                 O += a * red[w][r][2 + e];
@@ -2445,20 +2446,35 @@ __global__ __launch_bounds__(256) void k_attn_dec(const AttnItem* items, const R
 
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o, float* out,
-                           hipStream_t st, const DecGeom& dg) {
+                           hipStream_t st, const DecGeom& dg, int wide) {
     if (n_items <= 0) return hipSuccess;
     if (dg.on && (dg.nrows < 1 || dg.nrows > ATTN_DEC_ROWS || dg.nrows > max_rows || n_items != D.H * dg.nsplit))
         return hipErrorInvalidValue;
-#define NV_DEC(HDV, BF, RMV)                                                                                  \
-    NV_LAUNCH(HIP_KERNEL_NAME(k_attn_dec<HDV, BF, RMV>), dim3(n_items), dim3(256), 0, st, items, rows, q, \
-                       kv, layer, D, part_ml, part_o, out, t_stamp, dg)
+    if (wide && (!D.kv_bf16 || max_rows > ATTN_DEC_WIDE_ROWS)) return hipErrorInvalidValue;
+#define NV_DEC(HDV, BF, RMV, NWV)                                                                             \
+    do {                                                                                                      \
+        NV_LAUNCH(HIP_KERNEL_NAME(k_attn_dec<HDV, BF, RMV, NWV>), dim3(n_items), dim3(64 * NWV), 0, st, items, \
+                  rows, q, kv, layer, D, part_ml, part_o, out, t_stamp, dg);                                  \
+        if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_attn_dec<%d, %s, %d, %d>", HDV,               \
+                                BF ? "true" : "false", RMV, NWV);                                             \
+    } while (0)
 #define NV_DEC_R(HDV, BF)                                                                                     \
     do {                                                                                                     \
-        if (max_rows <= 1) NV_DEC(HDV, BF, 1);                                                               \
-        else if (max_rows <= 2) NV_DEC(HDV, BF, 2);                                                          \
-        else if (max_rows <= 4) NV_DEC(HDV, BF, 4);                                                          \
-        else NV_DEC(HDV, BF, 8);                                                                             \
+        if (max_rows <= 1) NV_DEC(HDV, BF, 1, 4);                                                            \
+        else if (max_rows <= 2) NV_DEC(HDV, BF, 2, 4);                                                       \
+        else if (max_rows <= 4) NV_DEC(HDV, BF, 4, 4);                                                       \
+        else NV_DEC(HDV, BF, 8, 4);                                                                          \
     } while (0)
+    if (wide) {
+        if (D.hd == 128) {
+            if (max_rows <= 1) NV_DEC(128, true, 1, ATTN_DEC_WIDE_WAVES); else NV_DEC(128, true, 2, ATTN_DEC_WIDE_WAVES);
+        } else if (D.hd == 64) {
+            if (max_rows <= 1) NV_DEC(64, true, 1, ATTN_DEC_WIDE_WAVES); else NV_DEC(64, true, 2, ATTN_DEC_WIDE_WAVES);
+        } else {
+            if (max_rows <= 1) NV_DEC(32, true, 1, ATTN_DEC_WIDE_WAVES); else NV_DEC(32, true, 2, ATTN_DEC_WIDE_WAVES);
+        }
+        return hipGetLastError();
+    }
     if (D.hd == 128) {
         if (D.kv_bf16) NV_DEC_R(128, true); else NV_DEC_R(128, false);
     } else if (D.hd == 64) {

@@ -248,6 +248,7 @@ struct nv_model {
     // the 16-row matrix-core tiles, which leave half their rows empty at 5-8 rows
     // (batch-1 decode: 0.417 -> 0.411 ms per segment-token against a threshold of 5)
     int mfma_min_rows = 9;
+    int n_cu = 256;               // compute units of the device (decode attention grid sizing)
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
     // goes up in one copy.  step: [uniforms MB*4 f32][pending tokens MB i32][current rows MB]
@@ -500,6 +501,7 @@ struct Tables {
     bool on_device;    // the tables were uploaded (some kernel of this group reads them)
     bool dec;          // decode-sized group: attention combines its splits in-kernel
     int max_rows;      // most rows in one decode-attention row block
+    bool wide = false; // decode attention on ATTN_DEC_WIDE_WAVES-wave blocks (long contexts)
     bool any_split;    // some row's key range was split (the combine pass is needed)
     int max_split;     // most splits of one row's key range
     double kv_bytes;   // keys and values the attention items read
@@ -561,11 +563,21 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         // decode-sized group: row blocks of ATTN_DEC_ROWS rows; each block's key range is cut
         // into nsplit pieces (at least 64 keys each, about 512 blocks in all) whose partial
         // softmax states the combine pass merges
-        int nrb = 0;
-        for (const Chunk& c : chunks) nrb += (c.nrows + ATTN_DEC_ROWS - 1) / ATTN_DEC_ROWS;
-        const int want = std::max(1, (kAttnBlocksTarget + m->H * nrb - 1) / (m->H * nrb));
+        int nrb = 0, mx_nr = 0, mx_ctx = 0;
+        for (const Chunk& c : chunks) {
+            nrb += (c.nrows + ATTN_DEC_ROWS - 1) / ATTN_DEC_ROWS;
+            mx_nr = std::max(mx_nr, std::min(ATTN_DEC_ROWS, c.nrows));
+            mx_ctx = std::max(mx_ctx, c.pos0 + c.nrows);
+        }
+        // long contexts on bf16 K/V: blocks of ATTN_DEC_WIDE_WAVES waves with long splits, at
+        // most one block per CU (so the splits of a row stay few enough for the O product to
+        // merge them as it loads)
+        t->wide = m->bf16 && mx_nr <= ATTN_DEC_WIDE_ROWS && mx_ctx > ATTN_DEC_WIDE_MIN_KEYS;
+        const int nw = t->wide ? ATTN_DEC_WIDE_WAVES : 4;
+        const int want = t->wide ? std::max(1, m->n_cu / (m->H * nrb))
+                                 : std::max(1, (kAttnBlocksTarget + m->H * nrb - 1) / (m->H * nrb));
         // keys per split: at most what one block's waves hold in flight
-        const int max_keys = 4 * ATTN_DEC_ITERS * (64 / (m->hd / 8));
+        const int max_keys = nw * ATTN_DEC_ITERS * (64 / (m->hd / 8));
         int slot = 0, row0 = 0, rbi = 0;
         t->max_rows = 0;
         t->dg = DecGeom{};
@@ -760,8 +772,8 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
             else
                 NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                     return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
-                                           m->part_o, m->attn_o, m->st, t.dg);
-                }, "nv::k_attn_dec"));
+                                           m->part_o, m->attn_o, m->st, t.dg, t.wide ? 1 : 0);
+                }));
             // one row: the O projection merges the splits itself (no combine pass)
             if (t.any_split && !fuse_merge(m, t))
                 NV_TRY(timed(m, NV_TIME_ATTENTION, (double)t.R * d * 4, [&] {
@@ -1133,6 +1145,12 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     }
     m->arena = (char*)align_up((size_t)m->arena);
     NV_HIP(m, init_kernel_attributes());
+    {
+        int dev = 0, ncu = 0;
+        NV_HIP(m, hipGetDevice(&dev));
+        NV_HIP(m, hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+        if (ncu > 0) m->n_cu = ncu;
+    }
 
     // carve the arena
     m->embed = m->take(P.embed);

@@ -474,9 +474,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t) {
 
 hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, const RowInfo* rows, const float* q,
                            const void* kv, int layer, const LayerDims& D, float* part_ml, float* part_o, float* out,
-                           hipStream_t, const DecGeom& dg) {
+                           hipStream_t, const DecGeom& dg, int wide) {
     if (n_items <= 0) return hipSuccess;
     CHECK(q && kv && part_ml && part_o && out && max_rows >= 1 && max_rows <= ATTN_DEC_ROWS, "decode attention args");
+    CHECK(!wide || (D.kv_bf16 && max_rows <= ATTN_DEC_WIDE_ROWS), "wide decode attention on a group it does not take");
+    // a split holds at most the keys the block's waves load at once
+    const int max_keys = (wide ? ATTN_DEC_WIDE_WAVES : 4) * ATTN_DEC_ITERS * (64 / (D.hd / 8));
+    for (int b = 0; b < n_items; ++b) {
+        const AttnItem it = dg.on ? dec_item(dg, b) : items[b];
+        CHECK(it.hi - it.lo <= max_keys, "decode attention: item %d covers %d keys, a block holds %d", b, it.hi - it.lo,
+              max_keys);
+    }
     if (dg.on)
         CHECK(dg.nrows >= 1 && dg.nrows <= max_rows && n_items == D.H * dg.nsplit, "decode attention plan by value");
     else
