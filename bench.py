@@ -371,7 +371,7 @@ def bench_batch(args, wl):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="decode steps (default 512); loss passes (10)")
+    ap.add_argument("--steps", type=int, default=None, help="decode steps (default: the workload's, 512 for A); loss passes (10)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 16; loss passes 2)")
     ap.add_argument("--workload", default="A",
                     help="A, B, D, E (decode, batch 1), C (16 sequences) or L (mixture objective)")
@@ -401,7 +401,7 @@ def main():
         return bench_loss(args, wl)
     if wl.batch > 1:
         return bench_batch(args, wl)
-    steps = args.steps if args.steps is not None else 512
+    steps = args.steps if args.steps is not None else wl.decode_steps
     warmup = args.warmup if args.warmup is not None else 16
     prompt = prompts(wl)[0]
     U = uniforms(wl, steps=max(steps, warmup))[:, 0, :]

@@ -98,12 +98,20 @@ nv_status nv_get_config(const nv_model *m, nv_config *out);
 /* Start (or restart) sequence `seq` with prompt tokens[0..n-1], n >= 1.
  * Positions 0..n-2 run through every layer (building their KV); tokens[n-1]
  * becomes the pending input that the next nv_step consumes at position n-1.
+ * Source: a forward pass both builds every layer's K/V and predicts the next token
+ * (gist.science summary, section 1); the prompt has no token to exit, so it runs at
+ * full depth and leaves complete caches (section 2, part "Inferenz: Piggybacking").
  * Restarting drops the sequence's KV, deferred states and frontiers.
  * Errors: NV_EINVAL (seq out of range, NULL tokens, n < 1, token >= vocab),
  * NV_ECAPACITY (n > max_ctx), NV_EDEVICE. */
 nv_status nv_prefill(nv_model *m, int32_t seq, const int32_t *tokens, int32_t n);
 
 /* One decode step for every prefilled sequence 0..n_seq-1 in lock-step.
+ * Source: the mixture output and its stick-breaking weights (gist.science summary,
+ * section 2 "Methodik", part "Architektur", equations for p_k and pi_mix); drawing exactly
+ * from the mixture by walking the gates and sampling only the stopping exit (section 3,
+ * "Exakte Sampling-Mischung"; abstract); the layers a token skips run later with the next
+ * token that reaches them, as one causal chunk (section 2, part "Inferenz: Piggybacking").
  *   uniforms   [n_seq][4] float32 in [0,1): u[0..2] walk gates 1..3 (stop at gate
  *              k iff u[k-1] < w_k), u[3] draws the token by inverse CDF of the
  *              stopping exit's softmax in token-id order (smallest id i with
@@ -174,7 +182,11 @@ nv_status nv_mixture_loss(nv_model *m, int32_t seq, const int32_t *tokens, int32
 /* Run every deferred segment of sequence `seq` (-1: all prefilled sequences)
  * over all consumed positions, with no gates and no heads.  Afterwards every
  * layer's KV is complete for every consumed position.  A second flush is a
- * no-op.  Errors: NV_EINVAL (seq out of range), NV_EDEVICE. */
+ * no-op.  Source: the deferred rows are the ones piggybacking would fill with the next
+ * deeper token; running them at once gives the complete, exact cache the method promises
+ * (gist.science summary, section 2, part "Inferenz: Piggybacking", "Ergebnis"; section 3,
+ * "Vollständige KV-Wiederherstellung").
+ * Errors: NV_EINVAL (seq out of range), NV_EDEVICE. */
 nv_status nv_flush(nv_model *m, int32_t seq);
 
 /* ---- one exit's draw on caller buffers --------------------------------------- */
