@@ -25,9 +25,10 @@ With random-init weights the residual stream after a segment has norm ~85-180, s
 linear term g_k . h (g_k ~ N(0, 0.02^2)) of the 1.5B model has a standard deviation of
 1.2-1.7 and a nonzero mean, and sigmoid(b_k) alone does not give the stated masses.  The
 1.5B workloads therefore use calibrated biases: the b_k for which the mean of p_k over the
-oracle's hidden states at the positions the workload decodes (512-1022 for the 512-token
-prompt, 8192-8446 for the 8192-token prompt; the linear term drifts with the position)
-equals the stated mass (tests/golden/make_gate_bias.py writes them, with the samples, to
+oracle's hidden states at the positions the workload decodes (511-1022 after the 512-token
+prompt, 8191-8446 after the 8192-token one; the linear term drifts with the position and
+with the prompt, so the workload's own prompt comes first and seeded uniform-random tokens
+stand in for the drawn ones) equals the stated mass (tests/golden/make_gate_bias.py writes them, with the samples, to
 tests/golden/gate_bias_1p5b.json).  The tiny model's linear term is small, so it keeps the
 zero-linear-term biases.  Benchmarks report the realised exit histogram.
 """
@@ -43,10 +44,11 @@ NEG_INF = float("-inf")
 BIAS_MASS_40_25_20_15 = (math.log(0.4 / 0.6), math.log(5.0 / 7.0), math.log(4.0 / 3.0))
 # logit(0.6), logit(0.5), logit(0.5)
 BIAS_MASS_60_20_10_10 = (math.log(0.6 / 0.4), 0.0, 0.0)
-# 1.5B model, calibrated on the oracle's hidden states at the decode positions of the
-# 512-token-prompt workloads and of the 8192-token one (tests/golden/gate_bias_1p5b.json)
-BIAS_CAL_1P5B_40_25_20_15 = (0.0976212954690873, -2.588711943519958, -0.07199422712384851)
-BIAS_CAL_1P5B_60_20_10_10 = (0.483891979959988, 0.47204847976457054, -0.2500382543420189)
+# 1.5B model, calibrated on the oracle's hidden states at the decode positions of workload A
+# (also used by the other 512-token-prompt workloads and C) and of workload D
+# (tests/golden/gate_bias_1p5b.json)
+BIAS_CAL_1P5B_40_25_20_15 = (-0.7148283503446942, -2.054615047072935, 0.9033168998118104)
+BIAS_CAL_1P5B_60_20_10_10 = (-0.34100759331458186, -1.1546249822822858, -0.2721350662432206)
 # every intermediate gate closed: sigmoid(-inf) = 0
 BIAS_ALL_LAST = (NEG_INF, NEG_INF, NEG_INF)
 

@@ -7,13 +7,15 @@ exit k is the mean over tokens of p_k = w_k prod_{j<k} (1 - w_j), with w_k = sig
 h^(l_k) + b_k) (gist.science summary, section 2 "Methodik", part "Architektur": equation
 for p_k).  The linear term drifts with the position (gate 1's mean falls from about +1.2
 at positions 64-164 to -1.0 at 896-1023), so each workload is calibrated where it decodes.
-This script runs the oracle's float64 forward over a seeded calibration prompt of
-uniform-random tokens through the first three segments (the gates need no more), keeps
-z_k = g_k . h^(l_k) at the workload's decode positions, and solves, exit by exit, for the
-b_k whose sample mean of p_k equals the stated mass (p_k is increasing in b_k when the
-earlier biases are fixed; bisection in float64):
-  A (512-token prompt, 512 steps):    1024 tokens, default_rng(3), positions 512..1022
-  D (8192-token prompt, 256 steps):   8448 tokens, default_rng(4), positions 8192..8446
+This script runs the oracle's float64 forward over each workload's own prompt followed by
+its decode steps' worth of seeded uniform-random tokens (stand-ins for the drawn tokens,
+which random-init heads spread near-uniformly over the vocabulary), through the first three
+segments (the gates need no more); it keeps z_k = g_k . h^(l_k) at the positions the decode
+steps consume, and solves, exit by exit, for the b_k whose sample mean of p_k equals the
+stated mass (p_k is increasing in b_k when the earlier biases are fixed; bisection in
+float64):
+  A (512-token prompt, 512 steps):   positions 511..1022, continuation default_rng(3)
+  D (8192-token prompt, 256 steps):  positions 8191..8446, continuation default_rng(4)
 
     python tests/golden/make_gate_bias.py       # writes tests/golden/gate_bias_1p5b.json
 """
@@ -28,10 +30,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 from oracle import model as om                       # noqa: E402
-from synth import M15B, cached_weights              # noqa: E402
+from synth import M15B, cached_weights, prompts, workload   # noqa: E402
 
 MASSES = {"A": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1)}
-SAMPLES = {"A": (3, 1024, 512), "D": (4, 8448, 8192)}     # prompt seed, prompt length, first position
+SAMPLES = {"A": 3, "D": 4}     # seed of the continuation tokens
 
 
 def sig(x):
@@ -58,12 +60,10 @@ def solve_biases(z: np.ndarray, masses) -> list:
     return out
 
 
-def sample_z(M, seed: int, n_tokens: int, first_pos: int) -> np.ndarray:
-    """The gates' linear terms z_k = g_k . h^(l_k) (k < 3) at positions first_pos..n_tokens-2
-    of a uniform-random prompt, from the oracle's layers (a causal chunk per layer)."""
-    rng = np.random.default_rng(seed)
-    tokens = rng.integers(0, M.V, size=n_tokens)
-    n = n_tokens - 1
+def sample_z(M, tokens: np.ndarray, first_pos: int) -> np.ndarray:
+    """The gates' linear terms z_k = g_k . h^(l_k) (k < 3) at positions first_pos..len-2 of
+    `tokens`, from the oracle's layers (a causal chunk per layer)."""
+    n = len(tokens) - 1
     kv = om.KVCache(M, n)
     pos = np.arange(n)
     X = np.asarray(M.embed[tokens[:n]], dtype=np.float64)
@@ -73,7 +73,7 @@ def sample_z(M, seed: int, n_tokens: int, first_pos: int) -> np.ndarray:
         for k in range(3):
             if l + 1 == M.exit_layers[k]:
                 z[:, k] = X @ M.gate_w[k]
-        print(f"seed {seed}: layer {l + 1}/{M.exit_layers[2]}", flush=True)
+        print(f"{len(tokens)} tokens: layer {l + 1}/{M.exit_layers[2]}", flush=True)
     return z[first_pos:]
 
 
@@ -81,11 +81,18 @@ def main():
     path = cached_weights(M15B)
     M = om.OracleModel(path)
     res = {"source": "tests/golden/make_gate_bias.py (oracle float64 forward, 1.5B model, seed-0 weights)"}
-    for name, (seed, n_tokens, first) in SAMPLES.items():
-        zs = sample_z(M, seed, n_tokens, first)
+    for name, seed in SAMPLES.items():
+        wl = workload(name)
+        prompt = prompts(wl)[0].astype(np.int64)
+        cont = np.random.default_rng(seed).integers(0, M.V, size=wl.decode_steps)
+        tokens = np.concatenate([prompt, cont])
+        first = len(prompt) - 1
+        zs = sample_z(M, tokens, first)
+        assert len(zs) == wl.decode_steps
         b = solve_biases(zs, MASSES[name])
-        res[name] = {"prompt": f"{n_tokens} uniform-random tokens, numpy default_rng({seed})",
-                     "positions": [first, n_tokens - 2], "mass": list(MASSES[name]), "bias": b,
+        res[name] = {"prompt": f"workload {name}'s prompt ({len(prompt)} tokens), then {wl.decode_steps} "
+                               f"uniform-random tokens, numpy default_rng({seed})",
+                     "positions": [first, first + wl.decode_steps - 1], "mass": list(MASSES[name]), "bias": b,
                      "z_mean": [float(np.mean(zs[:, k])) for k in range(3)],
                      "z_std": [float(np.std(zs[:, k])) for k in range(3)],
                      "z": [[round(float(v), 9) for v in row] for row in zs]}

@@ -1,7 +1,7 @@
 """The calibrated gate biases of the 1.5B workloads reproduce the stated exit masses on
 the calibration samples that tests/golden/make_gate_bias.py stored (the oracle's linear
-terms z_k = g_k . h^(l_k) at the positions each workload decodes: 512..1022 for the
-512-token prompt, 8192..8446 for the 8192-token prompt): the mean over positions of the
+terms z_k = g_k . h^(l_k) at the positions each workload's decode steps consume: 511..1022
+after A's 512-token prompt, 8191..8446 after D's 8192-token prompt): the mean over positions of the
 stick-breaking p_k (gist.science summary, section 2 "Methodik", part "Architektur":
 equation for p_k) with w_k = sigmoid(z_k + b_k) equals the stated mass.  The biases the
 workloads carry are the stored ones."""
@@ -29,7 +29,7 @@ def _masses(z, b):
 
 def test_calibrated_biases_give_stated_masses():
     g = json.load(open(GOLDEN))
-    for name, b_cfg, n in (("A", BIAS_CAL_1P5B_40_25_20_15, 511), ("D", BIAS_CAL_1P5B_60_20_10_10, 255)):
+    for name, b_cfg, n in (("A", BIAS_CAL_1P5B_40_25_20_15, 512), ("D", BIAS_CAL_1P5B_60_20_10_10, 256)):
         z = np.asarray(g[name]["z"])
         assert z.shape == (n, 3)
         assert np.allclose(g[name]["bias"], b_cfg, rtol=0, atol=1e-12)
