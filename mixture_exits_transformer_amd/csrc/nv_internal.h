@@ -236,6 +236,8 @@ hipError_t init_kernel_attributes();
 // end, until cleared with (nullptr, nullptr).
 void set_launch_events(hipEvent_t start, hipEvent_t stop);
 const char* last_launch_name();   // symbol of the last kernel issued while timing
+int take_launch_blocks();          // most blocks of a launch since the last call (then 0)
+void note_launch_blocks(int n);    // a launch issued outside the wrappers' macro had n blocks
 // Timing: block-stamp buffer the next stamped kernels write (nullptr: none).
 void set_launch_stamp(unsigned long long* stamps);
 constexpr int STAMP_BLOCKS = 65536;  // largest grid the timing stamps cover

@@ -37,10 +37,26 @@ static thread_local char t_name[160];
 
 const char* last_launch_name() { return t_name; }
 
+// Most blocks of any launch since the last take_launch_blocks() (the stamp entries written).
+static thread_local int t_blocks = 0;
 
+int take_launch_blocks() {
+    const int n = t_blocks;
+    t_blocks = 0;
+    return n;
+}
+
+void note_launch_blocks(int n) {
+    if (n > t_blocks) t_blocks = n;
+}
 
 #define NV_LAUNCH(K, G, B, SHM, ST, ...)                                                     \
     do {                                                                                     \
+        {                                                                                    \
+            const dim3 g_ = (G);                                                             \
+            const int nb_ = (int)(g_.x * g_.y * g_.z);                                       \
+            if (nb_ > t_blocks) t_blocks = nb_;                                              \
+        }                                                                                    \
         if (t_ev_stop) {                                                                     \
             hipExtLaunchKernelGGL((K), G, B, SHM, ST, t_ev_start, t_ev_stop, 0, __VA_ARGS__);  \
             t_ev_start = nullptr;                                                            \
@@ -166,8 +182,8 @@ __device__ __forceinline__ void epi_pair(const GemmArgs& a, int row, int n, floa
 
 // (first start, last end) over the block stamps of one launch into rec[0..1]; the stamp
 // slots are reset to (max, 0) for the next launch.
-__global__ __launch_bounds__(256) void k_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec) {
-    __shared__ unsigned long long lo[256], hi[256];
+__global__ __launch_bounds__(1024) void k_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec) {
+    __shared__ unsigned long long lo[1024], hi[1024];
     unsigned long long a = ~0ull, b = 0ull;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         a = min(a, stamps[2 * i]);
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(256) void k_stamp_reduce(unsigned long long* stamps
     lo[threadIdx.x] = a;
     hi[threadIdx.x] = b;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
+    for (int s = 512; s > 0; s >>= 1) {
         if ((int)threadIdx.x < s) {
             lo[threadIdx.x] = min(lo[threadIdx.x], lo[threadIdx.x + s]);
             hi[threadIdx.x] = max(hi[threadIdx.x], hi[threadIdx.x + s]);
@@ -192,7 +208,7 @@ __global__ __launch_bounds__(256) void k_stamp_reduce(unsigned long long* stamps
 }
 
 hipError_t launch_stamp_reduce(unsigned long long* stamps, int n, unsigned long long* rec, hipStream_t st) {
-    hipLaunchKernelGGL(k_stamp_reduce, dim3(1), dim3(256), 0, st, stamps, n, rec);
+    hipLaunchKernelGGL(k_stamp_reduce, dim3(1), dim3(1024), 0, st, stamps, n, rec);
     return hipGetLastError();
 }
 

@@ -433,12 +433,15 @@ nv_status timed(nv_model* m, int kind, double bytes, F&& launch, const char* nam
     // kernels that support stamps use them; others leave (max, 0)
     m->ev_stamped[i] = m->timing_stamps ? 1 : 0;
     if (m->timing_stamps) set_launch_stamp(m->d_blkstamps);
+    (void)take_launch_blocks();
     set_launch_events(m->ev[2 * i], m->ev[2 * i + 1]);
     const hipError_t le = launch();
     set_launch_events(nullptr, nullptr);
     set_launch_stamp(nullptr);
     NV_HIP(m, le);
-    if (m->timing_stamps) NV_HIP(m, launch_stamp_reduce(m->d_blkstamps, STAMP_BLOCKS, m->d_stamps + 2 * i, m->st));
+    // fold (and reset) only the stamp entries this launch's blocks wrote
+    const int nb = std::min(STAMP_BLOCKS, std::max(1, take_launch_blocks()));
+    if (m->timing_stamps) NV_HIP(m, launch_stamp_reduce(m->d_blkstamps, nb, m->d_stamps + 2 * i, m->st));
     m->ev_kind[i] = kind;
     m->ev_bytes[i] = bytes;
     m->ev_name[i] = name ? name : last_launch_name();

@@ -609,6 +609,7 @@ hipError_t launch_segment(const SegArgs& a, int blocks, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     void* args[] = {&b};
+    note_launch_blocks(blocks);
     hipError_t e = hipLaunchCooperativeKernel((const void*)k_segment, dim3(blocks), dim3(SEG_THREADS), args, 0, st);
     if (e != hipSuccess) return e;
     if (e1) e = hipEventRecord(e1, st);

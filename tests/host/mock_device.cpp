@@ -348,6 +348,8 @@ void current_launch_events(hipEvent_t* start, hipEvent_t* stop) {
     *stop = g_mock.ev1;
 }
 const char* last_launch_name() { return "mock kernel"; }
+int take_launch_blocks() { return 1; }
+void note_launch_blocks(int) {}
 void set_launch_stamp(unsigned long long* stamps) { g_mock.stamp = stamps; }
 unsigned long long* current_launch_stamp() { return g_mock.stamp; }
 
