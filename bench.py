@@ -423,8 +423,9 @@ def main():
         assert set(ex4) == {4}
         base = steps / dt4
 
-    # dominant kernel: the block-GEMM symbol with the most device time
-    gemms = sorted([k for k in ker if k[0] == "block_gemm"], key=lambda k: -k[2])
+    # dominant kernel: the block-GEMM or attention symbol with the most device time (the
+    # one-row gate/up product at a 512-token prompt, the decode attention at 8192)
+    gemms = sorted([k for k in ker if k[0] in ("block_gemm", "attention")], key=lambda k: -k[2])
     _, nl, ms, by, kname, span = gemms[0]
     achieved = by / (ms * 1e-3) / 1e9
     counted = counted_traffic(kname)

@@ -166,9 +166,9 @@ constexpr int ATTN_DEC_ITERS = 8;
 constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds
 // Long contexts (row blocks of at most ATTN_DEC_WIDE_ROWS rows, some context past
 // ATTN_DEC_WIDE_MIN_KEYS keys, bf16 K/V): blocks of ATTN_DEC_WIDE_WAVES waves, a split covering
-// up to 16 x 8 x (64 / (head_dim / 8)) keys (512 at head_dim 128), at most one block per CU.
-// An 8K context then takes about 21 splits per head at 12 heads instead of 65, so the one-row O
-// product merges them as it loads (no combine launch), and every CU streams one long range.
+// up to 16 x 8 x (64 / (head_dim / 8)) keys (512 at head_dim 128), one block per CU on about
+// 3/4 of the CUs.  An 8K context then takes 17 splits per head at 12 heads instead of 65, so
+// the one-row O product merges them as it loads (no combine launch).
 constexpr int ATTN_DEC_WIDE_WAVES = 16;
 constexpr int ATTN_DEC_WIDE_ROWS = 2;
 constexpr int ATTN_DEC_WIDE_MIN_KEYS = 4096;

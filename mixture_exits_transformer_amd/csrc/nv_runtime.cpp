@@ -577,7 +577,9 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         // merge them as it loads)
         t->wide = m->bf16 && mx_nr <= ATTN_DEC_WIDE_ROWS && mx_ctx > ATTN_DEC_WIDE_MIN_KEYS;
         const int nw = t->wide ? ATTN_DEC_WIDE_WAVES : 4;
-        const int want = t->wide ? std::max(1, m->n_cu / (m->H * nrb))
+        // (wide: about 3/4 of the CUs; the attention takes as long on 192 blocks as on 252 at
+        // an 8K context, and the O product merges fewer splits: D -1.4 % per step)
+        const int want = t->wide ? std::max(1, (m->n_cu * 3 / 4) / (m->H * nrb))
                                  : std::max(1, (kAttnBlocksTarget + m->H * nrb - 1) / (m->H * nrb));
         // keys per split: at most what one block's waves hold in flight
         const int max_keys = nw * ATTN_DEC_ITERS * (64 / (m->hd / 8));
@@ -771,7 +773,7 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
                 NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                     return launch_attn_mfma16(t.items, t.n_items, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
                                               m->part_o, m->attn_o, m->st, t.dg);
-                }, "nv::k_attn_mfma (decode items)"));
+                }));
             else
                 NV_TRY(timed(m, NV_TIME_ATTENTION, t.kv_bytes + (double)t.R * d * 8, [&] {
                     return launch_attn_dec(t.items, t.n_items, t.max_rows, t.rows, m->qbuf, m->kv, l, D, m->part_ml,
