@@ -36,8 +36,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 TIMING_NOTE = ("avg_launch_us: hipExtLaunchKernelGGL start/stop events on each launch on the model's stream, "
                "in an untimed pass identical to the timed one (launch to completion, as a rocprofv3 kernel "
-               "trace counts it); avg_span_us: first block start to last block end from device clock stamps, "
-               "in a second untimed pass of its own")
+               "trace counts it); avg_span_us (with --spans): first block start to last block end from device "
+               "clock stamps, in a further untimed pass of its own")
 # exit masses the workloads state (the gate biases are calibrated to give them)
 STATED_MASS = {"A": (0.4, 0.25, 0.2, 0.15), "C": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1),
                "E": (0.4, 0.25, 0.2, 0.15)}
@@ -105,17 +105,23 @@ def run_decode(lib, h, prompt, U, steps, warmup):
     return time.perf_counter() - t0, exits
 
 
+SPANS = False      # --spans: also run the stamp pass
+
+
 def two_pass_timing(lib, h, setup, work):
-    """Per-launch device timing of `work` (after `setup`) in two untimed passes: HIP events
-    only, then per-block device clock stamps as well (the small kernel that folds each
-    launch's stamps perturbs the events, so the spans come from a pass of their own).
-    Returns the events pass's class totals and its per-kernel rows, each with the stamp
-    pass's summed span (ms) of the same symbol in place of its own."""
+    """Per-launch device timing of `work` (after `setup`) in an untimed pass with HIP events
+    only; with --spans, a second pass with per-block device clock stamps as well (the small
+    kernel that folds each launch's stamps perturbs the events, so the spans come from a
+    pass of their own).  Returns the events pass's class totals and its per-kernel rows,
+    each with the stamp pass's summed span (ms) of the same symbol, or None."""
     setup()
     lib.nv_timing_enable(h, 1)
     work()
     tim = lib.nv_timing_read(h)
     ker = lib.nv_timing_kernels(h)
+    if not SPANS:
+        lib.nv_timing_enable(h, 0)
+        return tim, [k[:5] + (None,) for k in ker]
     setup()
     lib.nv_timing_enable(h, 2)
     work()
@@ -379,9 +385,13 @@ def main():
     ap.add_argument("--no-baseline", action="store_true", help="skip the exit-4-forced run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--spans", action="store_true",
+                    help="also time first block start to last block end (device stamps) in a pass of its own")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    global SPANS
+    SPANS = args.spans
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path "
               f"runs on a single GPU", file=sys.stderr)
