@@ -25,6 +25,7 @@ roofline of the dominant block GEMM against the bf16 matrix-core peak.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -88,6 +89,19 @@ def calibration_copy(out):
     out["calibration_copy_bytes"] = 1 << 30
 
 
+class paused_gc:
+    """Timed regions run with Python's cyclic garbage collector paused (after a collection):
+    one full collection in an interpreter that holds torch takes about 40 ms, and it landed
+    inside one of the 512 timed decode steps (8 % of the run)."""
+
+    def __enter__(self):
+        gc.collect()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        gc.enable()
+
+
 def run_decode(lib, h, prompt, U, steps, warmup):
     """Warm up, restart the sequence, then time `steps` decode steps."""
     import torch
@@ -96,13 +110,15 @@ def run_decode(lib, h, prompt, U, steps, warmup):
         lib.nv_step(h, U[t:t + 1])
     lib.nv_prefill(h, 0, prompt)
     exits = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(steps):
-        _, ex = lib.nv_step(h, U[t:t + 1])
-        exits.append(int(ex[0]))
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0, exits
+    with paused_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            _, ex = lib.nv_step(h, U[t:t + 1])
+            exits.append(int(ex[0]))
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+    return dt, exits
 
 
 SPANS = False      # --spans: also run the stamp pass
@@ -201,12 +217,13 @@ def bench_loss(args, wl):
     h = lib.nv_load(path, 1, n)
     for _ in range(warmup):
         lib.nv_mixture_loss(h, 0, tokens, 0.5)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        L = lib.nv_mixture_loss(h, 0, tokens, 0.5)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    with paused_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            L = lib.nv_mixture_loss(h, 0, tokens, 0.5)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
     tim, ker = two_pass_timing(lib, h, lambda: None, lambda: lib.nv_mixture_loss(h, 0, tokens, 0.5))
     lib.nv_free(h)
     m = wl.model
@@ -297,22 +314,25 @@ def bench_batch(args, wl):
         if warmup:
             lib.nv_generate(h, slots, Uw, policy)
         prefill_all(h)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        toks, exs = lib.nv_generate(h, slots, Ut, policy)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, exs
+        with paused_gc():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            toks, exs = lib.nv_generate(h, slots, Ut, policy)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+        return dt, exs
 
     h = lib.nv_load(path, B, max_ctx)
     dt_g, ex_g = timed_generate(h, lib.SCHED_GREEDY)
     dt_l, ex_l = timed_generate(h, lib.SCHED_LOCKSTEP)
     prefill_all(h)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(steps):
-        lib.nv_step(h, Ut[:, t, :])
-    torch.cuda.synchronize()
-    dt_s = time.perf_counter() - t0
+    with paused_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            lib.nv_step(h, Ut[:, t, :])
+        torch.cuda.synchronize()
+        dt_s = time.perf_counter() - t0
     tim, ker = two_pass_timing(lib, h, lambda: prefill_all(h), lambda: lib.nv_generate(h, slots, Ut, lib.SCHED_GREEDY))
     lib.nv_free(h)
     base = None
