@@ -103,25 +103,35 @@ class paused_gc:
 
 
 def run_decode(lib, h, prompt, U, steps, warmup):
-    """Warm up, restart the sequence, then time `steps` decode steps."""
+    """Warm up, restart the sequence, then time `steps` decode steps: once through
+    nv_generate (the library's decode loop: one call, draws read back through its ring of
+    pinned buffers) and once as a loop of nv_step calls from Python (one synchronous call
+    per token).  Both run the same computation and give the same tokens and exits.
+    Returns (generate seconds, nv_step-loop seconds, exits)."""
     import torch
     lib.nv_prefill(h, 0, prompt)
     for t in range(warmup):
         lib.nv_step(h, U[t:t + 1])
     lib.nv_prefill(h, 0, prompt)
-    exits = []
+    with paused_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, ex = lib.nv_generate(h, [0], U[None, :steps, :], lib.SCHED_GREEDY)
+        torch.cuda.synchronize()
+        dt_g = time.perf_counter() - t0
+    exits = [int(e) for e in ex.ravel()]
+    lib.nv_prefill(h, 0, prompt)
+    exits_s = []
     with paused_gc():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(steps):
-            _, ex = lib.nv_step(h, U[t:t + 1])
-            exits.append(int(ex[0]))
+            _, e = lib.nv_step(h, U[t:t + 1])
+            exits_s.append(int(e[0]))
         torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-    return dt, exits
-
-
-SPANS = False      # --spans: also run the stamp pass
+        dt_s = time.perf_counter() - t0
+    assert exits_s == exits, "nv_generate and the nv_step loop took different exits"
+    return dt_g, dt_s, exits
 
 
 def two_pass_timing(lib, h, setup, work):
@@ -439,19 +449,20 @@ def main():
 
     path = cached_weights(wl.model)
     h = lib.nv_load(path, 1, max_ctx)
-    dt, exits = run_decode(lib, h, prompt, U, steps, warmup)
+    dt, dt_s, exits = run_decode(lib, h, prompt, U, steps, warmup)
     tim, ker = timing_pass(lib, h, prompt, U, steps)
     lib.nv_free(h)
     tok_s = steps / dt
 
-    base = None
+    base = base_s = None
     if not args.no_baseline:
         m4 = replace(wl.model, gate_bias=BIAS_ALL_LAST)
         h4 = lib.nv_load(cached_weights(m4), 1, max_ctx)
-        dt4, ex4 = run_decode(lib, h4, prompt, U, steps, warmup)
+        dt4, dt4_s, ex4 = run_decode(lib, h4, prompt, U, steps, warmup)
         lib.nv_free(h4)
         assert set(ex4) == {4}
         base = steps / dt4
+        base_s = steps / dt4_s
 
     # dominant kernel: the block-GEMM or attention symbol with the most device time (the
     # one-row gate/up product at a 512-token prompt, the decode attention at 8192)
@@ -492,7 +503,10 @@ def main():
                          "avg_us": round(k[2] / max(k[1], 1) * 1e3, 3),
                          "GBps": round(k[3] / (k[2] * 1e-3) / 1e9, 1) if k[2] > 0 else None} for k in top],
         "kernel_classes_ms_per_step": {k: round(v[0] / steps, 4) for k, v in tim.items()},
+        "decode_api": "nv_generate (one sequence); nv_step_loop_tokens_per_s: one nv_step call per token",
+        "nv_step_loop_tokens_per_s": round(steps / dt_s, 2),
         "exit4_forced_tokens_per_s": round(base, 2) if base else None,
+        "exit4_forced_nv_step_loop_tokens_per_s": round(base_s, 2) if base else None,
         "speedup_vs_exit4": round(tok_s / base - 1.0, 4) if base else None,
         "exit_histogram": [int(x) for x in hist],
         "exit_mass_stated": list(STATED_MASS.get(wl.name, ())) or None,

@@ -1738,6 +1738,7 @@ nv_status nv_generate(nv_model* m, const int32_t* seqs, int32_t n_seq, int32_t n
     };
 
     std::vector<int> exit_of(m->max_batch, kMaxExits);
+    std::vector<float> u4(m->max_batch, 0.f);
     int remaining = n_seq;
     while (remaining > 0) {
         int cnt[kMaxExits] = {0, 0, 0, 0}, oldest[kMaxExits] = {0, 0, 0, 0};
@@ -1812,8 +1813,12 @@ nv_status nv_generate(nv_model* m, const int32_t* seqs, int32_t n_seq, int32_t n
             if (x.t < T) ++x.age;
         for (int slot : rest) g[idx_of[slot]].q = sg + 1;
         if (stopping.empty()) continue;
-        for (int slot : stopping) exit_of[slot] = sg + 1;
-        NV_TRY(run_heads(m, stopping, exit_of, d_unif));
+        for (int slot : stopping) {
+            exit_of[slot] = sg + 1;
+            // the token uniform on the host, for the head product with the fused draw
+            u4[slot] = uniforms[((size_t)idx_of[slot] * T + g[idx_of[slot]].t) * 4 + 3];
+        }
+        NV_TRY(run_heads(m, stopping, exit_of, d_unif, u4.data()));
         if (ring[ring_next].pending) NV_TRY(full_sync());
         NV_HIP(m, hipMemcpyAsync(m->h_ring + (size_t)ring_next * m->max_batch, m->d_tok_out,
                                  (size_t)m->max_batch * 4, hipMemcpyDeviceToHost, m->st));
