@@ -36,8 +36,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TIMING_NOTE = ("avg_launch_us: hipExtLaunchKernelGGL start/stop events on each launch on the model's stream, "
-               "in an untimed pass identical to the timed one (launch to completion, as a rocprofv3 kernel "
-               "trace counts it); avg_span_us (with --spans): first block start to last block end from device "
+               "in untimed passes identical to the timed one (decode: as many as make 100 steps or more; launch "
+               "to completion, as a rocprofv3 kernel trace counts it); avg_span_us (with --spans): first block start to last block end from device "
                "clock stamps, in a further untimed pass of its own")
 # exit masses the workloads state (the gate biases are calibrated to give them)
 STATED_MASS = {"A": (0.4, 0.25, 0.2, 0.15), "C": (0.4, 0.25, 0.2, 0.15), "D": (0.6, 0.2, 0.1, 0.1),
@@ -58,23 +58,39 @@ def kernel_source_sha1():
     return h.hexdigest()
 
 
-def counted_traffic(kname):
-    """HBM bytes per launch of `kname` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summaries under profiles/, or None when none covers this kernel or the kernel
-    sources changed since the counters were taken."""
+def profiled(kname, field):
+    """(value, source) of `field` for kernel symbol `kname` from the machine-readable block
+    of a committed summary under profiles/ (rocprofv3 counters or kernel trace), or None
+    when none covers this kernel or the kernel sources changed since it was taken."""
     import glob
-    want = kname.replace(", false>", ">")
     sha = kernel_source_sha1()
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         kv = {}
         with open(path) as f:
             for line in f:
                 k, sep, v = line.partition(": ")
-                if sep and k in ("kernel", "kernel_source_sha1", "traffic_bytes_per_launch"):
+                if sep and k in ("kernel", "kernel_source_sha1", field):
                     kv[k] = v.strip()
-        if kv.get("kernel", "").replace(", false>", ">") == want and kv.get("kernel_source_sha1") == sha:
-            return int(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+        if kv.get("kernel") == kname and kv.get("kernel_source_sha1") == sha and field in kv:
+            return float(kv[field]), os.path.relpath(path, ROOT)
     return None
+
+
+def counted_traffic(kname):
+    """HBM bytes per launch of `kname` from the committed FETCH_SIZE/WRITE_SIZE summaries."""
+    r = profiled(kname, "traffic_bytes_per_launch")
+    return (int(r[0]), r[1]) if r else None
+
+
+def profile_fields(kname, bytes_per_launch, peak):
+    """The committed rocprofv3 kernel-trace average of the dominant symbol, beside the
+    live events figure (the events average moves by several per cent between runs of
+    the same code; the profiler's kernel durations much less)."""
+    r = profiled(kname, "rocprof_avg_us")
+    if not r:
+        return {"rocprof_avg_us": None, "rocprof_frac": None, "rocprof_source": None}
+    return {"rocprof_avg_us": r[0], "rocprof_frac": round(bytes_per_launch / (r[0] * 1e-6) / 1e9 / peak, 4),
+            "rocprof_source": r[1]}
 
 
 def calibration_copy(out):
@@ -134,20 +150,29 @@ def run_decode(lib, h, prompt, U, steps, warmup):
     return dt_g, dt_s, exits
 
 
-def two_pass_timing(lib, h, setup, work):
-    """Per-launch device timing of `work` (after `setup`) in an untimed pass with HIP events
-    only; with --spans, a second pass with per-block device clock stamps as well (the small
-    kernel that folds each launch's stamps perturbs the events, so the spans come from a
-    pass of their own).  Returns the events pass's class totals and its per-kernel rows,
-    each with the stamp pass's summed span (ms) of the same symbol, or None."""
-    setup()
-    lib.nv_timing_enable(h, 1)
-    work()
-    tim = lib.nv_timing_read(h)
-    ker = lib.nv_timing_kernels(h)
-    if not SPANS:
+def two_pass_timing(lib, h, setup, work, passes=1):
+    """Per-launch device timing of `work` (after `setup`) in `passes` untimed passes with
+    HIP events only (summed: the events average of one short pass moves by a few per cent
+    from one pass to the next); with --spans, one more pass with per-block device clock
+    stamps as well (the small kernel that folds each launch's stamps perturbs the events,
+    so the spans come from a pass of their own).  Returns the events passes' class totals
+    and per-kernel rows, each with the stamp pass's summed span (ms) of the same symbol
+    scaled to the same launch count, or None."""
+    tim, acc = None, {}
+    for _ in range(passes):
+        setup()
+        lib.nv_timing_enable(h, 1)
+        work()
+        t1 = lib.nv_timing_read(h)
+        tim = t1 if tim is None else {c: tuple(a + b for a, b in zip(tim[c], t1[c])) for c in tim}
+        for k in lib.nv_timing_kernels(h):
+            key = (k[0], k[4])
+            n, ms, by = acc.get(key, (0, 0.0, 0.0))
+            acc[key] = (n + k[1], ms + k[2], by + k[3])
         lib.nv_timing_enable(h, 0)
-        return tim, [k[:5] + (None,) for k in ker]
+    ker = [(c, n, ms, by, name) for (c, name), (n, ms, by) in acc.items()]
+    if not SPANS:
+        return tim, [k + (None,) for k in ker]
     setup()
     lib.nv_timing_enable(h, 2)
     work()
@@ -156,8 +181,13 @@ def two_pass_timing(lib, h, setup, work):
     rows = []
     for k in ker:
         n2, span = spans.get((k[0], k[4]), (0, None))
-        rows.append(k[:5] + (span * k[1] / n2 if span is not None and n2 else None,))
+        rows.append(k + (span * k[1] / n2 if span is not None and n2 else None,))
     return tim, rows
+
+
+def events_passes(steps):
+    """Events passes for a decode of `steps` steps: at least about 100 steps in all."""
+    return max(1, -(-100 // max(steps, 1)))
 
 
 def timing_pass(lib, h, prompt, U, steps):
@@ -165,7 +195,7 @@ def timing_pass(lib, h, prompt, U, steps):
     def work():
         for t in range(steps):
             lib.nv_step(h, U[t:t + 1])
-    return two_pass_timing(lib, h, lambda: lib.nv_prefill(h, 0, prompt), work)
+    return two_pass_timing(lib, h, lambda: lib.nv_prefill(h, 0, prompt), work, events_passes(steps))
 
 
 def cpu_baseline(wl, path, prompt, U, budget_s):
@@ -496,13 +526,15 @@ def main():
                      "traffic_source": counted[1] if counted else None,
                      "launches": nl, "avg_launch_us": round(ms / max(nl, 1) * 1e3, 3),
                      "avg_span_us": round(span / max(nl, 1) * 1e3, 3) if span else None,
-                     "bytes_per_launch": round(by / max(nl, 1)), "timing": TIMING_NOTE},
+                     "bytes_per_launch": round(by / max(nl, 1)), "timing": TIMING_NOTE,
+                     **profile_fields(kname, by / max(nl, 1), HBM_PEAK_GBS)},
         "block_gemm_all": {"achieved_GBps": round(tim["block_gemm"][1] / (tim["block_gemm"][0] * 1e-3) / 1e9, 1),
                            "launches": tim["block_gemm"][2]},
         "top_kernels": [{"kernel": k[4], "class": k[0], "launches": k[1],
                          "avg_us": round(k[2] / max(k[1], 1) * 1e3, 3),
                          "GBps": round(k[3] / (k[2] * 1e-3) / 1e9, 1) if k[2] > 0 else None} for k in top],
-        "kernel_classes_ms_per_step": {k: round(v[0] / steps, 4) for k, v in tim.items()},
+        "kernel_classes_ms_per_step": {k: round(v[0] / (steps * events_passes(steps)), 4) for k, v in tim.items()},
+        "events_passes": events_passes(steps),
         "decode_api": "nv_generate (one sequence); nv_step_loop_tokens_per_s: one nv_step call per token",
         "nv_step_loop_tokens_per_s": round(steps / dt_s, 2),
         "exit4_forced_tokens_per_s": round(base, 2) if base else None,

@@ -32,6 +32,14 @@ void current_launch_events(hipEvent_t* start, hipEvent_t* stop) {
     *stop = t_ev_stop;
 }
 
+// 16-byte load with the nontemporal hint, for data read once per launch whose next use is
+// beyond every cache level (a decode step's weights, the K/V cache).
+typedef unsigned int stream_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+    const stream_u4 v = __builtin_nontemporal_load((const stream_u4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Symbol of the last kernel a launch wrapper issued while timing (as profilers print it).
 static thread_local char t_name[160];
 
@@ -1027,6 +1035,7 @@ __device__ __forceinline__ void exit_partial(const GemmArgs& a, const float* zb)
     }
 }
 
+template <int PER>   // partials per thread: ceil(nb / XD_THREADS) <= PER <= XD_PER
 __global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int nb, const float* logits, float u,
                                                           int* token) {
     __shared__ float s_red[XD_THREADS / 64];
@@ -1036,22 +1045,22 @@ __global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int
     __shared__ float s_mb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int NW = XD_THREADS / 64;
-    const int per = (nb + XD_THREADS - 1) / XD_THREADS;          // <= XD_PER (checked at launch)
+    const int per = (nb + XD_THREADS - 1) / XD_THREADS;          // <= PER (checked at launch)
     const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
     if (tid == 0) {
         s_bstar = -1;
         s_last = -1;
     }
-    float pm[XD_PER], ps[XD_PER];
+    float pm[PER], ps[PER];
 #pragma unroll
-    for (int i = 0; i < XD_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const float2 v = *(const float2*)(part + 2 * (b0 + i < b1 ? b0 + i : 0));   // past the range: block 0, unused
         pm[i] = v.x;
         ps[i] = v.y;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < XD_PER; ++i)
+    for (int i = 0; i < PER; ++i)
         if (b0 + i < b1) mx = fmaxf(mx, pm[i]);
     mx = wave_max(mx);
     if (lane == 0) s_red[wave] = mx;
@@ -1059,13 +1068,14 @@ __global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int
     float M = s_red[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
-    // t_b in float64; this thread's sum in block order
-    double t[XD_PER];
+    // t_b = s_b e^(m_b - M) in float32 (each at most 8, relative error ~1e-7); this thread's
+    // sum, and every running sum below, in float64 in block order
+    float t[PER];
     double loc = 0.0;
 #pragma unroll
-    for (int i = 0; i < XD_PER; ++i) {
-        t[i] = (b0 + i < b1 && pm[i] != -INFINITY) ? (double)ps[i] * exp((double)pm[i] - (double)M) : 0.0;
-        loc += t[i];
+    for (int i = 0; i < PER; ++i) {
+        t[i] = (b0 + i < b1 && pm[i] != -INFINITY) ? ps[i] * expf(pm[i] - M) : 0.f;
+        loc += (double)t[i];
     }
     // exclusive prefix of the thread sums in thread order (fixed order: waves, then lanes)
     double inc = loc;
@@ -1093,9 +1103,9 @@ __global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int
         int bs = -1;
         float mbs = -INFINITY, mprev = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < XD_PER; ++i) {
+        for (int i = 0; i < PER; ++i) {
             if (bs < 0 && b0 + i < b1) {
-                const double nx = cum + t[i];
+                const double nx = cum + (double)t[i];
                 if (target < nx) {
                     bs = b0 + i;
                     pre = cum;
@@ -1118,8 +1128,8 @@ __global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int
     // the last block with a nonzero weight (for the fall-back)
     int lb = -1;
 #pragma unroll
-    for (int i = 0; i < XD_PER; ++i)
-        if (b0 + i < b1 && t[i] > 0.0) lb = b0 + i;
+    for (int i = 0; i < PER; ++i)
+        if (b0 + i < b1 && t[i] > 0.f) lb = b0 + i;
     if (lb >= 0) atomicMax(&s_last, lb);
     __syncthreads();
     if (tid == 0) {
@@ -1139,7 +1149,7 @@ __global__ __launch_bounds__(XD_THREADS) void k_exit_draw(const float* part, int
 #pragma unroll
                 for (int j = 0; j < KS_CPB; ++j) z[j] = zb[j];
             }
-            const double f = mb == -INFINITY ? 0.0 : exp((double)mb - (double)M);
+            const double f = mb == -INFINITY ? 0.0 : (double)expf(mb - M);
             float c = 0.f;
             tok = bs * KS_CPB + KS_CPB - 1;
 #pragma unroll
@@ -1168,7 +1178,10 @@ hipError_t launch_exit_draw(const float* part, int nb, const float* logits, floa
     if (nb < 1 || nb > XD_PER * XD_THREADS || !part || !logits || !token || !(u >= 0.0f && u < 1.0f))
         return hipErrorInvalidValue;
     if (t_ev_stop) snprintf(t_name, sizeof(t_name), "nv::k_exit_draw");
-    NV_LAUNCH(k_exit_draw, dim3(1), dim3(XD_THREADS), 0, st, part, nb, logits, u, token);
+    if (nb <= 8 * XD_THREADS)
+        NV_LAUNCH(HIP_KERNEL_NAME(k_exit_draw<8>), dim3(1), dim3(XD_THREADS), 0, st, part, nb, logits, u, token);
+    else
+        NV_LAUNCH(HIP_KERNEL_NAME(k_exit_draw<XD_PER>), dim3(1), dim3(XD_THREADS), 0, st, part, nb, logits, u, token);
     return hipGetLastError();
 }
 
@@ -1254,7 +1267,7 @@ __global__ __launch_bounds__(512) void k_gemv_ks(GemmArgs a) {
 
     uint4 w[KS_CPB];
 #pragma unroll
-    for (int c = 0; c < KS_CPB; ++c) w[c] = *(const uint4*)((const char*)a.W + ((size_t)(n0 + c) * K + k0) * ESZ);
+    for (int c = 0; c < KS_CPB; ++c) w[c] = stream_load16((const char*)a.W + ((size_t)(n0 + c) * K + k0) * ESZ);
     // every weight load is issued before anything waits on the activations
     __builtin_amdgcn_sched_barrier(0);
     if (a.contig && ethr && er < R) ectx = epi_prefetch<EPIT>(a, er, n0 + ec);
@@ -2309,14 +2322,6 @@ __device__ __forceinline__ void sm_merge(float& m, float& l, float* o, float m2,
     m = M;
 }
 
-// Keys and values are read once per step (the cache of all layers outgrows the caches), so
-// their loads carry the nontemporal hint: D 0.979 -> 0.971 ms per step in a same-box A/B.
-typedef unsigned int kv_u4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 kv_stream_load(const void* p) {
-    const kv_u4 v = __builtin_nontemporal_load((const kv_u4*)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 template <int HD, bool KVBF, int RM, int NW>
 __global__ __launch_bounds__(64 * NW) void k_attn_dec(const AttnItem* items, const RowInfo* rows, const float* q,
                                                       const void* kv, int layer, LayerDims D, float* part_ml,
@@ -2358,8 +2363,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(const AttnItem* items, con
         // so all are issued back to back and waited for in order
         const int key = min(it.lo + (i * NW + wave) * KPI + g, it.hi - 1);
         if constexpr (KVBF) {
-            kr[i] = kv_stream_load((const uint16_t*)kv + kb + (int64_t)key * HD);
-            vr[i] = kv_stream_load((const uint16_t*)kv + vb + (int64_t)key * HD);
+            // read once per step: the cache of all layers outgrows the caches (D 0.979 ->
+            // 0.971 ms per step with the hint, same-box A/B)
+            kr[i] = stream_load16((const uint16_t*)kv + kb + (int64_t)key * HD);
+            vr[i] = stream_load16((const uint16_t*)kv + vb + (int64_t)key * HD);
         } else {
             kr[i] = *(const uint4*)((const float*)kv + kb + (int64_t)key * HD);
             vr[i] = *(const uint4*)((const float*)kv + vb + (int64_t)key * HD);
@@ -2544,20 +2551,19 @@ __device__ __forceinline__ void publish_stop(int* host_flags, int seq, int tag, 
 __global__ __launch_bounds__(256) void k_gate(const RowInfo* rows, const int* seqs, int n, const float* Hs, int d,
                                               const float* gw, float bias, const float* uniforms, int ucol,
                                               double* w_out, int* stop_out, int* host_flags, int tag) {
-    __shared__ double red[256];
+    __shared__ double wsum[4];
     const int i = blockIdx.x;
     if (i >= n) return;
     const float* h = Hs + (int64_t)rows[i].hrow * d;
     double acc = 0.0;
     for (int k = threadIdx.x; k < d; k += blockDim.x) acc += (double)gw[k] * (double)h[k];
-    red[threadIdx.x] = acc;
+    // in-wave butterfly, then the four waves in a fixed order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = acc;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
     if (threadIdx.x == 0) {
-        const double z = red[0] + (double)bias;
+        const double z = ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) + (double)bias;
         double w;
         if (z >= 0.0) {
             w = 1.0 / (1.0 + exp(-z));
