@@ -82,7 +82,20 @@ struct GemmArgs {
     // also writes the (max, sum of exp(z - max)) of its KS_CPB logits to xd_part[2b], [2b+1];
     // launch_exit_draw then draws the token from them without re-reading every logit.
     float* xd_part;       // [N / 8][2]
+    // Decode-sized row groups on the matrix cores with K split across blocks (non-head
+    // products, sk_min_rows <= R <= sk_max_rows, K a multiple of SK_KC): each K slice's
+    // fp32 partial tile goes to sk_ws ([K/SK_KC][R][N], then the per-slice sums of squares
+    // [K/SK_KC][R] for RMSNorm), and a second kernel adds the slices in order and applies
+    // the epilogue.  sk_cap is sk_ws's size in floats; sk_min_rows 0 turns the path off.
+    float* sk_ws;
+    int64_t sk_cap;
+    int sk_min_rows, sk_max_rows;
+    int sk_ntb;           // 16-column tiles per block: bits 0-3 with RMSNorm, bits 4-7 without (1 or 2)
 };
+
+// K slice of one block of the split-K decode product (k_gemm_sk).
+constexpr int SK_KC = 512;
+constexpr int SK_MAX_ROWS = 64;
 
 // The exit draw: one block of XD_THREADS threads merges the head product's per-block
 // partials; a thread holds at most XD_PER of them (N / 8 <= XD_PER * XD_THREADS).
@@ -149,6 +162,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // (normalised when norm_w is set) to abf, then k_gemm_bf16 runs on them.  With
 // launch_rows_bf16 first and abf_ready set, launch_gemm runs only the product.
 bool gemm_uses_bf16_rows(const GemmArgs& a);
+// K slices of the split-K decode product when `a` takes it, else 0.
+int sk_slices(const GemmArgs& a);
 hipError_t launch_rows_bf16(const GemmArgs& a, hipStream_t st);
 // Decode-sized row blocks (<= ATTN_DEC_ROWS rows): each item is one split of one
 // (row block, head); split partials are merged by launch_attn_combine.

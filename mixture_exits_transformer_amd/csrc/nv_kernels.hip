@@ -989,9 +989,22 @@ static void launch_gemm_bf16_bn(const GemmArgs& a, dim3 grid, hipStream_t st) {
     }
 }
 
+// Whether a product takes the split-K decode path, and its slice count.
+int sk_slices(const GemmArgs& a) {
+    if (!a.wbf16 || a.head || a.comb || !a.sk_ws || a.mfma_min_rows <= 0 || a.sk_min_rows <= 0 || a.R < a.sk_min_rows ||
+        a.R > a.sk_max_rows || a.R > SK_MAX_ROWS || a.K % SK_KC || a.N % 32 || a.out_bf16 || a.abf_ready || a.xent_part ||
+        a.xd_part || a.epi < EPI_STORE || a.epi > EPI_SILU)
+        return 0;
+    const int ntb = a.norm_w ? (a.sk_ntb & 15) : ((a.sk_ntb >> 4) & 15);
+    if ((ntb != 1 && ntb != 2) || a.N % (16 * ntb)) return 0;
+    const int nks = a.K / SK_KC;
+    if ((int64_t)nks * a.R * (a.N + 1) > a.sk_cap) return 0;
+    return nks;
+}
+
 bool gemm_uses_bf16_rows(const GemmArgs& a) {
     return a.wbf16 && a.abf && a.mfma_min_rows > 0 && a.R >= GB_MIN_ROWS && a.N % 64 == 0 && a.K % GB_BK == 0 &&
-           !a.comb;
+           !a.comb && !sk_slices(a);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1507,6 +1520,163 @@ __global__ __launch_bounds__(1024) void k_gemm_mfma_ks(GemmArgs a) {
     stamp_end(a.stamp, t_begin);
 }
 
+// Decode-sized row groups (up to 16 MT rows) on the matrix cores with K split across
+// blocks.  Block (x, y) owns 16 NTB output columns and the K slice [SK_KC y, SK_KC (y + 1));
+// its four waves are NTB column tiles times 4 / NTB k-parts of KPW steps of 32.  The rows'
+// slice is staged once per block in LDS as bf16 (times the RMSNorm weight for NORM), the
+// weight fragments stream straight into registers, the k-parts are added through LDS and
+// the block stores its fp32 partial tile (column tile 0 also its rows' sums of squares).
+// A 1536-column product thus runs on 96 x K/512 blocks instead of 96, so that every
+// compute unit streams weights.  k_gemm_sk_reduce then adds the slices in slice order and
+// applies RMSNorm's row scale and the product's epilogue.
+template <int MT, int NTB, bool NORM>
+__global__ __launch_bounds__(256) void k_gemm_sk(GemmArgs a, float* part, float* pss) {
+    constexpr int KPARTS = 4 / NTB;
+    constexpr int KPW = SK_KC / (KPARTS * 32);   // k-steps per wave
+    constexpr int LDA = SK_KC + 8;               // bf16 per LDS row: rows 16 bytes apart in bank order
+    constexpr int RP = 16 * MT;
+    constexpr int RW = RP / 4;                   // rows staged per wave
+    static_assert(SK_KC == 512, "the staging below covers 512 values per row with 64 lanes");
+    __shared__ __attribute__((aligned(16))) uint16_t as[RP][LDA];
+    __shared__ f32x4_t red[KPARTS - 1 > 0 ? KPARTS - 1 : 1][NTB][MT][64];
+    const unsigned long long t_begin = stamp_begin(a.stamp);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nt = wave % NTB, kp = wave / NTB;
+    const int K = a.K, R = a.R, N = a.N;
+    const int n0 = blockIdx.x * 16 * NTB, ks = blockIdx.y, k0 = ks * SK_KC;
+
+    // weight fragments: row n0 + 16 nt + lane % 16, k = k0 + 32 (kp KPW + s) + 8 (lane / 16)
+    u32x4 wv[KPW];
+    {
+        const uint16_t* wp = (const uint16_t*)a.W + (int64_t)(n0 + nt * 16 + (lane & 15)) * K + k0 +
+                             32 * kp * KPW + 8 * (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < KPW; ++s) wv[s] = __builtin_nontemporal_load((const u32x4*)(wp + 32 * s));
+    }
+    // the rows' slice: wave w stages rows w, w + 4, ...; a lane takes floats 4 lane .. 4 lane + 3
+    // and 256 + 4 lane .. 256 + 4 lane + 3 (rows past R are zero)
+    float4 gv[2];
+    if constexpr (NORM) {
+        gv[0] = *(const float4*)(a.norm_w + k0 + 4 * lane);
+        gv[1] = *(const float4*)(a.norm_w + k0 + 256 + 4 * lane);
+    }
+    float4 xv[RW][2];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        const int r = wave + 4 * i;
+        if (r < R) {
+            const float* ap = a.A + (int64_t)(a.a_rows ? a.a_rows[r].hrow : r) * a.lda + k0 + 4 * lane;
+            xv[i][0] = *(const float4*)ap;
+            xv[i][1] = *(const float4*)(ap + 256);
+        } else {
+            xv[i][0] = xv[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    float ss[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+        const int r = wave + 4 * i;
+        float4 x0 = xv[i][0], x1 = xv[i][1];
+        if constexpr (NORM) {
+            float t = x0.x * x0.x;
+            t = fmaf(x0.y, x0.y, t); t = fmaf(x0.z, x0.z, t); t = fmaf(x0.w, x0.w, t);
+            t = fmaf(x1.x, x1.x, t); t = fmaf(x1.y, x1.y, t); t = fmaf(x1.z, x1.z, t); t = fmaf(x1.w, x1.w, t);
+            ss[i] = t;
+            x0.x *= gv[0].x; x0.y *= gv[0].y; x0.z *= gv[0].z; x0.w *= gv[0].w;
+            x1.x *= gv[1].x; x1.y *= gv[1].y; x1.z *= gv[1].z; x1.w *= gv[1].w;
+        }
+        *(uint2*)&as[r][4 * lane] = make_uint2(pack_bf2(x0.x, x0.y), pack_bf2(x0.z, x0.w));
+        *(uint2*)&as[r][256 + 4 * lane] = make_uint2(pack_bf2(x1.x, x1.y), pack_bf2(x1.z, x1.w));
+    }
+    if constexpr (NORM) {
+        if (blockIdx.x == 0) {   // one block per slice stores the slice's sums of squares
+#pragma unroll
+            for (int i = 0; i < RW; ++i) {
+                const int r = wave + 4 * i;
+                const float t = wave_total(ss[i]);
+                if (lane == 0 && r < R) pss[ks * R + r] = t;
+            }
+        }
+    }
+    __syncthreads();
+
+    f32x4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) {
+        const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, wv[s]);
+        const int kk = 32 * (kp * KPW + s) + 8 * (lane >> 4);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const u32x4 au = *(const u32x4*)&as[mt * 16 + (lane & 15)][kk];
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, au), bf, acc[mt], 0, 0, 0);
+        }
+    }
+    if constexpr (KPARTS > 1) {
+        if (kp > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) red[kp - 1][nt][mt][lane] = acc[mt];
+        }
+        __syncthreads();
+        if (kp == 0) {
+#pragma unroll
+            for (int q = 0; q < KPARTS - 1; ++q)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] += red[q][nt][mt][lane];
+        }
+    }
+    if (kp == 0) {
+        // acc[mt][i] is (row mt*16 + 4 (lane / 16) + i, column lane % 16) of the tile
+        const int col = n0 + nt * 16 + (lane & 15);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = mt * 16 + 4 * (lane >> 4) + i;
+                if (row < R) part[((int64_t)ks * R + row) * N + col] = acc[mt][i];
+            }
+    }
+    stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
+}
+
+// The slices of k_gemm_sk added in slice order, RMSNorm's row scale, then the product's
+// epilogue on the column pair (col, col + 1) of one row.
+template <bool NORM>
+__global__ __launch_bounds__(256) void k_gemm_sk_reduce(GemmArgs a, const float* part, const float* pss, int nks) {
+    const int np = a.N >> 1;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= a.R * np) return;
+    const int row = idx / np, col = 2 * (idx - row * np);
+    float y = 0.f, u = 0.f, sq = 0.f;
+    for (int s0 = 0; s0 < nks; s0 += 8) {
+        // eight slices' loads issued before the first add
+        float2 p[8];
+        float q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = s0 + j;
+            p[j] = s < nks ? *(const float2*)(part + ((int64_t)s * a.R + row) * a.N + col) : make_float2(0.f, 0.f);
+            q[j] = NORM && s < nks ? pss[s * a.R + row] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (s0 + j < nks) {
+                y += p[j].x;
+                u += p[j].y;
+                sq += q[j];
+            }
+        }
+    }
+    if constexpr (NORM) {
+        const float inv = 1.0f / sqrtf(sq / (float)a.K + a.eps);
+        y *= inv;
+        u *= inv;
+    }
+    const EpiCtx e = epi_prepare(a, row, col);
+    epi_apply(a, e, row, col, y, u);
+}
+
 static bool use_mfma(const GemmArgs& a) {
     return a.wbf16 && a.mfma_min_rows > 0 && a.R >= a.mfma_min_rows && a.K % MF_BK == 0 && a.N % 64 == 0 &&
            (a.norm_w == nullptr || a.rms_ws != nullptr);
@@ -1532,6 +1702,37 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         if (a.epi != EPI_RESID) return hipErrorInvalidValue;
         if (t_ev_stop) snprintf(t_name, sizeof(t_name), "void nv::k_gemv_ks<true, 1, 0, true, %d>(nv::GemmArgs)", EPI_RESID);
         NV_LAUNCH(HIP_KERNEL_NAME(k_gemv_ks<true, 1, 0, true, EPI_RESID>), dim3(a.N / KS_CPB), dim3(64 * nw), 0, st, b);
+        return hipGetLastError();
+    }
+    // decode-sized row groups on the matrix cores, K split across blocks
+    if (const int nks = sk_slices(a)) {
+        const int mt = (a.R + 15) / 16;
+        const bool norm = a.norm_w != nullptr;
+        const int ntb = norm ? (a.sk_ntb & 15) : ((a.sk_ntb >> 4) & 15);
+        float* part = a.sk_ws;
+        float* pss = part + (int64_t)nks * a.R * a.N;
+        const dim3 grid(a.N / (16 * ntb), nks), block(256);
+        if (t_ev_stop)
+            snprintf(t_name, sizeof(t_name), "void nv::k_gemm_sk<%d, %d, %s>(nv::GemmArgs)", mt, ntb,
+                     norm ? "true" : "false");
+#define NV_SK2(MTV, NTV)                                                                                      \
+    do {                                                                                                     \
+        if (norm) NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_sk<MTV, NTV, true>), grid, block, 0, st, b, part, pss);   \
+        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_sk<MTV, NTV, false>), grid, block, 0, st, b, part, pss);       \
+    } while (0)
+#define NV_SK(MTV)                                                                                            \
+    do {                                                                                                     \
+        if (ntb == 1) NV_SK2(MTV, 1); else NV_SK2(MTV, 2);                                                   \
+    } while (0)
+        if (mt == 1) NV_SK(1); else if (mt == 2) NV_SK(2); else if (mt == 3) NV_SK(3); else NV_SK(4);
+#undef NV_SK
+#undef NV_SK2
+        // the reduction belongs to the same timed product; its blocks store no stamps
+        const int stamped = t_blocks;
+        const dim3 rgrid((a.R * (a.N / 2) + 255) / 256);
+        if (norm) NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_sk_reduce<true>), rgrid, block, 0, st, b, part, pss, nks);
+        else NV_LAUNCH(HIP_KERNEL_NAME(k_gemm_sk_reduce<false>), rgrid, block, 0, st, b, part, pss, nks);
+        t_blocks = stamped;
         return hipGetLastError();
     }
     // decode-sized rows, vector ALUs (rows <= 8, and below the matrix-core threshold)

@@ -81,6 +81,7 @@ struct Plan {
     size_t tables = 0, small = 0, logits = 0, router_hid = 0;
     size_t seg = 0;     // persistent segment kernel: tagged exchange buffers, counters, layer table
     size_t xd = 0;      // exit draw: the head product's per-block softmax partials
+    int64_t sk_floats = 0;   // split-K decode products: slice partials and sums of squares
     int loss_ch = 0;    // mixture objective: rows per head pass
     size_t loss = 0;    // its logits, per-row router outputs / log-probabilities / losses, row tables
     size_t total = 0;
@@ -185,6 +186,12 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
     p.xd = align_up((size_t)(V / 8) * 2 * 4);
+    // the largest (K / SK_KC) x N over the layer products, for SK_MAX_ROWS rows
+    {
+        const int64_t kd = (int64_t)d / SK_KC, kf = (int64_t)F / SK_KC;
+        const int64_t kn = std::max({kd * 3 * (int64_t)d, kd * 2 * (int64_t)F, kf * (int64_t)d});
+        p.sk_floats = kn > 0 ? (int64_t)SK_MAX_ROWS * (kn + std::max(kd, kf)) : 0;
+    }
     // rows per head pass of the mixture objective: every pass re-reads the head weights, so
     // a pass takes as many rows as a 256 MiB logits workspace holds (at least 256, at most
     // the row capacity); NVIUM_LOSS_ROWS sets it instead (tests of ragged passes)
@@ -200,7 +207,8 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
              align_up((size_t)p.loss_ch * ((V + 63) / 64) * 8) + align_up((size_t)p.loss_ch * 4);
     p.total = p.abf + p.loss + p.router_hid + p.embed + L * p.layer_w + kMaxExits * p.exit_w + p.shared_head +
               p.hidden + p.kv + p.rope + p.qbuf + p.attn_o +
-              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + p.xd + kAlign;
+              p.mlp + p.part_ml + p.part_o + p.rms + p.tables + p.small + p.logits + p.seg + p.xd +
+              align_up((size_t)p.sk_floats * 4) + kAlign;
     return p;
 }
 
@@ -248,6 +256,14 @@ struct nv_model {
     // the 16-row matrix-core tiles, which leave half their rows empty at 5-8 rows
     // (batch-1 decode: 0.417 -> 0.411 ms per segment-token against a threshold of 5)
     int mfma_min_rows = 9;
+    // row groups of sk_min_rows..sk_max_rows rows take the split-K matrix-core product when
+    // K is a multiple of SK_KC (0: never).  Batch-16 decode (1.5B, 16 x 32 tokens): 1.766 ms
+    // per segment-step with none, 1.617 for 9-32 rows, 1.560 for 5-32, 1.526 for 5-64; batch
+    // 1 at prompt 512 and 8192 within 2 %, the same or better
+    int sk_min_rows = 5, sk_max_rows = SK_MAX_ROWS;
+    int sk_ntb = 2 | (1 << 4);   // 16-column tiles per block with / without RMSNorm
+    float* sk_ws = nullptr;
+    int64_t sk_cap = 0;
     int n_cu = 256;               // compute units of the device (decode attention grid sizing)
     char* d_tables = nullptr;
     // Small per-step blocks; each has a pinned host mirror of the same layout so that it
@@ -516,6 +532,10 @@ struct Tables {
 bool gemv_only(const nv_model* m, int R) {
     if (R < 1 || R > 8) return false;
     if (m->bf16 && m->mfma_min_rows > 0 && R >= m->mfma_min_rows) return false;
+    // the split-K matrix-core product reads the row tables
+    if (m->bf16 && m->sk_ws && m->mfma_min_rows > 0 && m->sk_min_rows > 0 && R >= m->sk_min_rows &&
+        R <= m->sk_max_rows)
+        return false;
     const int epc = m->bf16 ? 8 : 4;
     for (int K : {m->d, m->F})
         if (K % epc || K % 4 || (K / epc + 63) / 64 > 8) return false;
@@ -726,6 +746,11 @@ nv_status run_segment(nv_model* m, int s, const Tables& t) {
         g.rms_ws = m->rms_ws;
         g.abf = m->abf;
         g.mfma_min_rows = m->mfma_min_rows;
+        g.sk_ws = m->sk_ws;
+        g.sk_cap = m->sk_cap;
+        g.sk_min_rows = m->sk_min_rows;
+        g.sk_max_rows = m->sk_max_rows;
+        g.sk_ntb = m->sk_ntb;
         g.contig = t.contig ? 1 : 0;
         g.a_row0 = g.o_row0 = t.hrow0;
         g.seq0 = t.seq0;
@@ -1209,6 +1234,16 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     m->rms_ws = (float*)m->take(P.rms);
     m->abf = (uint16_t*)m->take(P.abf);
     if (const char* e = std::getenv("NVIUM_MFMA_MIN_ROWS")) m->mfma_min_rows = std::atoi(e);
+    if (P.sk_floats > 0) {
+        m->sk_ws = (float*)m->take(align_up((size_t)P.sk_floats * 4));
+        m->sk_cap = P.sk_floats;
+    }
+    if (const char* e = std::getenv("NVIUM_SK_MIN_ROWS")) m->sk_min_rows = std::atoi(e);
+    if (const char* e = std::getenv("NVIUM_SK_MAX_ROWS")) m->sk_max_rows = std::atoi(e);
+    if (const char* e = std::getenv("NVIUM_SK_NTB")) {   // "<with RMSNorm>,<without>"
+        int a = 0, b = 0;
+        if (std::sscanf(e, "%d,%d", &a, &b) == 2) m->sk_ntb = (a & 15) | ((b & 15) << 4);
+    }
     m->d_tables = m->take(P.tables);
     m->d_stepblk = m->take(m->stepblk_bytes());
     m->d_gatelist = m->take(m->list_bytes());

@@ -318,8 +318,20 @@ const char* hipGetErrorString(hipError_t e) { return e == hipSuccess ? "no error
 namespace nv {
 
 // The shape rules the host runtime branches on, as the kernels state them.
+int sk_slices(const GemmArgs& a) {
+    if (!a.wbf16 || a.head || a.comb || !a.sk_ws || a.mfma_min_rows <= 0 || a.sk_min_rows <= 0 || a.R < a.sk_min_rows ||
+        a.R > a.sk_max_rows || a.R > SK_MAX_ROWS || a.K % SK_KC || a.N % 32 || a.out_bf16 || a.abf_ready || a.xent_part ||
+        a.xd_part || a.epi < EPI_STORE || a.epi > EPI_SILU)
+        return 0;
+    const int ntb = a.norm_w ? (a.sk_ntb & 15) : ((a.sk_ntb >> 4) & 15);
+    if ((ntb != 1 && ntb != 2) || a.N % (16 * ntb)) return 0;
+    const int nks = a.K / SK_KC;
+    return (int64_t)nks * a.R * (a.N + 1) > a.sk_cap ? 0 : nks;
+}
+
 bool gemm_uses_bf16_rows(const GemmArgs& a) {
-    return a.wbf16 && a.abf && a.mfma_min_rows > 0 && a.R >= 33 && a.N % 64 == 0 && a.K % 64 == 0 && !a.comb;
+    return a.wbf16 && a.abf && a.mfma_min_rows > 0 && a.R >= 33 && a.N % 64 == 0 && a.K % 64 == 0 && !a.comb &&
+           !sk_slices(a);
 }
 
 bool attn_mfma_ok(const LayerDims& D) { return D.kv_bf16 && (D.hd == 32 || D.hd == 64 || D.hd == 128); }

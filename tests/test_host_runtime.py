@@ -12,7 +12,8 @@ the next position, the per-segment frontiers and that flushing completes every l
 Shapes: the tiny model (float32, head_dim 32), its bf16 form on each matrix-product path, the
 shared-head / adapter / router-MLP form with ragged loss passes, and a 4-layer bf16 model with
 head_dim 128 at an 8K context (prompts longer than the 4096-row launch group, 128 key splits)
-and on the one-launch-per-segment kernel.
+and on the one-launch-per-segment kernel, and with the split-K decode product taking
+groups of 5-64 rows (its MLP width 512 is one K slice).
 
 The whole library with host sanitizers is checked by an opt-in test (about 2.5 minutes of
 hipcc): NVIUM_SANITIZE_LIBRARY=1 builds it and runs tests/test_abi_cpu.py against it.
@@ -44,6 +45,7 @@ CASES = [
     ("forms", 3, 128, "20,9,64", {"NVIUM_LOSS_ROWS": "7"}),
     ("hd128", 2, 8500, "8200,300", {}),
     ("hd128", 2, 1200, "1000,70", {"NVIUM_SEGMENT": "1"}),
+    ("hd128", 4, 600, "40,17,3,100", {"NVIUM_SK_MIN_ROWS": "5", "NVIUM_SK_MAX_ROWS": "64"}),
 ]
 
 SAN_ENV = {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=1",
@@ -60,7 +62,7 @@ def driver(tmp_path_factory):
 def test_host_runtime_sanitized(driver, weights_dir, model, batch, ctx, lens, env):
     path = cached_weights(MODELS[model], weights_dir)
     e = dict(os.environ)
-    for k in ("NVIUM_MFMA_MIN_ROWS", "NVIUM_LOSS_ROWS", "NVIUM_SEGMENT"):
+    for k in ("NVIUM_MFMA_MIN_ROWS", "NVIUM_LOSS_ROWS", "NVIUM_SEGMENT", "NVIUM_SK_MIN_ROWS", "NVIUM_SK_MAX_ROWS"):
         e.pop(k, None)
     e.update(SAN_ENV)
     e.update(env)
