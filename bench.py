@@ -35,6 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SPANS = False          # --spans: also a pass with per-block device clock stamps
+EVENTS_PASSES = 0      # --events-passes: events passes of a decode (0: enough for 100 steps)
 TIMING_NOTE = ("avg_launch_us: hipExtLaunchKernelGGL start/stop events on each launch on the model's stream, "
                "in untimed passes identical to the timed one (decode: as many as make 100 steps or more; launch "
                "to completion, as a rocprofv3 kernel trace counts it); avg_span_us (with --spans): first block start to last block end from device "
@@ -186,7 +188,10 @@ def two_pass_timing(lib, h, setup, work, passes=1):
 
 
 def events_passes(steps):
-    """Events passes for a decode of `steps` steps: at least about 100 steps in all."""
+    """Events passes for a decode of `steps` steps: at least about 100 steps in all
+    (--events-passes sets the count instead)."""
+    if EVENTS_PASSES:
+        return EVENTS_PASSES
     return max(1, -(-100 // max(steps, 1)))
 
 
@@ -447,11 +452,14 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--spans", action="store_true",
                     help="also time first block start to last block end (device stamps) in a pass of its own")
+    ap.add_argument("--events-passes", type=int, default=0,
+                    help="events passes of a decode (default: enough for 100 steps)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
-    global SPANS
+    global SPANS, EVENTS_PASSES
     SPANS = args.spans
+    EVENTS_PASSES = max(0, args.events_passes)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path "
               f"runs on a single GPU", file=sys.stderr)
