@@ -137,8 +137,9 @@ nv_status nv_step_forced(nv_model *m, const float *uniforms, const int32_t *next
                                 ones still going run segment 2, ...; one token per sequence per
                                 round (what repeated nv_step calls do) */
 #define NV_SCHED_GREEDY 1    /* each tick runs the segment with the highest
-                                (waiting sequences + half the longest wait there, in ticks);
-                                ties go to the deeper segment */
+                                (waiting sequences + 16 x the longest wait there, in ticks;
+                                the environment variable NVIUM_SCHED_AGE read by nv_load
+                                sets the weight); ties go to the deeper segment */
 
 /* Batched decoding where sequences advance through the segments independently (the
  * gptget.net summary's limitations section names the batched-inference strategy as

@@ -262,6 +262,10 @@ struct nv_model {
     // 1 at prompt 512 and 8192 within 2 %, the same or better
     int sk_min_rows = 5, sk_max_rows = SK_MAX_ROWS;
     int sk_ntb = 2 | (1 << 4);   // 16-column tiles per block with / without RMSNorm
+    // greedy scheduling: weight of the longest wait (ticks) in a segment's score.  Workload C
+    // (16 sequences, 1.5B): 0 -> 4632 tokens/s, 0.5 -> 4836, 2 -> 4839, 4 -> 5093, 8 -> 5216,
+    // 16 and more -> 5288-5294 (the lock-step schedule; lock-step itself 5291-5298)
+    double sched_age = 16.0;
     float* sk_ws = nullptr;
     int64_t sk_cap = 0;
     int n_cu = 256;               // compute units of the device (decode attention grid sizing)
@@ -1240,6 +1244,7 @@ nv_status nv_load(const char* path, int32_t max_batch, int32_t max_ctx, void* de
     }
     if (const char* e = std::getenv("NVIUM_SK_MIN_ROWS")) m->sk_min_rows = std::atoi(e);
     if (const char* e = std::getenv("NVIUM_SK_MAX_ROWS")) m->sk_max_rows = std::atoi(e);
+    if (const char* e = std::getenv("NVIUM_SCHED_AGE")) m->sched_age = std::atof(e);
     if (const char* e = std::getenv("NVIUM_SK_NTB")) {   // "<with RMSNorm>,<without>"
         int a = 0, b = 0;
         if (std::sscanf(e, "%d,%d", &a, &b) == 2) m->sk_ntb = (a & 15) | ((b & 15) << 4);
@@ -1791,12 +1796,12 @@ nv_status nv_generate(nv_model* m, const int32_t* seqs, int32_t n_seq, int32_t n
                     break;
                 }
         } else {
-            // the segment with the most waiting sequences, plus half the longest wait
-            // there in ticks; ties go to the deeper segment
+            // the segment with the most waiting sequences, plus sched_age times the
+            // longest wait there in ticks; ties go to the deeper segment
             double best = -1.0;
             for (int k = 0; k < kMaxExits; ++k)
                 if (cnt[k]) {
-                    const double sc = cnt[k] + 0.5 * oldest[k];
+                    const double sc = cnt[k] + m->sched_age * oldest[k];
                     if (sc >= best) {
                         best = sc;
                         sg = k;
