@@ -991,7 +991,7 @@ static void launch_gemm_bf16_bn(const GemmArgs& a, dim3 grid, hipStream_t st) {
 
 // Whether a product takes the split-K decode path, and its slice count.
 int sk_slices(const GemmArgs& a) {
-    if (!a.wbf16 || a.head || a.comb || !a.sk_ws || a.mfma_min_rows <= 0 || a.sk_min_rows <= 0 || a.R < a.sk_min_rows ||
+    if (!a.wbf16 || a.head > 1 || a.comb || !a.sk_ws || a.mfma_min_rows <= 0 || a.sk_min_rows <= 0 || a.R < a.sk_min_rows ||
         a.R > a.sk_max_rows || a.R > SK_MAX_ROWS || a.K % SK_KC || a.N % 32 || a.out_bf16 || a.abf_ready || a.xent_part ||
         a.xd_part || a.epi < EPI_STORE || a.epi > EPI_SILU)
         return 0;

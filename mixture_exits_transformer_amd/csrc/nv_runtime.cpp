@@ -186,10 +186,11 @@ Plan make_plan(const nv_config& c, int max_batch, int max_ctx) {
             align_up((size_t)c.n_heads * SEG_SMAX * (2 + hd) * 8) + align_up(4);
     p.router_hid = align_up((size_t)max_batch * (c.router_dim > 0 ? c.router_dim : 1) * 8);
     p.xd = align_up((size_t)(V / 8) * 2 * 4);
-    // the largest (K / SK_KC) x N over the layer products, for SK_MAX_ROWS rows
+    // the largest (K / SK_KC) x N over the layer products and the exit heads, for
+    // SK_MAX_ROWS rows
     {
         const int64_t kd = (int64_t)d / SK_KC, kf = (int64_t)F / SK_KC;
-        const int64_t kn = std::max({kd * 3 * (int64_t)d, kd * 2 * (int64_t)F, kf * (int64_t)d});
+        const int64_t kn = std::max({kd * 3 * (int64_t)d, kd * 2 * (int64_t)F, kf * (int64_t)d, kd * (int64_t)V});
         p.sk_floats = kn > 0 ? (int64_t)SK_MAX_ROWS * (kn + std::max(kd, kf)) : 0;
     }
     // rows per head pass of the mixture objective: every pass re-reads the head weights, so
@@ -1469,6 +1470,11 @@ static nv_status run_heads(nv_model* m, const std::vector<int>& seqs, const std:
     g.rms_ws = m->rms_ws;
     g.abf = m->abf;
     g.mfma_min_rows = m->mfma_min_rows;
+    g.sk_ws = m->sk_ws;
+    g.sk_cap = m->sk_cap;
+    g.sk_min_rows = m->sk_min_rows;
+    g.sk_max_rows = m->sk_max_rows;
+    g.sk_ntb = m->sk_ntb;
     if (m->cfg.head_form == 1) {
         float* X = m->attn_o;   // [ns][d] gathered rows, then adapter outputs
         float* S = m->mlp;      // [ns][r] adapter hidden units

@@ -105,3 +105,38 @@ def test_splitk_and_single_block_paths_agree(lib, weights_dir, monkeypatch):
     for (k1, v1), (k2, v2) in zip(*kvs):
         assert rel(k1, k2) < 1e-2 and rel(v1, v2) < 1e-2
 
+
+
+def test_splitk_multirow_heads(lib, weights_dir, monkeypatch):
+    """Eight sequences stopping at one exit in every step: the exit head of 8 rows and the
+    block products of 8-64-row groups take the split-K product.  Each sequence's tokens,
+    exits, logits and gates against its own oracle run (the exit pattern forced, the same
+    for all eight: 1, 2, 3 and 4 in turn, with deferred chunks at every depth)."""
+    monkeypatch.delenv("NVIUM_MFMA_MIN_ROWS", raising=False)
+    monkeypatch.delenv("NVIUM_SK_MIN_ROWS", raising=False)
+    path = cached_weights(SK_MODEL, weights_dir)
+    M = om.OracleModel(path)
+    B, n_steps = 8, 12
+    pattern = [1, 2, 3, 4] * (n_steps // 4)
+    rng = np.random.default_rng(21)
+    prompts = [rng.integers(0, M.V, size=int(rng.integers(6, 30))) for _ in range(B)]
+    Us = [_forced_u(pattern, rng) for _ in range(B)]
+    max_ctx = 30 + n_steps
+    oracle = [om.generate(M, prompts[b], Us[b], max_ctx=max_ctx)[0] for b in range(B)]
+    h = lib.nv_load(path, B, max_ctx)
+    try:
+        for b in range(B):
+            lib.nv_prefill(h, b, prompts[b])
+        res = StepCheck()
+        for t in range(n_steps):
+            U = np.stack([oracle[b][t].u for b in range(B)]).astype(np.float32)
+            nxt = np.array([oracle[b][t].token for b in range(B)], np.int32)
+            tok, ex = lib.nv_step_forced(h, U, nxt)
+            for b in range(B):
+                assert ex[b] == pattern[t]
+                check_step(t, oracle[b][t], int(tok[b]), int(ex[b]), lib.nv_debug_logits(h, b),
+                           lib.nv_debug_gates(h, b), res, logit_band=True)
+        print("\nsplit-K heads of 8 rows:", end=" ")
+        res.finish(TOL)
+    finally:
+        lib.nv_free(h)
