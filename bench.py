@@ -105,6 +105,15 @@ def calibration_copy(out):
     dst.copy_(src)
     torch.cuda.synchronize()
     out["calibration_copy_bytes"] = 1 << 30
+    # the same copy timed (three more, events on torch's stream): HBM read + write rate of a
+    # plain device copy, a practical ceiling beside the 8 TB/s data-sheet peak
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    out["calibration_copy_GBps"] = round(3 * 2 * (1 << 30) / (t0.elapsed_time(t1) * 1e-3) / 1e9, 1)
 
 
 class paused_gc:
