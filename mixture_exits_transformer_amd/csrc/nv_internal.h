@@ -181,10 +181,12 @@ constexpr int ATTN_DEC_ITERS = 8;
 constexpr int ATTN_COMB_MAX = 4096;      // splits of one (row, head) the combine pass holds
 // Long contexts (row blocks of at most ATTN_DEC_WIDE_ROWS rows, some context past
 // ATTN_DEC_WIDE_MIN_KEYS keys, bf16 K/V): blocks of ATTN_DEC_WIDE_WAVES waves, a split covering
-// up to 16 x 8 x (64 / (head_dim / 8)) keys (512 at head_dim 128), one block per CU on about
-// 3/4 of the CUs.  An 8K context then takes 17 splits per head at 12 heads instead of 65, so
-// the one-row O product merges them as it loads (no combine launch).
+// up to 16 x ATTN_DEC_WIDE_ITERS x (64 / (head_dim / 8)) keys (576 at head_dim 128), one block
+// per CU on about 3/4 of the CUs.  An 8K context then takes 15-16 splits per head at 12 heads
+// instead of 65, so the one-row O product merges them as it loads (no combine launch), in two
+// batches of 8 (512-key splits made 17 past 8192 keys, and a third batch)
 constexpr int ATTN_DEC_WIDE_WAVES = 16;
+constexpr int ATTN_DEC_WIDE_ITERS = 9;
 constexpr int ATTN_DEC_WIDE_ROWS = 2;
 constexpr int ATTN_DEC_WIDE_MIN_KEYS = 4096;
 // wide: use the ATTN_DEC_WIDE_WAVES-wave blocks (bf16 K/V, max_rows <= ATTN_DEC_WIDE_ROWS)

@@ -2532,7 +2532,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(const AttnItem* items, con
     constexpr int DPL = 8;
     constexpr int LPK = HD / DPL;       // lanes per key
     constexpr int KPI = 64 / LPK;       // keys per wave instruction
-    constexpr int NIT = ATTN_DEC_ITERS; // key groups per wave: a split holds at most NW * KPI * NIT keys
+    // key groups per wave: a split holds at most NW * KPI * NIT keys
+    constexpr int NIT = NW == ATTN_DEC_WIDE_WAVES ? ATTN_DEC_WIDE_ITERS : ATTN_DEC_ITERS;
     __shared__ float red[NW][RM][HD + 2];
     const AttnItem it = dg.on ? dec_item(dg, blockIdx.x) : items[blockIdx.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

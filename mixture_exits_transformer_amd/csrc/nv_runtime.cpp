@@ -607,7 +607,7 @@ nv_status upload_tables(nv_model* m, const std::vector<Chunk>& chunks, Tables* t
         const int want = t->wide ? std::max(1, (m->n_cu * 3 / 4) / (m->H * nrb))
                                  : std::max(1, (kAttnBlocksTarget + m->H * nrb - 1) / (m->H * nrb));
         // keys per split: at most what one block's waves hold in flight
-        const int max_keys = nw * ATTN_DEC_ITERS * (64 / (m->hd / 8));
+        const int max_keys = nw * (t->wide ? ATTN_DEC_WIDE_ITERS : ATTN_DEC_ITERS) * (64 / (m->hd / 8));
         int slot = 0, row0 = 0, rbi = 0;
         t->max_rows = 0;
         t->dg = DecGeom{};

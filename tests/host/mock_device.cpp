@@ -493,7 +493,7 @@ hipError_t launch_attn_dec(const AttnItem* items, int n_items, int max_rows, con
     CHECK(q && kv && part_ml && part_o && out && max_rows >= 1 && max_rows <= ATTN_DEC_ROWS, "decode attention args");
     CHECK(!wide || (D.kv_bf16 && max_rows <= ATTN_DEC_WIDE_ROWS), "wide decode attention on a group it does not take");
     // a split holds at most the keys the block's waves load at once
-    const int max_keys = (wide ? ATTN_DEC_WIDE_WAVES : 4) * ATTN_DEC_ITERS * (64 / (D.hd / 8));
+    const int max_keys = (wide ? ATTN_DEC_WIDE_WAVES * ATTN_DEC_WIDE_ITERS : 4 * ATTN_DEC_ITERS) * (64 / (D.hd / 8));
     for (int b = 0; b < n_items; ++b) {
         const AttnItem it = dg.on ? dec_item(dg, b) : items[b];
         CHECK(it.hi - it.lo <= max_keys, "decode attention: item %d covers %d keys, a block holds %d", b, it.hi - it.lo,
