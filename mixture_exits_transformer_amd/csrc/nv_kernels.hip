@@ -916,6 +916,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
         cs = cs + 1 == ST ? 0 : cs + 1;
     }
     __syncthreads();                                   // all reads of the last stage are done
+    // residual epilogue: the tile's output rows, fetched once while the tile goes to LDS
+    const int rows = min(BM, a.R - m0);
+    static_assert(BM <= NTH, "one thread per row of the tile");
+    __shared__ int s_orow[EPI == EPI_RESID && HEAD == 0 ? BM : 1];
+    int orow_t = 0;
+    if constexpr (EPI == EPI_RESID && HEAD == 0) {
+        if (tid < rows) orow_t = a.o_rows ? a.o_rows[m0 + tid].hrow : m0 + tid;
+    }
     // the output tile goes through LDS (the operand buffers are free now), so that the
     // epilogue runs as one compact loop with coalesced stores
 #pragma unroll
@@ -925,8 +933,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 Cs[(wm * WR + i * 16 + 4 * (lane >> 4) + e) * CLD + wn * WN + t * 16 + (lane & 15)] = acc[i][t][e];
+    if constexpr (EPI == EPI_RESID && HEAD == 0) {
+        if (tid < rows) s_orow[tid] = orow_t;
+    }
     __syncthreads();
-    const int rows = min(BM, a.R - m0);
     if constexpr (HEAD != 0) {
         if (a.xent_part) {
             // fused cross-entropy: TPR threads per row (adjacent lanes) reduce each 64-column
@@ -965,10 +975,33 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(GemmArgs a) {
             return;
         }
     }
-    for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
-        const int r = idx / (BN / 2), c = 2 * (idx - r * (BN / 2));
-        const float2 v = *(const float2*)&Cs[r * CLD + c];
-        epi_pair_t<EPI>(a, m0 + r, n0 + c, v.x, v.y);
+    if constexpr (EPI == EPI_RESID && HEAD == 0) {
+        // each thread keeps one column pair (c, c + 1) and takes every RPI-th row; the
+        // residual values of all its rows are loaded before the first store, so their
+        // latencies overlap instead of following one another (O/down at 2047 rows:
+        // 33.7 -> 30.2 us per launch)
+        constexpr int PPR = BN / 2, RPI = NTH / PPR, IT = BM / RPI;
+        static_assert(NTH % PPR == 0 && BM % RPI == 0, "a fixed column pair per thread");
+        const int c = 2 * (tid % PPR), rt = tid / PPR, n = n0 + c;
+        float2 res[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int r = rt + it * RPI;
+            res[it] = r < rows ? *(const float2*)(a.out + (int64_t)s_orow[r] * a.ldo + n) : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int r = rt + it * RPI;
+            if (r >= rows) break;
+            const float2 v = *(const float2*)&Cs[r * CLD + c];
+            *(float2*)(a.out + (int64_t)s_orow[r] * a.ldo + n) = make_float2(res[it].x + v.x, res[it].y + v.y);
+        }
+    } else {
+        for (int idx = tid; idx < rows * (BN / 2); idx += NTH) {
+            const int r = idx / (BN / 2), c = 2 * (idx - r * (BN / 2));
+            const float2 v = *(const float2*)&Cs[r * CLD + c];
+            epi_pair_t<EPI>(a, m0 + r, n0 + c, v.x, v.y);
+        }
     }
     stamp_end_lin(a.stamp, t_begin, STAMP_BLOCKS);
 }
