@@ -79,6 +79,12 @@ size_t nv_mem_required(const char *weights_path, int32_t max_batch, int32_t max_
  * same way for both calls):
  *   NVIUM_MFMA_MIN_ROWS  rows from which products use the matrix cores (default 9;
  *                        0: never), for tests of the vector-ALU paths;
+ *   NVIUM_SK_MIN_ROWS, NVIUM_SK_MAX_ROWS  row groups that take the split-K
+ *                        matrix-core product when K is a multiple of 512 (default 5
+ *                        and 64; 0: never);
+ *   NVIUM_SK_NTB=a,b     16-column tiles per split-K block with / without RMSNorm
+ *                        (1 or 2; default 2,1);
+ *   NVIUM_SCHED_AGE      nv_generate's greedy aging weight (default 16);
  *   NVIUM_SEGMENT=1      one-row decode segments in the persistent segment kernel;
  *   NVIUM_LOSS_ROWS      rows per head pass of nv_mixture_loss (default: as many as
  *                        a 256 MiB logits workspace holds, at least 256).
