@@ -78,7 +78,7 @@ class StepCheck:
 
     def finish(self, logit_tol: float, gate_bound: float = GATE_BOUND_BF16, max_logit_explained=1,
                max_gate_explained: int = 1) -> None:
-        """Assert the run's verdict: no unexplained mismatch, logits within `logit_tol`,
+        """Assert the run's outcome: no unexplained mismatch, logits within `logit_tol`,
         walked gates within `gate_bound` of the oracle's, and at most the given number of
         draws accepted only through the widened (bf16) bands (max_logit_explained None: any
         number, for vocabularies whose token intervals are narrower than the CDF shift the
