@@ -129,6 +129,41 @@ class paused_gc:
         gc.enable()
 
 
+CALIBRATION_SAMPLE = os.path.join(ROOT, "tests", "golden", "gate_bias_1p5b.json")
+
+
+def expected_window_mass(wl, p0, n):
+    """Mean stick-breaking exit probabilities over decode positions p0 .. p0+n-1, from the
+    stored gate-calibration sample: the gate logits g_k . h at those positions, taken on the
+    workload's prompt followed by uniform stand-in tokens (the run draws its own tokens, so
+    its hidden states differ), with the workload's biases.  None when the sample does not
+    cover the window.  The stated mass holds on average over the whole calibrated range; a
+    short window sees the drift of the router's linear term with the position."""
+    import numpy as np
+    try:
+        with open(CALIBRATION_SAMPLE) as f:
+            cal = json.load(f).get(wl.name)
+    except OSError:
+        return None
+    if not cal:
+        return None
+    lo, hi = cal["positions"]
+    if p0 < lo or p0 + n - 1 > hi:
+        return None
+    z = np.asarray(cal["z"], dtype=np.float64)[p0 - lo:p0 - lo + n]
+    w = 1.0 / (1.0 + np.exp(-(z + np.asarray(wl.model.gate_bias, dtype=np.float64))))
+    p = np.empty((n, 4))
+    rest = np.ones(n)
+    for k in range(3):
+        p[:, k] = rest * w[:, k]
+        rest = rest * (1.0 - w[:, k])
+    p[:, 3] = rest
+    return {"value": [round(float(x), 4) for x in p.mean(axis=0)],
+            "positions": [p0, p0 + n - 1],
+            "source": "gate-calibration sample (tests/golden/gate_bias_1p5b.json): oracle hidden states on "
+                      "the workload's prompt plus uniform stand-in tokens, not this run's draws"}
+
+
 def run_decode(lib, h, prompt, U, steps, warmup):
     """Warm up, restart the sequence, then time `steps` decode steps: once through
     nv_generate (the library's decode loop: one call, draws read back through its ring of
@@ -519,6 +554,7 @@ def main():
     counted = counted_traffic(kname)
     top = sorted(ker, key=lambda k: -k[2])[:8]
     hist = np.bincount(np.asarray(exits), minlength=5)[1:]
+    window_mass = expected_window_mass(wl, len(prompt) - 1, steps)
     out = {
         "metric": "generated tokens/s, 1.5B bs=1, vs exit-4-forced decode; achieved HBM GB/s",
         "value": round(tok_s, 2),
@@ -560,6 +596,7 @@ def main():
         "exit_histogram": [int(x) for x in hist],
         "exit_mass_stated": list(STATED_MASS.get(wl.name, ())) or None,
         "exit_mass_realised": [round(float(x) / steps, 4) for x in hist],
+        "exit_mass_expected_window": window_mass,
         "mean_segments_per_token": round(float(np.mean(exits)), 4),
         # the step's cost per segment a token runs: tokens/s moves with the realised exit mix
         # (which last-bit rounding changes on random-init weights), this figure does not
