@@ -51,3 +51,20 @@ def test_workloads_carry_the_calibrated_biases():
     assert workload("A").model.gate_bias == BIAS_CAL_1P5B_40_25_20_15
     assert workload("C").model.gate_bias == BIAS_CAL_1P5B_40_25_20_15
     assert workload("D").model.gate_bias == BIAS_CAL_1P5B_60_20_10_10
+
+
+def test_bench_window_mass():
+    """bench.py's expected exit mass of a timed window: over the whole calibrated range it is
+    the stated mass; over A's first 20 positions it is the drifted mass of those positions;
+    outside the sample, and for workloads without one, it is None."""
+    import bench
+    m = bench.expected_window_mass(workload("A"), 511, 512)
+    assert np.allclose(m["value"], [0.4, 0.25, 0.2, 0.15], atol=1e-4), m
+    assert m["positions"] == [511, 1022]
+    m = bench.expected_window_mass(workload("D"), 8191, 256)
+    assert np.allclose(m["value"], [0.6, 0.2, 0.1, 0.1], atol=1e-4), m
+    g = json.load(open(GOLDEN))
+    w20 = _masses(np.asarray(g["A"]["z"])[:20], BIAS_CAL_1P5B_40_25_20_15)
+    assert np.allclose(bench.expected_window_mass(workload("A"), 511, 20)["value"], w20, atol=1e-4)
+    assert bench.expected_window_mass(workload("A"), 1010, 20) is None      # past position 1022
+    assert bench.expected_window_mass(workload("B"), 511, 20) is None       # no calibration sample
